@@ -1,0 +1,46 @@
+"""Rotary position embedding, GPT-NeoX ("rotate half") form.  TEST INFRASTRUCTURE.
+
+"TensorRT-LLM source analysis report", section 1.1, lists rotary_embedding
+among the attention parameters and names GPT-NeoX among the RoPE variants; it
+gives no formula.  "TensorRT-LLM source teardown part 1", AttentionMetadata
+section, defines position_ids as each token's position within its sequence.
+Readings taken (no page states them):
+
+* a token at 0-based absolute position m of its sequence is rotated by angle
+  m * theta_j on the pair (x_j, x_{j + R/2}), j = 0 .. R/2 - 1, where R is the
+  rotary dimension (the head dimension unless stated otherwise) and
+  theta_j = base ** (-2 j / R); dimensions >= R pass through unchanged;
+* rotation: y_j = x_j cos - x_{j+R/2} sin,  y_{j+R/2} = x_{j+R/2} cos + x_j sin,
+  each output as two fp64 products and one fp64 add/subtract (numpy evaluates
+  them as separate IEEE operations, no fused multiply-add);
+* applied to every query head and every new key head; values are not rotated.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def neox_inv_freq(base: float, rot_dim: int) -> np.ndarray:
+    j = np.arange(rot_dim // 2, dtype=np.float64)
+    return np.power(np.float64(base), -(2.0 * j) / np.float64(rot_dim))
+
+
+def neox_tables(base: float, rot_dim: int, max_pos: int):
+    """fp64 cos/sin tables [max_pos, rot_dim/2] of angle m * theta_j."""
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * neox_inv_freq(base, rot_dim)[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope_neox(x: np.ndarray, positions: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray,
+              rot_dim: int) -> np.ndarray:
+    """Rotate x [n, heads, D] (fp64) at positions [n] with tables [P, rot_dim/2]."""
+    x = np.asarray(x, dtype=np.float64)
+    half = rot_dim // 2
+    c = cos_t[positions][:, None, :]
+    s = sin_t[positions][:, None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:rot_dim]
+    y = x.copy()
+    y[..., :half] = x1 * c - x2 * s
+    y[..., half:rot_dim] = x2 * c + x1 * s
+    return y

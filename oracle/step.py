@@ -1,0 +1,147 @@
+"""One step of one layer over an in-flight batch.  TEST INFRASTRUCTURE.
+
+The step (from the pages' description of the problem):
+
+1. lengths -- request r brings n_r new tokens (1 for a generation request) on
+   top of p_r cached ones, S_r = p_r + n_r ("TensorRT-LLM source analysis
+   report", section 1.1 sequence_length / context_lengths; the teardown's
+   AttentionMetadata section); packed rows carry no padding and context
+   requests come before generation requests (report, section 1.3);
+2. append -- rotate the new q and k at their absolute positions p_r + i
+   (RoPE, see ``rope``), round q to the io format (q_out), store the rotated k
+   and the raw v in the cache format (see ``codecs``) at cache positions
+   p_r .. S_r - 1 (study notes, section "KVCacheManager": the attention op
+   itself writes the new K/V through the block table);
+3. attention -- each new row attends over cache positions 0 .. its own
+   position (see ``attention``), reading q_out and the stored K/V as decoded.
+
+The oracle keeps each request's cache contiguous.  Only ``expected_pool``
+knows the paged layout, which it writes by its definition: the pool is
+[num_blocks, 2, tokens_per_block, num_kv_heads, head_dim] with K at index 0 and
+V at index 1 (teardown, KV cache manager interfaces), and cache position t of
+request r lives in block table[r][t // T], slot t % T (report, section 1.2
+kv_cache_block_offsets; teardown, get_batch_cache_indices).
+
+History ("already cached") values come from the workload generator as io-format
+values that count as already rotated; the oracle stores them in the cache format
+with the same codec as new tokens, without rotation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+from .attention import attend
+from .rope import neox_tables, rope_neox
+
+
+def io_decode(batch, bits) -> np.ndarray:
+    return codecs.decode(bits, batch.shape.io_dtype)
+
+
+def tables(batch, max_pos: int | None = None):
+    sh = batch.shape
+    if max_pos is None:
+        max_pos = int(batch.sequence_lengths.max()) if batch.num_requests else 1
+    return neox_tables(sh.rope_theta, sh.rot_dim, max(max_pos, 1))
+
+
+def append_request(batch, r: int, tabs, rope: bool = True):
+    """Return (q_out, k_store, v_store) of request r's new tokens.
+
+    q_out is in the io representation; k_store/v_store in the cache
+    representation.  ``rope=False`` stores k unrotated and skips q.
+    """
+    sh = batch.shape
+    n = int(batch.context_lengths[r])
+    p = int(batch.past_lengths[r])
+    pos = np.arange(p, p + n)
+    k = io_decode(batch, batch.new_k(r))
+    v = io_decode(batch, batch.new_v(r))
+    q_out = None
+    if rope:
+        cos_t, sin_t = tabs
+        q = io_decode(batch, batch.new_q(r))
+        q_out = codecs.encode(rope_neox(q, pos, cos_t, sin_t, sh.rot_dim), sh.io_dtype)
+        k = rope_neox(k, pos, cos_t, sin_t, sh.rot_dim)
+    k_store = codecs.encode(k, sh.kv_dtype, sh.k_scale)
+    v_store = codecs.encode(v, sh.kv_dtype, sh.v_scale)
+    return q_out, k_store, v_store
+
+
+def history_request(batch, r: int):
+    """Stored cache contents of request r's p_r already-cached positions."""
+    sh = batch.shape
+    k = codecs.encode(io_decode(batch, batch.hist_k(r)), sh.kv_dtype, sh.k_scale)
+    v = codecs.encode(io_decode(batch, batch.hist_v(r)), sh.kv_dtype, sh.v_scale)
+    return k, v
+
+
+def cache_request(batch, r: int, tabs):
+    """(q_out, K, V): request r's rotated q (io repr) and its whole cache after
+    the append, decoded to fp64, contiguous by position [S_r, Hkv, D]."""
+    sh = batch.shape
+    q_out, k_new, v_new = append_request(batch, r, tabs)
+    k_hist, v_hist = history_request(batch, r)
+    K = codecs.decode(np.concatenate([k_hist, k_new], axis=0), sh.kv_dtype, sh.k_scale)
+    V = codecs.decode(np.concatenate([v_hist, v_new], axis=0), sh.kv_dtype, sh.v_scale)
+    return q_out, K, V
+
+
+def attention_request(batch, r: int, tabs, heads=None, rows=None) -> np.ndarray:
+    """fp64 attention output of request r's new rows: [n_r (or len(rows)), H (or len(heads)), D]."""
+    q_out, K, V = cache_request(batch, r, tabs)
+    p = int(batch.past_lengths[r])
+    q = io_decode(batch, q_out)
+    positions = p + np.arange(q.shape[0])
+    if rows is not None:
+        rows = np.asarray(rows)
+        q, positions = q[rows], positions[rows]
+    return attend(q, K, V, positions, heads=heads)
+
+
+def run(batch):
+    """Whole step: dict with packed q_out (io repr), out (fp64 [N, H, D]) and the
+    per-request stored new K/V."""
+    tabs = tables(batch)
+    q_outs, outs, k_new, v_new = [], [], [], []
+    for r in range(batch.num_requests):
+        q_out, kn, vn = append_request(batch, r, tabs)
+        q_outs.append(q_out)
+        k_new.append(kn)
+        v_new.append(vn)
+        outs.append(attention_request(batch, r, tabs))
+    return {
+        "q_out": np.concatenate(q_outs, axis=0),
+        "out": np.concatenate(outs, axis=0),
+        "k_new": k_new,
+        "v_new": v_new,
+    }
+
+
+def expected_pool(batch, sentinel, include_new: bool = True, include_history: bool = True):
+    """The whole paged pool [nb, 2, T, Hkv, D] (cache representation) after the
+    history fill and the step's append; slots nobody writes hold ``sentinel``."""
+    sh = batch.shape
+    T = sh.tokens_per_block
+    pool = np.full((batch.num_pool_blocks, 2, T, sh.num_kv_heads, sh.head_dim), sentinel,
+                   dtype=codecs.storage_dtype(sh.kv_dtype))
+    tabs = tables(batch)
+    for r in range(batch.num_requests):
+        p = int(batch.past_lengths[r])
+        S = int(batch.sequence_lengths[r])
+        parts = []
+        if include_history:
+            kh, vh = history_request(batch, r)
+            parts.append((np.arange(0, p), kh, vh))
+        if include_new:
+            _, kn, vn = append_request(batch, r, tabs)
+            parts.append((np.arange(p, S), kn, vn))
+        for pos, ks, vs in parts:
+            if pos.size == 0:
+                continue
+            blk = batch.block_table[r, pos // T]
+            slot = pos % T
+            pool[blk, 0, slot] = ks
+            pool[blk, 1, slot] = vs
+    return pool

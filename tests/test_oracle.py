@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against closed forms, invariants, a printed example,
+library special cases and a pure-Python brute force (no GPU)."""
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import codecs as C
+from oracle import rope as R
+from oracle import step as S
+from workloads import synth as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ------------------------------------------------------------------ helpers
+class Crafted(W.Batch):
+    """A batch whose values are given explicitly (io representation)."""
+
+    def set_values(self, q, k, v, hk, hv):
+        self._vals = dict(q=q, k=k, v=v, hk=hk, hv=hv)
+        return self
+
+    def new_q(self, r):
+        return self._vals["q"][r]
+
+    def new_k(self, r):
+        return self._vals["k"][r]
+
+    def new_v(self, r):
+        return self._vals["v"][r]
+
+    def hist_k(self, r):
+        return self._vals["hk"][r]
+
+    def hist_v(self, r):
+        return self._vals["hv"][r]
+
+
+def crafted(shape, ctx=(), gen_past=(), seed=0, fill=None):
+    b = W.make_batch(shape, ctx=ctx, gen_past=gen_past, seed=seed)
+    cb = Crafted(**{f: getattr(b, f) for f in ("shape", "seed", "request_types", "context_lengths",
+                                                "sequence_lengths", "block_table", "num_pool_blocks", "label")})
+    H, Hkv, D = shape.num_heads, shape.num_kv_heads, shape.head_dim
+    n, p = b.context_lengths, b.past_lengths
+    fill = fill or (lambda tag, r, rows, heads: np.zeros((rows, heads, D), np.float32))
+    q = [fill("q", r, int(n[r]), H) for r in range(b.num_requests)]
+    k = [fill("k", r, int(n[r]), Hkv) for r in range(b.num_requests)]
+    v = [fill("v", r, int(n[r]), Hkv) for r in range(b.num_requests)]
+    hk = [fill("hk", r, int(p[r]), Hkv) for r in range(b.num_requests)]
+    hv = [fill("hv", r, int(p[r]), Hkv) for r in range(b.num_requests)]
+    return cb.set_values(q, k, v, hk, hv)
+
+
+def rand_unit(rng, shape):
+    return rng.standard_normal(shape)
+
+
+# ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("rot", [64, 128, 32])
+def test_rope_identity_at_position_zero_and_norm_preserving(rot):
+    rng = np.random.default_rng(1)
+    D = 128 if rot <= 128 else rot
+    x = rand_unit(rng, (50, 3, D))
+    cos_t, sin_t = R.neox_tables(1e4, rot, 5000)
+    y0 = R.rope_neox(x, np.zeros(50, int), cos_t, sin_t, rot)
+    assert np.array_equal(y0, x)
+    pos = rng.integers(0, 5000, 50)
+    y = R.rope_neox(x, pos, cos_t, sin_t, rot)
+    h = rot // 2
+    n_in = x[..., :h] ** 2 + x[..., h:rot] ** 2
+    n_out = y[..., :h] ** 2 + y[..., h:rot] ** 2
+    assert np.allclose(n_out, n_in, rtol=1e-12, atol=1e-15)
+    assert np.array_equal(y[..., rot:], x[..., rot:])         # dims past the rotary part pass through
+
+
+def test_rope_is_complex_multiplication_on_rotate_half_pairs():
+    rng = np.random.default_rng(2)
+    rot, base = 128, 5e5
+    x = rand_unit(rng, (40, 2, rot))
+    pos = rng.integers(0, 30000, 40)
+    cos_t, sin_t = R.neox_tables(base, rot, 30000)
+    y = R.rope_neox(x, pos, cos_t, sin_t, rot)
+    z = x[..., :64] + 1j * x[..., 64:]
+    ang = pos[:, None].astype(np.float64) * R.neox_inv_freq(base, rot)[None, :]
+    w = z * np.exp(1j * ang)[:, None, :]
+    assert np.allclose(y[..., :64], w.real, rtol=0, atol=1e-12)
+    assert np.allclose(y[..., 64:], w.imag, rtol=0, atol=1e-12)
+
+
+def test_rope_pairs_are_j_and_j_plus_half():
+    rot = 64
+    cos_t, sin_t = R.neox_tables(1e4, rot, 10)
+    for j in (0, 5, 31, 32, 40, 63):
+        x = np.zeros((1, 1, rot)); x[0, 0, j] = 1.0
+        y = R.rope_neox(x, np.array([7]), cos_t, sin_t, rot)
+        nz = set(np.nonzero(np.abs(y[0, 0]) > 1e-15)[0].tolist())
+        partner = j + 32 if j < 32 else j - 32
+        assert nz <= {j, partner} and j in nz
+
+
+def test_rope_relative_position_and_composition():
+    rng = np.random.default_rng(3)
+    rot = 128
+    cos_t, sin_t = R.neox_tables(1e4, rot, 4000)
+    q = rand_unit(rng, (1, 1, rot)); k = rand_unit(rng, (1, 1, rot))
+    for (m, n, c) in [(10, 3, 100), (0, 500, 7), (1500, 1499, 2000)]:
+        a = np.sum(R.rope_neox(q, np.array([m]), cos_t, sin_t, rot) * R.rope_neox(k, np.array([n]), cos_t, sin_t, rot))
+        b = np.sum(R.rope_neox(q, np.array([m + c]), cos_t, sin_t, rot) * R.rope_neox(k, np.array([n + c]), cos_t, sin_t, rot))
+        assert abs(a - b) < 1e-9
+    x = rand_unit(rng, (1, 1, rot))
+    ab = R.rope_neox(R.rope_neox(x, np.array([123]), cos_t, sin_t, rot), np.array([456]), cos_t, sin_t, rot)
+    direct = R.rope_neox(x, np.array([579]), cos_t, sin_t, rot)
+    assert np.allclose(ab, direct, atol=1e-11)
+
+
+def test_rope_frequency_ladder():
+    # pair 0 turns by exactly 1 radian per position; consecutive pairs slow by
+    # a constant factor base^(2/R); the pair past the last would turn at 1/base.
+    for base, rot in [(1e4, 64), (5e5, 128)]:
+        f = R.neox_inv_freq(base, rot)
+        assert f[0] == 1.0
+        ratios = f[:-1] / f[1:]
+        assert np.allclose(ratios, ratios[0], rtol=1e-12)
+        assert np.isclose(f[-1] / ratios[0], 1.0 / base, rtol=1e-12)
+        cos_t, sin_t = R.neox_tables(base, rot, 3)
+        x = np.zeros((1, 1, rot)); x[0, 0, 0] = 1.0
+        y = R.rope_neox(x, np.array([1]), cos_t, sin_t, rot)
+        assert math.isclose(math.atan2(y[0, 0, rot // 2], y[0, 0, 0]), 1.0, rel_tol=1e-15)
+
+
+# ------------------------------------------------------------------ softmax / attention
+def test_softmax_printed_temperature_example():
+    rows = [l.split() for l in open(os.path.join(HERE, "golden", "softmax_temperature.txt"))
+            if l.strip() and not l.startswith("#")]
+    for r in rows:
+        logits = np.array([float(v) for v in r[1:4]])
+        printed = np.array([float(v) for v in r[4:7]])
+        p = A.softmax_rows(logits[None, :])[0]
+        matches = np.allclose(np.round(p, 2), printed, atol=1e-9)
+        assert matches == (r[7] == "ok"), r
+
+
+def test_softmax_invariants():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((20, 33)) * 5
+    p = A.softmax_rows(x)
+    assert np.allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert np.allclose(A.softmax_rows(x + 123.25), p, atol=1e-15)
+    assert np.allclose(A.softmax_rows(np.full((2, 7), 3.0)), 1.0 / 7, atol=1e-16)
+    xm = x.copy(); xm[:, 5:] = -np.inf
+    pm = A.softmax_rows(xm)
+    assert np.all(pm[:, 5:] == 0) and np.allclose(pm.sum(1), 1)
+
+
+def test_attend_closed_form_zero_keys_gives_running_mean():
+    L, D = 200, 16
+    K = np.zeros((L, 2, D))
+    V = np.broadcast_to(np.arange(L, dtype=np.float64)[:, None, None], (L, 2, D)).copy()
+    pos = np.array([0, 1, 17, 63, 64, 199])
+    q = np.random.default_rng(5).standard_normal((len(pos), 4, D))
+    out = A.attend(q, K, V, pos)
+    want = (pos / 2.0)[:, None, None]
+    assert np.allclose(out, np.broadcast_to(want, out.shape), atol=1e-12)
+
+
+def test_attend_single_key_and_one_hot_probe():
+    rng = np.random.default_rng(6)
+    D, L = 64, 60
+    V = rng.standard_normal((L, 1, D))
+    K = np.zeros((L, 1, D))
+    for t in range(L):
+        K[t, 0, t % D] = 60.0
+    q = rng.standard_normal((1, 1, D))
+    assert np.allclose(A.attend(q, K, V, np.array([0]))[0, 0], V[0, 0], atol=1e-15)
+    for tstar in (0, 13, 59):
+        qq = np.zeros((1, 1, D)); qq[0, 0, tstar % D] = 1.0
+        out = A.attend(qq, K, V, np.array([L - 1]), scale=1.0)[0, 0]
+        assert np.allclose(out, V[tstar, 0], atol=1e-20 + 1e-12)
+
+
+def test_attend_gqa_mapping_is_contiguous_groups():
+    D, L, H, Hkv = 8, 10, 8, 2
+    K = np.zeros((L, Hkv, D))
+    V = np.zeros((L, Hkv, D))
+    for g in range(Hkv):
+        V[:, g, :] = g + 1
+    q = np.random.default_rng(7).standard_normal((3, H, D))
+    out = A.attend(q, K, V, np.array([2, 5, 9]))
+    for h in range(H):
+        assert np.allclose(out[:, h], h // (H // Hkv) + 1)
+
+
+def test_attend_gqa_equals_mha_with_repeated_kv_heads():
+    rng = np.random.default_rng(8)
+    H, Hkv, D, L = 12, 3, 16, 40
+    q = rng.standard_normal((5, H, D)); K = rng.standard_normal((L, Hkv, D)); V = rng.standard_normal((L, Hkv, D))
+    pos = np.array([0, 7, 20, 38, 39])
+    a = A.attend(q, K, V, pos)
+    b = A.attend(q, np.repeat(K, H // Hkv, axis=1), np.repeat(V, H // Hkv, axis=1), pos)
+    assert np.allclose(a, b, atol=1e-13)
+
+
+def _brute_attend(q, K, V, pos, scale):
+    n, H, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(K[0]); G = H // Hkv
+    out = [[[0.0] * D for _ in range(H)] for _ in range(n)]
+    for i in range(n):
+        for h in range(H):
+            g = h // G
+            s = [scale * sum(q[i][h][d] * K[t][g][d] for d in range(D)) for t in range(pos[i] + 1)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for d in range(D):
+                out[i][h][d] = sum(e[t] * V[t][g][d] for t in range(len(e))) / z
+    return out
+
+
+def test_attend_matches_pure_python_brute_force():
+    rng = np.random.default_rng(9)
+    H, Hkv, D, L = 4, 2, 8, 20
+    q = rng.standard_normal((6, H, D)); K = rng.standard_normal((L, Hkv, D)); V = rng.standard_normal((L, Hkv, D))
+    pos = np.array([0, 3, 10, 11, 19, 19])
+    got = A.attend(q, K, V, pos)
+    ref = np.array(_brute_attend(q.tolist(), K.tolist(), V.tolist(), pos.tolist(), 1 / math.sqrt(D)))
+    assert np.allclose(got, ref, atol=1e-12)
+
+
+# ------------------------------------------------------------------ step
+def _f32(x):
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def test_step_matches_pure_python_brute_force_fp32():
+    # tiny mixed batch: one chunked context request then two generation requests
+    sh = W.Shape("t", 4, 2, 8, 4, W.FP32, W.FP32, 100.0)
+    rng = np.random.default_rng(10)
+    fill = lambda tag, r, rows, heads: rng.standard_normal((rows, heads, 8)).astype(np.float32)
+    b = crafted(sh, ctx=[(5, 4)], gen_past=[6, 3], fill=fill)
+    res = S.run(b)
+    # brute force: angles with math.pow/cos/sin, rotation in Python floats, fp32 rounding via struct
+    H, Hkv, D, rot = 4, 2, 8, 8
+    rows_q, rows_o = [], []
+    for r in range(b.num_requests):
+        p = int(b.past_lengths[r]); n = int(b.context_lengths[r])
+        def rot_vec(x, m):
+            y = list(x)
+            for j in range(rot // 2):
+                a = m * math.pow(100.0, -2.0 * j / rot)
+                c, s = math.cos(a), math.sin(a)
+                y[j] = x[j] * c - x[j + rot // 2] * s
+                y[j + rot // 2] = x[j + rot // 2] * c + x[j] * s
+            return y
+        K = [[[float(v) for v in b.hist_k(r)[t][g]] for g in range(Hkv)] for t in range(p)]
+        Vv = [[[float(v) for v in b.hist_v(r)[t][g]] for g in range(Hkv)] for t in range(p)]
+        qs = []
+        for i in range(n):
+            qs.append([[_f32(v) for v in rot_vec([float(v) for v in b.new_q(r)[i][h]], p + i)] for h in range(H)])
+            K.append([[_f32(v) for v in rot_vec([float(v) for v in b.new_k(r)[i][g]], p + i)] for g in range(Hkv)])
+            Vv.append([[float(v) for v in b.new_v(r)[i][g]] for g in range(Hkv)])
+        rows_q += qs
+        rows_o += _brute_attend(qs, K, Vv, [p + i for i in range(n)], 1 / math.sqrt(D))
+    assert np.allclose(res["q_out"].astype(np.float64), np.array(rows_q), rtol=2 ** -23, atol=0)
+    assert np.allclose(res["out"], np.array(rows_o), atol=1e-6)
+
+
+def test_step_chunked_equals_unchunked():
+    sh = W.Shape("c", 4, 2, 16, 8, W.FP32, W.FP32, 1e4)
+    rng = np.random.default_rng(11)
+    n_all, first = 29, 16                      # first chunk is a block multiple
+    q = rng.standard_normal((n_all, 4, 16)).astype(np.float32)
+    k = rng.standard_normal((n_all, 2, 16)).astype(np.float32)
+    v = rng.standard_normal((n_all, 2, 16)).astype(np.float32)
+    one = crafted(sh, ctx=[(n_all, 0)]).set_values([q], [k], [v], [k[:0]], [v[:0]])
+    full = S.run(one)
+    c1 = crafted(sh, ctx=[(first, 0)]).set_values([q[:first]], [k[:first]], [v[:first]], [k[:0]], [v[:0]])
+    r1 = S.run(c1)
+    # the second chunk sees the first chunk's stored (rotated) K and raw V as its history
+    c2 = crafted(sh, ctx=[(n_all - first, first)]).set_values(
+        [q[first:]], [k[first:]], [v[first:]], [r1["k_new"][0]], [r1["v_new"][0]])
+    r2 = S.run(c2)
+    assert np.array_equal(np.concatenate([r1["q_out"], r2["q_out"]]), full["q_out"])
+    assert np.allclose(np.concatenate([r1["out"], r2["out"]]), full["out"], atol=1e-13)
+
+
+def test_step_generation_row_sees_every_cached_token_including_its_own():
+    # zero keys: a generation token at position p (S = p + 1 keys) must average V over 0..p
+    sh = W.Shape("g", 2, 1, 8, 4, W.FP32, W.FP32, 1e4)
+    def fill(tag, r, rows, heads):
+        if tag in ("hv",):
+            return np.broadcast_to(np.arange(rows, dtype=np.float32)[:, None, None], (rows, heads, 8)).copy()
+        if tag == "v":
+            return np.full((rows, heads, 8), 9.0, np.float32)       # the new token's V at position 9
+        if tag == "q":
+            return np.ones((rows, heads, 8), np.float32)
+        return np.zeros((rows, heads, 8), np.float32)
+    b = crafted(sh, gen_past=[9], fill=fill)
+    out = S.run(b)["out"]
+    assert np.allclose(out, 4.5, atol=1e-12)                    # mean of 0..9
+
+
+def test_expected_pool_layout_and_permutation_invariance():
+    sh = W.SHAPES[4]
+    base = None
+    for seed in (21, 22, 23):
+        b = W.make_batch(sh, ctx=[(70, 64)], gen_past=[5, 130], seed=seed)
+        b = W.Batch(b.shape, 99, b.request_types, b.context_lengths, b.sequence_lengths,
+                    b.block_table, b.num_pool_blocks)            # same values, different table
+        pool = S.expected_pool(b, sentinel=0xFFFF)
+        T = sh.tokens_per_block
+        tabs = S.tables(b)
+        caches = []
+        for r in range(b.num_requests):
+            Sr = int(b.sequence_lengths[r])
+            t = np.arange(Sr)
+            kg = pool[b.block_table[r, t // T], 0, t % T]
+            vg = pool[b.block_table[r, t // T], 1, t % T]
+            kh, vh = S.history_request(b, r)
+            _, kn, vn = S.append_request(b, r, tabs)
+            assert np.array_equal(kg, np.concatenate([kh, kn]))
+            assert np.array_equal(vg, np.concatenate([vh, vn]))
+            caches.append((kg, vg))
+        used = np.zeros(b.num_pool_blocks, bool)
+        for r in range(b.num_requests):
+            nb = (int(b.sequence_lengths[r]) + T - 1) // T
+            used[b.block_table[r, :nb]] = True
+        assert np.all(pool[~used] == 0xFFFF)
+        if base is None:
+            base = caches
+        else:
+            for (a1, a2), (b1, b2) in zip(base, caches):
+                assert np.array_equal(a1, b1) and np.array_equal(a2, b2)
+
+
+def test_fp8_cache_dequantises_what_was_quantised():
+    b = W.small_workload(5)
+    tabs = S.tables(b)
+    q_out, K, V = S.cache_request(b, 0, tabs)
+    s = b.shape.k_scale
+    codes = C.f64_to_e4m3(K / s)
+    assert np.array_equal(C.e4m3_to_f64(codes) * s, K)            # K holds exactly representable values
+    hk = C.bf16_to_f64(b.hist_k(0))
+    assert np.max(np.abs(K[: hk.shape[0]] - hk)) <= 2.0 ** -4 * np.max(np.abs(hk)) + 1e-12
+
+
+def test_small_workload_runs_and_rows_are_convex_combinations():
+    for k in (1, 3, 4):
+        b = W.small_workload(k)
+        res = S.run(b)
+        assert res["out"].shape == (b.num_tokens, b.shape.num_heads, b.shape.head_dim)
+        # each output is a convex combination of the request's V rows
+        tabs = S.tables(b)
+        off = b.token_offsets
+        for r in range(b.num_requests):
+            _, _, V = S.cache_request(b, r, tabs)
+            o = res["out"][off[r]:off[r + 1]]
+            G = b.shape.group
+            for h in range(0, b.shape.num_heads, G):
+                g = h // G
+                assert np.all(o[:, h] <= V[:, g].max(axis=0) + 1e-12)
+                assert np.all(o[:, h] >= V[:, g].min(axis=0) - 1e-12)

@@ -1,0 +1,55 @@
+"""The seeded input generator: determinism, lengths, block tables, value formats."""
+import numpy as np
+
+from workloads import synth as W
+
+
+def test_deterministic_per_seed_and_per_request():
+    a, b = W.workload(2), W.workload(2)
+    assert np.array_equal(a.sequence_lengths, b.sequence_lengths)
+    assert np.array_equal(a.block_table, b.block_table)
+    assert np.array_equal(a.hist_k(3), b.hist_k(3))
+    assert not np.array_equal(a.hist_k(3)[:10], a.hist_k(4)[:10])
+
+
+def test_workload_lengths_follow_their_recipes():
+    w1 = W.workload(1)
+    assert list(w1.request_types) == [W.CONTEXT, W.GENERATION]
+    assert list(w1.context_lengths) == [37, 1] and list(w1.sequence_lengths) == [37, 51]
+    assert w1.num_pool_blocks == 16
+    w2 = W.workload(2)
+    assert w2.num_requests == 64 and np.all(w2.context_lengths == 1)
+    assert w2.past_lengths.min() >= 512 and w2.past_lengths.max() <= 4096
+    w3 = W.workload(3)
+    assert np.all(w3.context_lengths == 2048) and np.all(w3.past_lengths == 0)
+    w4 = W.workload(4)
+    assert list(w4.past_lengths[:4]) == [0, 1024, 2048, 3072] and w4.num_contexts == 4
+    assert w4.num_tokens == 4224 <= w4.shape.max_num_tokens
+    assert np.all(w4.past_lengths[:4] % 64 == 0)
+    w5 = W.workload(5)
+    assert w5.past_lengths.min() >= 16384 and w5.past_lengths.max() <= 32768
+
+
+def test_block_table_is_injective_and_in_range():
+    for k in W.WORKLOADS:
+        b = W.workload(k)
+        T = b.shape.tokens_per_block
+        ids = []
+        for r in range(b.num_requests):
+            nb = (int(b.sequence_lengths[r]) + T - 1) // T
+            row = b.block_table[r]
+            assert np.all(row[:nb] >= 0) and np.all(row[nb:] == -1)
+            ids.extend(row[:nb].tolist())
+        assert len(set(ids)) == len(ids)
+        assert min(ids) >= 0 and max(ids) < b.num_pool_blocks
+
+
+def test_values_are_exact_in_the_io_format():
+    b = W.small_workload(3)
+    q = b.new_q(0)
+    assert q.dtype == np.uint16
+    f = W.make_batch(W.SHAPES[1], ctx=[(5, 0)], seed=3)
+    assert f.new_q(0).dtype == np.float32
+    # bf16 values are the float32 draws truncated to their upper half
+    raw = W._rng(b.seed, "q", 0).standard_normal(q.shape, dtype=np.float32)
+    assert np.array_equal(q, (raw.view(np.uint32) >> 16).astype(np.uint16))

@@ -1,0 +1,228 @@
+"""Seeded synthetic batches shaped like the five workloads of the hot path.
+
+Recipe (the same for every workload):
+
+* one ``numpy.random.Generator(PCG64(SeedSequence([seed, tag, index])))`` per
+  (purpose, request), so that any single request's inputs can be regenerated
+  on their own;
+* request lengths are explicit or drawn with ``integers(lo, hi, endpoint=True)``;
+* physical block IDs are the first ``sum(ceil(S_r / T))`` entries of
+  ``permutation(pool_blocks)``, handed out to (request, logical block) in
+  request order; unused table entries are -1;
+* values are ``standard_normal`` drawn in float32.  For a bf16 io dtype the
+  float32 draw is cut to its upper 16 bits (truncation toward zero, a pure bit
+  operation), so every value is exactly representable in the io dtype and both
+  sides start from the same numbers.
+
+Values are returned in the io dtype's own representation: ``float32`` arrays
+for fp32, ``uint16`` bit patterns for bf16.  History ("already cached") values
+are returned the same way; they count as already rotated, and each side writes
+them into its own cache representation (for an fp8 cache that means its own
+quantiser).
+
+Nothing here rotates, rounds to a storage format, scatters into pages or
+attends: those are the method, and each compared side implements them itself.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+FP32, BF16, FP8_E4M3 = "fp32", "bf16", "fp8_e4m3"
+CONTEXT, GENERATION = 0, 1
+
+_TAGS = {"lengths": 1, "blocks": 2, "q": 3, "k": 4, "v": 5, "hist_k": 6, "hist_v": 7}
+
+
+def _rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TAGS[tag], index])))
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Per-layer attention shape and storage formats."""
+    name: str
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    tokens_per_block: int
+    io_dtype: str
+    kv_dtype: str
+    rope_theta: float
+    rotary_dim: int = 0          # 0 means head_dim
+    k_scale: float = 1.0         # fp8 cache only: real value = scale * stored value
+    v_scale: float = 1.0
+    max_num_tokens: int = 8192
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def rot_dim(self) -> int:
+        return self.rotary_dim or self.head_dim
+
+
+@dataclass
+class Batch:
+    """One in-flight batch: lengths, block table and lazily drawn values."""
+    shape: Shape
+    seed: int
+    request_types: np.ndarray      # int32 [B]; CONTEXT rows first
+    context_lengths: np.ndarray    # int32 [B]; n_r, tokens this request brings to the step
+    sequence_lengths: np.ndarray   # int32 [B]; S_r = cached + n_r
+    block_table: np.ndarray        # int32 [B, max_blocks_per_seq]; -1 where unused
+    num_pool_blocks: int
+    label: str = ""
+
+    # ---- lengths -------------------------------------------------------
+    @property
+    def num_requests(self) -> int:
+        return int(self.request_types.shape[0])
+
+    @property
+    def past_lengths(self) -> np.ndarray:
+        return (self.sequence_lengths - self.context_lengths).astype(np.int32)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.context_lengths.sum())
+
+    @property
+    def num_contexts(self) -> int:
+        return int((self.request_types == CONTEXT).sum())
+
+    @property
+    def token_offsets(self) -> np.ndarray:
+        """int64 [B+1]: request r owns packed rows offsets[r] .. offsets[r+1]-1."""
+        return np.concatenate([[0], np.cumsum(self.context_lengths.astype(np.int64))])
+
+    @property
+    def max_context_length(self) -> int:
+        ctx = self.context_lengths[self.request_types == CONTEXT]
+        return int(ctx.max()) if ctx.size else 0
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    # ---- values --------------------------------------------------------
+    def _draw(self, tag: str, r: int, rows: int, heads: int) -> np.ndarray:
+        x = _rng(self.seed, tag, r).standard_normal((rows, heads, self.shape.head_dim), dtype=np.float32)
+        if self.shape.io_dtype == BF16:
+            x = (x.view(np.uint32) >> 16).astype(np.uint16)
+        elif self.shape.io_dtype != FP32:
+            raise ValueError(self.shape.io_dtype)
+        return x
+
+    def new_q(self, r: int) -> np.ndarray:
+        return self._draw("q", r, int(self.context_lengths[r]), self.shape.num_heads)
+
+    def new_k(self, r: int) -> np.ndarray:
+        return self._draw("k", r, int(self.context_lengths[r]), self.shape.num_kv_heads)
+
+    def new_v(self, r: int) -> np.ndarray:
+        return self._draw("v", r, int(self.context_lengths[r]), self.shape.num_kv_heads)
+
+    def hist_k(self, r: int) -> np.ndarray:
+        return self._draw("hist_k", r, int(self.past_lengths[r]), self.shape.num_kv_heads)
+
+    def hist_v(self, r: int) -> np.ndarray:
+        return self._draw("hist_v", r, int(self.past_lengths[r]), self.shape.num_kv_heads)
+
+    def packed(self, which: str) -> np.ndarray:
+        """Concatenate new_q / new_k / new_v over requests in packed row order."""
+        parts = [getattr(self, which)(r) for r in range(self.num_requests)]
+        return np.concatenate(parts, axis=0)
+
+
+def make_batch(shape: Shape, ctx=(), gen_past=(), seed: int = 0, pool_blocks_min: int = 0,
+               label: str = "") -> Batch:
+    """Build a batch from explicit lengths.
+
+    ``ctx`` is a sequence of (n_r, past_r) for context requests (their chunk
+    and the tokens already cached before it); ``gen_past`` lists the cached
+    length of each generation request (each brings one new token).
+    """
+    T = shape.tokens_per_block
+    types, n, s = [], [], []
+    for (nr, pr) in ctx:
+        types.append(CONTEXT); n.append(int(nr)); s.append(int(pr) + int(nr))
+    for pr in gen_past:
+        types.append(GENERATION); n.append(1); s.append(int(pr) + 1)
+    types = np.asarray(types, np.int32)
+    n = np.asarray(n, np.int32)
+    s = np.asarray(s, np.int32)
+    need = [(int(x) + T - 1) // T for x in s]
+    total = int(sum(need))
+    pool = max(total, int(pool_blocks_min))
+    ids = _rng(seed, "blocks").permutation(pool)[:total].astype(np.int32)
+    width = max(need) if need else 1
+    table = np.full((len(need), max(width, 1)), -1, np.int32)
+    pos = 0
+    for r, k in enumerate(need):
+        table[r, :k] = ids[pos:pos + k]
+        pos += k
+    return Batch(shape, seed, types, n, s, table, pool, label)
+
+
+# ---- the five workloads --------------------------------------------------
+SHAPES = {
+    1: Shape("tiny-mixed-fp32", 4, 2, 64, 16, FP32, FP32, 1.0e4),
+    2: Shape("decode-mha-bf16", 32, 32, 128, 64, BF16, BF16, 1.0e4),
+    3: Shape("prefill-gqa4-bf16", 32, 8, 128, 64, BF16, BF16, 5.0e5),
+    4: Shape("mixed-gqa8-bf16", 64, 8, 128, 64, BF16, BF16, 5.0e5),
+    5: Shape("longdecode-gqa4-fp8kv", 32, 8, 128, 64, BF16, FP8_E4M3, 5.0e5,
+             k_scale=2.0 ** -6, v_scale=2.0 ** -6),
+}
+
+
+def _uniform_pasts(seed: int, count: int, lo: int, hi: int) -> list[int]:
+    return [int(x) for x in _rng(seed, "lengths").integers(lo, hi, size=count, endpoint=True)]
+
+
+def workload(k: int) -> Batch:
+    """Full-size workload k (1..5)."""
+    seed = 1000 + k
+    sh = SHAPES[k]
+    if k == 1:
+        return make_batch(sh, ctx=[(37, 0)], gen_past=[50], seed=seed, pool_blocks_min=16, label="w1")
+    if k == 2:
+        return make_batch(sh, gen_past=_uniform_pasts(seed, 64, 512, 4096), seed=seed, label="w2")
+    if k == 3:
+        return make_batch(sh, ctx=[(2048, 0)] * 8, seed=seed, label="w3")
+    if k == 4:
+        return make_batch(sh, ctx=[(1024, 0), (1024, 1024), (1024, 2048), (1024, 3072)],
+                          gen_past=_uniform_pasts(seed, 128, 256, 4096), seed=seed, label="w4")
+    if k == 5:
+        return make_batch(sh, gen_past=_uniform_pasts(seed, 16, 16384, 32768), seed=seed, label="w5")
+    raise KeyError(k)
+
+
+def small_workload(k: int) -> Batch:
+    """Workload k at a size the oracle finishes in seconds: same heads,
+    head_dim, block size and dtypes; several blocks and a ragged tail."""
+    seed = 2000 + k
+    sh = SHAPES[k]
+    if k == 1:
+        return make_batch(sh, ctx=[(37, 0)], gen_past=[50], seed=seed, pool_blocks_min=16, label="s1")
+    if k == 2:
+        return make_batch(sh, gen_past=_uniform_pasts(seed, 6, 60, 700), seed=seed, label="s2")
+    if k == 3:
+        return make_batch(sh, ctx=[(300, 0), (190, 0)], seed=seed, label="s3")
+    if k == 4:
+        return make_batch(sh, ctx=[(128, 0), (192, 128), (100, 384)],
+                          gen_past=_uniform_pasts(seed, 6, 20, 500), seed=seed, label="s4")
+    if k == 5:
+        return make_batch(sh, gen_past=_uniform_pasts(seed, 4, 1000, 3000), seed=seed, label="s5")
+    raise KeyError(k)
+
+
+WORKLOADS = (1, 2, 3, 4, 5)
+SMALL_WORKLOADS = (1, 2, 3, 4, 5)
+
+
+def with_shape(batch: Batch, **changes) -> Batch:
+    """Same lengths and table with a modified shape (used by invariance tests)."""
+    return replace(batch, shape=replace(batch.shape, **changes))
