@@ -1,0 +1,291 @@
+// The extern "C" entry points declared in include/pkv.h: validate on the host, then
+// enqueue the kernels of one step on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "pkv.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+// ---------------------------------------------------------------- opt-in kernel timing
+struct TimingRec {
+  const char* name;
+  hipEvent_t beg, end;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_spare;
+
+hipEvent_t take_event() {
+  if (!g_spare.empty()) {
+    hipEvent_t e = g_spare.back();
+    g_spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    on = g_timing;
+  }
+  if (!on) return launch();
+  hipEvent_t b, e;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    b = take_event();
+    e = take_event();
+  }
+  if (b) (void)hipEventRecord(b, s);
+  const hipError_t err = launch();
+  if (e) (void)hipEventRecord(e, s);
+  if (b && e) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_recs.push_back({name, b, e});
+  }
+  return err;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return set_err(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int fmt_of(int32_t dt) { return dt == PKV_FP32 ? pkv::F_FP32 : dt == PKV_BF16 ? pkv::F_BF16 : pkv::F_FP8; }
+
+int check_rows(const void* p, int64_t stride, int64_t min_elems, int32_t dtype, const char* name) {
+  if (stride < min_elems)
+    return set_err(PKV_ERR_INVALID_ARG, std::string(name) + ": row stride shorter than one row");
+  if (!aligned16(p) || (stride * pkv::io_bytes(dtype)) % 16)
+    return set_err(PKV_ERR_INVALID_ARG, std::string(name) + ": rows must start on 16-byte boundaries");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+size_t pkv_workspace_size(const pkv_attn_desc* desc, int32_t max_num_requests, int32_t max_seq_len) {
+  std::string err;
+  if (pkv::validate_desc(desc, err) != PKV_OK) {
+    g_err = err;
+    return 0;
+  }
+  return pkv::workspace_upper_bound(*desc, max_num_requests, max_seq_len);
+}
+
+size_t pkv_workspace_size_for_batch(const pkv_attn_desc* desc, const pkv_batch_desc* batch) {
+  std::string err;
+  pkv::BatchPlan plan;
+  if (pkv::validate_desc(desc, err) != PKV_OK || pkv::validate_batch(desc, batch, &plan, err) != PKV_OK) {
+    g_err = err;
+    return 0;
+  }
+  return plan.ws_bytes;
+}
+
+int32_t pkv_rope_cos_sin(double base, int32_t rotary_dim, int32_t max_pos, double* cos_sin, void* stream) {
+  if (!(std::isfinite(base) && base > 0.0)) return set_err(PKV_ERR_INVALID_ARG, "rope base must be finite and > 0");
+  if (rotary_dim < 2 || rotary_dim % 2) return set_err(PKV_ERR_INVALID_ARG, "rotary_dim must be even and >= 2");
+  if (max_pos < 0) return set_err(PKV_ERR_INVALID_ARG, "max_pos < 0");
+  if (max_pos == 0) return PKV_OK;
+  if (!cos_sin) return set_err(PKV_ERR_INVALID_ARG, "cos_sin is NULL");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      timed("rope_table", s, [&] { return pkv::launch_rope_table(base, rotary_dim, max_pos, cos_sin, s); });
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return PKV_OK;
+}
+
+int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q, int64_t q_row_stride,
+                        const void* k, const void* v, int64_t kv_row_stride, const double* rope_cos_sin,
+                        int32_t rope_max_pos, void* q_out, void* kv_pool, void* stream) {
+  std::string err;
+  int rc = pkv::validate_desc(desc, err);
+  if (rc != PKV_OK) return set_err(rc, err);
+  pkv::BatchPlan plan;
+  rc = pkv::validate_batch(desc, batch, &plan, err);
+  if (rc != PKV_OK) return set_err(rc, err);
+  if (plan.N == 0) return PKV_OK;
+  const int32_t H = desc->num_heads, Hkv = desc->num_kv_heads, D = desc->head_dim;
+  if ((q == nullptr) != (q_out == nullptr)) return set_err(PKV_ERR_INVALID_ARG, "q and q_out must both be given or both NULL");
+  if (!k || !v || !kv_pool) return set_err(PKV_ERR_INVALID_ARG, "k, v and kv_pool must not be NULL");
+  if (q) {
+    if ((rc = check_rows(q, q_row_stride, static_cast<int64_t>(H) * D, desc->io_dtype, "q")) != PKV_OK) return rc;
+    if (!aligned16(q_out)) return set_err(PKV_ERR_INVALID_ARG, "q_out must be 16-byte aligned");
+  }
+  if ((rc = check_rows(k, kv_row_stride, static_cast<int64_t>(Hkv) * D, desc->io_dtype, "k")) != PKV_OK) return rc;
+  if ((rc = check_rows(v, kv_row_stride, static_cast<int64_t>(Hkv) * D, desc->io_dtype, "v")) != PKV_OK) return rc;
+  if (!aligned16(kv_pool)) return set_err(PKV_ERR_INVALID_ARG, "kv_pool must be 16-byte aligned");
+  if (desc->rope_style == PKV_ROPE_NEOX) {
+    if (!rope_cos_sin) return set_err(PKV_ERR_INVALID_ARG, "rope_cos_sin is NULL");
+    if (!aligned16(rope_cos_sin)) return set_err(PKV_ERR_INVALID_ARG, "rope_cos_sin must be 16-byte aligned");
+    if (rope_max_pos < plan.max_S)
+      return set_err(PKV_ERR_INVALID_ARG, "rope_max_pos=" + std::to_string(rope_max_pos) +
+                                              " does not cover position " + std::to_string(plan.max_S - 1));
+  }
+  pkv::AppendArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_stride = q_row_stride;
+  a.kv_stride = kv_row_stride;
+  a.cos_sin = rope_cos_sin;
+  a.max_pos = rope_max_pos;
+  a.q_out = q_out;
+  a.pool = kv_pool;
+  a.ctx_len = batch->context_lengths;
+  a.seq_len = batch->sequence_lengths;
+  a.table = batch->kv_cache_block_offsets;
+  a.B = plan.B;
+  a.N = plan.N;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.T = desc->tokens_per_block;
+  a.R = pkv::rot_dim(*desc);
+  a.mbps = batch->max_blocks_per_seq;
+  a.num_blocks = batch->num_pool_blocks;
+  const bool fp8 = desc->kv_dtype == PKV_FP8_E4M3;
+  a.inv_k_scale = fp8 ? 1.0 / static_cast<double>(desc->k_scale_quant_orig) : 1.0;
+  a.inv_v_scale = fp8 ? 1.0 / static_cast<double>(desc->v_scale_quant_orig) : 1.0;
+  a.io_fmt = fmt_of(desc->io_dtype);
+  a.kv_fmt = fmt_of(desc->kv_dtype);
+  a.rope = desc->rope_style == PKV_ROPE_NEOX;
+  a.max_n = plan.max_n;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed("append_rope", s, [&] { return pkv::launch_append(a, s); });
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PKV_OK;
+}
+
+int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
+                              int64_t q_row_stride, const void* kv_pool, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  std::string err;
+  int rc = pkv::validate_desc(desc, err);
+  if (rc != PKV_OK) return set_err(rc, err);
+  pkv::BatchPlan plan;
+  rc = pkv::validate_batch(desc, batch, &plan, err);
+  if (rc != PKV_OK) return set_err(rc, err);
+  if (plan.N == 0) return PKV_OK;
+  const int32_t H = desc->num_heads, D = desc->head_dim;
+  if (!q || !kv_pool || !out) return set_err(PKV_ERR_INVALID_ARG, "q, kv_pool and out must not be NULL");
+  if ((rc = check_rows(q, q_row_stride, static_cast<int64_t>(H) * D, desc->io_dtype, "q")) != PKV_OK) return rc;
+  if (!aligned16(out) || !aligned16(kv_pool)) return set_err(PKV_ERR_INVALID_ARG, "out and kv_pool must be 16-byte aligned");
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return set_err(PKV_ERR_WORKSPACE, "workspace of " + std::to_string(plan.ws_bytes) + " bytes required, " +
+                                            std::to_string(workspace ? workspace_bytes : 0) + " given");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return set_err(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  pkv::AttnArgs a{};
+  a.q = q;
+  a.q_stride = q_row_stride;
+  a.pool = kv_pool;
+  a.out = out;
+  a.ctx_len = batch->context_lengths;
+  a.seq_len = batch->sequence_lengths;
+  a.table = batch->kv_cache_block_offsets;
+  a.B = plan.B;
+  a.N = plan.N;
+  a.H = H;
+  a.Hkv = desc->num_kv_heads;
+  a.D = D;
+  a.T = desc->tokens_per_block;
+  a.mbps = batch->max_blocks_per_seq;
+  a.num_blocks = batch->num_pool_blocks;
+  const double scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0 / std::sqrt(static_cast<double>(D));
+  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  const bool fp8 = desc->kv_dtype == PKV_FP8_E4M3;
+  a.k_scale = fp8 ? desc->k_scale_quant_orig : 1.f;
+  a.v_scale = fp8 ? desc->v_scale_quant_orig : 1.f;
+  a.io_fmt = fmt_of(desc->io_dtype);
+  a.kv_fmt = fmt_of(desc->kv_dtype);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (plan.num_ctx > 0) {
+    a.req_begin = 0;
+    a.req_end = plan.num_ctx;
+    a.row_begin = 0;
+    a.max_n = plan.max_ctx_n;
+    if (plan.fast_prefill)
+      e = timed("prefill_mfma", s, [&] { return pkv::launch_prefill(a, s); });
+    else
+      e = timed("attn_generic_ctx", s, [&] { return pkv::launch_attn_generic(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "context attention launch");
+  }
+  if (plan.num_gen > 0) {
+    a.req_begin = plan.num_ctx;
+    a.req_end = plan.B;
+    a.row_begin = plan.ctx_tokens;
+    a.max_n = 1;
+    if (plan.fast_decode) {
+      a.chunk = plan.chunk;
+      a.max_splits = plan.max_splits;
+      a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_off);
+      a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_off);
+      e = timed("decode_split", s, [&] { return pkv::launch_decode_split(a, s); });
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+      e = timed("decode_combine", s, [&] { return pkv::launch_decode_combine(a, s); });
+      if (e != hipSuccess) return hip_fail(e, "decode combine launch");
+    } else {
+      e = timed("attn_generic_gen", s, [&] { return pkv::launch_attn_generic(a, s); });
+      if (e != hipSuccess) return hip_fail(e, "generation attention launch");
+    }
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_kernel_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_recs) {
+    g_spare.push_back(r.beg);
+    g_spare.push_back(r.end);
+  }
+  g_recs.clear();
+  g_timing = on != 0;
+  return PKV_OK;
+}
+
+int32_t pkv_kernel_timings(const char** names, float* milliseconds, int32_t max_entries) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  const int32_t n = static_cast<int32_t>(g_recs.size());
+  for (int32_t i = 0; i < n && i < max_entries; ++i) {
+    if (hipEventSynchronize(g_recs[i].end) != hipSuccess) return set_err(PKV_ERR_HIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_recs[i].beg, g_recs[i].end) != hipSuccess)
+      return set_err(PKV_ERR_HIP, "event elapsed time failed");
+    if (names) names[i] = g_recs[i].name;
+    if (milliseconds) milliseconds[i] = ms;
+  }
+  return n;
+}
+
+}  // extern "C"

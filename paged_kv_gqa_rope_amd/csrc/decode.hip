@@ -1,0 +1,309 @@
+// Generation-phase (decode) attention over the paged cache: split-KV pass + combine.
+//
+// "TensorRT-LLM 1.0 study notes", 6.3: a generation request has one query token that
+// attends to every cached token, reached block by block through the block table; the
+// phase is bound by HBM bandwidth.  This design splits each request's keys into
+// chunks so that even a handful of long requests fills all 256 CUs, and merges the
+// per-chunk partial results (running max m, sum l, unnormalised output o) in a
+// second pass with the same rescaling identity FlashAttention uses to merge tiles
+// (study notes 6.2, update of acc_o by the new running max).
+//
+// Pass 1, one workgroup per (generation request, KV head, chunk); 4 waves, each
+// streaming 64-key tiles of the chunk:
+//   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, loaded straight
+//     from HBM in operand layout; B = the G query heads of the KV head (GQA group,
+//     G <= 16, padded with zero heads), kept in registers for the whole chunk.
+//   * online softmax per head on the accumulators (lanes l, l^16, l^32, l^48 hold the
+//     same head), exp2 with the log2(e) factor folded into the scale.
+//   * O += P V on MFMA: A = P (heads x 32 keys) straight from the score registers,
+//     B = V read transposed from an LDS copy of the tile with ds_read_b64_tr_b16.
+//   * an fp8 cache is dequantised to bf16 on load (exact: every e4m3 value is a
+//     bf16 value); k_scale folds into the softmax scale and v_scale into the
+//     combine, so the pass works on raw codes times one.
+// Pass 2, one wave per (request, query head): M = max m_s, L = sum 2^(m_s-M) l_s,
+// O = sum 2^(m_s-M) o_s / L in a fixed order (no atomics: bitwise reproducible).
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTile = 64;          // keys per wave iteration
+constexpr int kD = 128;            // head_dim handled here
+constexpr int kVStride = 136;      // LDS row stride (bf16 elements) of a staged V tile
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
+  const float2 a = e4m3x2_to_f32(c.x), b = e4m3x2_hi_to_f32(c.x);
+  const float2 d = e4m3x2_to_f32(c.y), e = e4m3x2_hi_to_f32(c.y);
+  auto hi = [](float x) { return __float_as_uint(x) >> 16; };  // exact: e4m3 fits bf16
+  return make_uint4(hi(a.x) | (hi(a.y) << 16), hi(b.x) | (hi(b.y) << 16), hi(d.x) | (hi(d.y) << 16),
+                    hi(e.x) | (hi(e.y) << 16));
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnArgs a) {
+  const int split = blockIdx.x, g = blockIdx.y, rg = blockIdx.z;
+  const int r = a.req_begin + rg;
+  const int S = a.seq_len[r];
+  const int k0 = split * a.chunk;
+  if (k0 >= S || split >= a.max_splits) return;               // uniform over the block
+  const int kend = min(k0 + a.chunk, S);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int li = lane % 16, lg = lane / 16;
+  const int G = a.H / a.Hkv;
+  const int64_t row = static_cast<int64_t>(a.row_begin) + rg;
+  const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
+  const int32_t* table = a.table + static_cast<int64_t>(r) * a.mbps;
+
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
+
+  // B operand Q^T: head n = li, dims lg*32 + ks*8 + j (the dim order inside a
+  // contraction is free as long as K uses the same one).
+  bf16x8 qf[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
+                         static_cast<int64_t>(g * G + min(li, G - 1)) * kD + lg * 32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 8);
+      if (li >= G) u = make_uint4(0, 0, 0, 0);
+      qf[ks] = as_bf16x8(u);
+    }
+  }
+  const float xscale = a.scale_log2 * a.k_scale;
+
+  float m_run = -INFINITY, l_run = 0.f;                         // for head li
+  f32x4 o[8];                                                   // O[head lg*4+i][dim nb*16+li]
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ntiles = (kend - k0 + kTile - 1) / kTile;
+  uint16_t* vt = vtile[wave];
+  for (int t = wave; t < ntiles; t += kWaves) {
+    const int tb = k0 + t * kTile;
+    // ---- K in A-operand layout: key tb + kb*16 + li, dims lg*32 .. lg*32+31
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(tb + kb * 16 + li, kend - 1);        // clamp: never read unwritten slots
+      int32_t blk = table[key / a.T];
+      blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+      const int64_t base = ((static_cast<int64_t>(blk) * 2) * a.T + key % a.T) * kv_row +
+                           static_cast<int64_t>(g) * kD + lg * 32;
+      if constexpr (KV == F_BF16) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(p[ks]);
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base);
+        const uint4 c0 = p[0], c1 = p[1];
+        kf[kb][0] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c0.x, c0.y)));
+        kf[kb][1] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c0.z, c0.w)));
+        kf[kb][2] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c1.x, c1.y)));
+        kf[kb][3] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c1.z, c1.w)));
+      }
+    }
+    // ---- V rows, coalesced: bf16 16 keys x 4 lanes... (16 lanes per 256-byte row)
+    uint4 vr[16];
+    if constexpr (KV == F_BF16) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int key = min(tb + it * 4 + lg, kend - 1);
+        int32_t blk = table[key / a.T];
+        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int64_t base = ((static_cast<int64_t>(blk) * 2 + 1) * a.T + key % a.T) * kv_row +
+                             static_cast<int64_t>(g) * kD + li * 8;
+        vr[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base);
+      }
+    } else {
+      // 8 lanes x 16 codes per 128-byte row, 8 keys per load
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int key = min(tb + it * 8 + lane / 8, kend - 1);
+        int32_t blk = table[key / a.T];
+        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int64_t base = ((static_cast<int64_t>(blk) * 2 + 1) * a.T + key % a.T) * kv_row +
+                             static_cast<int64_t>(g) * kD + (lane % 8) * 16;
+        const uint4 c = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base);
+        vr[2 * it] = e4m3x8_to_bf16x8(make_uint2(c.x, c.y));
+        vr[2 * it + 1] = e4m3x8_to_bf16x8(make_uint2(c.z, c.w));
+      }
+    }
+    // ---- scores S^T[key][head]: lane holds head li, keys tb + kb*16 + lg*4 + i
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[ks], sacc[kb], 0, 0, 0);
+    }
+    float x[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = tb + kb * 16 + lg * 4 + i;
+        x[kb * 4 + i] = key < kend ? sacc[kb][i] * xscale : -INFINITY;
+        tmax = fmaxf(tmax, x[kb * 4 + i]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_run, tmax);                    // finite: key tb is always valid
+    const float alpha = exp2f(m_run - m_new);
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x[e] = exp2f(x[e] - m_new);
+      lsum += x[e];
+    }
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    // rescale O rows: lane's O rows are heads lg*4+i; their alpha lives in lane lg*4+i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ah = __shfl(alpha, lg * 4 + i, kWave);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ah;
+    }
+    // P as the A operand: row = head li, k-slot j <-> key 32*ks2 + (j/4)*16 + lg*4 + j%4
+    bf16x8 pa[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint4 u;
+      uint32_t* w = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j0 = 2 * jj, j1 = 2 * jj + 1;
+        const float p0 = x[(2 * ks2 + j0 / 4) * 4 + j0 % 4];
+        const float p1 = x[(2 * ks2 + j1 / 4) * 4 + j1 % 4];
+        w[jj] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
+      }
+      pa[ks2] = as_bf16x8(u);
+    }
+    // ---- V tile into this wave's LDS region (row-major [key][dim])
+    wave_lds_fence();
+    if constexpr (KV == F_BF16) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        *reinterpret_cast<uint4*>(vt + (it * 4 + lg) * kVStride + li * 8) = vr[it];
+    } else {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        uint16_t* d = vt + (it * 8 + lane / 8) * kVStride + (lane % 8) * 16;
+        *reinterpret_cast<uint4*>(d) = vr[2 * it];
+        *reinterpret_cast<uint4*>(d + 8) = vr[2 * it + 1];
+      }
+    }
+    wave_lds_fence();
+    // ---- O += P V: B operand = V[keys][dims nb*16 .. +15] read transposed
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int krow = ks2 * 32 + lg * 4 + li / 4;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const uint16_t* src = vt + krow * kVStride + nb * 16 + 4 * (li % 4);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 16 * kVStride));
+        const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                   __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks2], as_bf16x8(u), o[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the 4 waves' partial states, then write the chunk's (m, l, o)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&vtile[0][0]);          // [wave][16 heads][kD]
+  __shared__ float ml[kWaves][16][2];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + lg * 4 + i) * kD + nb * 16 + li] = o[nb][i];
+  if (lg == 0) {
+    ml[wave][li][0] = m_run;
+    ml[wave][li][1] = l_run;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * kD; e += kThreads) {
+    const int h = e / kD, d = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w][h][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float s = ml[w][h][0] == -INFINITY ? 0.f : exp2f(ml[w][h][0] - M);
+      L += s * ml[w][h][1];
+      O += s * red[(w * 16 + h) * kD + d];
+    }
+    const int64_t part = (static_cast<int64_t>(rg) * a.H + g * G + h) * a.max_splits + split;
+    a.ws_o[part * kD + d] = O;
+    if (d == 0) {
+      a.ws_ml[part * 2] = M;
+      a.ws_ml[part * 2 + 1] = L;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWave) void decode_combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x, rg = blockIdx.y, lane = threadIdx.x;
+  const int r = a.req_begin + rg;
+  const int S = a.seq_len[r];
+  const int ns = min((S + a.chunk - 1) / a.chunk, a.max_splits);
+  const int64_t base = (static_cast<int64_t>(rg) * a.H + h) * a.max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = exp2f(a.ws_ml[(base + s) * 2] - M);
+    L += w * a.ws_ml[(base + s) * 2 + 1];
+    o0 += w * a.ws_o[(base + s) * kD + lane];
+    o1 += w * a.ws_o[(base + s) * kD + lane + kWave];
+  }
+  const float inv = a.v_scale / L;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(a.row_begin) + rg) * a.H * kD +
+                  static_cast<int64_t>(h) * kD;
+  out[lane] = static_cast<uint16_t>(f32_to_bf16(o0 * inv));
+  out[lane + kWave] = static_cast<uint16_t>(f32_to_bf16(o1 * inv));
+}
+
+}  // namespace
+
+hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.max_splits, a.Hkv, a.req_end - a.req_begin);
+  if (a.kv_fmt == F_FP8)
+    hipLaunchKernelGGL(decode_split_kernel<F_FP8>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<F_BF16>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.H, a.req_end - a.req_begin);
+  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

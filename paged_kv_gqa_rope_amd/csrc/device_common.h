@@ -1,0 +1,116 @@
+// Device helpers shared by the gfx950 kernels: element formats, reductions, index math.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace pkv {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- element formats
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, nearest-even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// fp64 -> bf16 in one rounding (nearest-even), over the whole range: subnormal results,
+// overflow to infinity, NaN.  Works on the binary64 bit pattern: the kept part is the
+// sign, 11-bit exponent and top 7 fraction bits; the dropped 45 bits decide the rounding.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(b >> 48) & 0x8000u;
+  const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+  if (a > 0x7FF0000000000000ull) return sign | 0x7FC0u;               // NaN
+  const uint32_t E = static_cast<uint32_t>(a >> 52);                   // biased binary64 exponent
+  if (E >= 897u) {                                                     // result is normal (or overflows)
+    const uint64_t r = (a + 0xFFFFFFFFFFFull + ((a >> 45) & 1ull)) >> 45;   // exponent:fraction7, rounded
+    if (r >= (static_cast<uint64_t>(896 + 255) << 7)) return sign | 0x7F80u;
+    return sign | static_cast<uint32_t>(r - (896ull << 7));
+  }
+  // subnormal (or zero) bf16: value / 2^-133 rounded to an integer q <= 128
+  const uint64_t m = E ? ((a & 0xFFFFFFFFFFFFFull) | (1ull << 52)) : (a & 0xFFFFFFFFFFFFFull);
+  const uint32_t s = 942u - (E ? E : 1u);                              // >= 46
+  if (s >= 54u) return sign;                                           // below half the smallest subnormal
+  const uint64_t q = (m + ((1ull << (s - 1)) - 1ull) + ((m >> s) & 1ull)) >> s;
+  return sign | static_cast<uint32_t>(q);
+}
+
+// fp64 -> OCP E4M3 in one rounding (nearest-even), saturating finite overflow and
+// infinities to +-448.  Kept part: exponent and top 3 fraction bits; 49 bits dropped.
+__device__ __forceinline__ uint32_t f64_to_e4m3(double x) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(b >> 56) & 0x80u;
+  const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+  if (a > 0x7FF0000000000000ull) return sign | 0x7Fu;                  // NaN
+  const uint32_t E = static_cast<uint32_t>(a >> 52);
+  if (E >= 1017u) {                                                    // normal e4m3 range or above
+    const uint64_t r = (a + 0xFFFFFFFFFFFFull + ((a >> 49) & 1ull)) >> 49;
+    const uint64_t code = r - (1016ull << 3);
+    return sign | static_cast<uint32_t>(code > 0x7Eull ? 0x7Eull : code);
+  }
+  const uint64_t m = E ? ((a & 0xFFFFFFFFFFFFFull) | (1ull << 52)) : (a & 0xFFFFFFFFFFFFFull);
+  const uint32_t s = 1066u - (E ? E : 1u);                             // >= 50
+  if (s >= 54u) return sign;
+  const uint64_t q = (m + ((1ull << (s - 1)) - 1ull) + ((m >> s) & 1ull)) >> s;
+  return sign | static_cast<uint32_t>(q);
+}
+
+// OCP E4M3 -> fp32 for two codes (bytes 0 and 1 of `packed`), hardware conversion.
+__device__ __forceinline__ float2 e4m3x2_to_f32(uint32_t packed) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed), false);
+  return make_float2(v[0], v[1]);
+}
+// bytes 2 and 3
+__device__ __forceinline__ float2 e4m3x2_hi_to_f32(uint32_t packed) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed), true);
+  return make_float2(v[0], v[1]);
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum of len[0 .. r-1] over one wave (every lane gets the result).
+__device__ __forceinline__ int64_t wave_prefix(const int32_t* __restrict__ len, int r) {
+  int64_t s = 0;
+  for (int j = threadIdx.x % kWave; j < r; j += kWave) s += len[j];
+  return wave_sum_i64(s);
+}
+
+// Same over a whole block (blockDim.x a multiple of 64, <= 1024); every thread gets it.
+__device__ __forceinline__ int64_t block_prefix(const int32_t* __restrict__ len, int r) {
+  __shared__ int64_t part[16];
+  int64_t s = 0;
+  for (int j = threadIdx.x; j < r; j += blockDim.x) s += len[j];
+  s = wave_sum_i64(s);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) part[w] = s;
+  __syncthreads();
+  int64_t t = 0;
+  for (int i = 0; i < nw; ++i) t += part[i];
+  return t;
+}
+
+}  // namespace pkv

@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// element formats of io tensors and the KV pool
+enum : int { F_FP32 = 0, F_BF16 = 1, F_FP8 = 2 };
+
+struct AppendArgs {
+  const void* q;            // may be null (then q_out is null)
+  const void* k;
+  const void* v;
+  int64_t q_stride, kv_stride;   // elements
+  const double* cos_sin;    // [max_pos][R/2][2]
+  int32_t max_pos;
+  void* q_out;
+  void* pool;
+  const int32_t* ctx_len;   // device n_r
+  const int32_t* seq_len;   // device S_r
+  const int32_t* table;     // device [B][mbps]
+  int32_t B, N, H, Hkv, D, T, R, mbps;
+  int64_t num_blocks;
+  double inv_k_scale, inv_v_scale;   // fp8 cache: 1/scale; otherwise 1
+  int32_t io_fmt, kv_fmt, rope;
+  int32_t max_n;            // largest n_r (grid extent)
+};
+
+struct AttnArgs {
+  const void* q;
+  int64_t q_stride;         // elements
+  const void* pool;
+  void* out;
+  const int32_t* ctx_len;
+  const int32_t* seq_len;
+  const int32_t* table;
+  int32_t B, N, H, Hkv, D, T, mbps;
+  int64_t num_blocks;
+  float scale_log2;         // softmax scale * log2(e)
+  float k_scale, v_scale;   // dequantisation scales (1 unless fp8)
+  int32_t io_fmt, kv_fmt;
+  int32_t req_begin, req_end;    // requests [begin, end) handled by this launch
+  int32_t row_begin;             // packed row of request req_begin
+  int32_t max_n;                 // largest n_r among the handled requests
+  // split-KV decode
+  int32_t chunk, max_splits;
+  float* ws_ml;             // [num_gen][H][max_splits][2]
+  float* ws_o;              // [num_gen][H][max_splits][D]
+};
+
+hipError_t launch_rope_table(double base, int32_t rot, int32_t max_pos, double* cos_sin, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
+
+}  // namespace pkv

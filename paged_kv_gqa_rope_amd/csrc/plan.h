@@ -1,0 +1,56 @@
+// Host-side validation and launch planning.  No HIP types here, so this part of the
+// library is ordinary C++ and its rules can be exercised without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Derived facts about one batch, computed on the host from the host copies.
+struct BatchPlan {
+  int32_t B = 0, N = 0;
+  int32_t num_ctx = 0, num_gen = 0;
+  int32_t ctx_tokens = 0;     // packed rows owned by context requests (they come first)
+  int32_t max_ctx_n = 0;      // longest context chunk
+  int32_t max_n = 0;          // largest n_r over all requests
+  int32_t max_S = 0;          // largest S_r over all requests
+  int32_t max_S_gen = 0;      // largest S_r over generation requests
+  int64_t ctx_pairs = 0;      // causal (query, key) pairs of context rows
+  int64_t gen_keys = 0;       // sum of S_r over generation requests
+  // split-KV decode policy (generation rows on the MFMA decode path)
+  bool fast_decode = false;
+  bool fast_prefill = false;
+  int32_t chunk = 0;          // keys per split, a multiple of tokens_per_block
+  int32_t max_splits = 0;     // max over generation requests of ceil(S_r / chunk)
+  int64_t decode_items = 0;   // (request, kv head, split) work items
+  // workspace layout (bytes)
+  size_t ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
+};
+
+// Numeric limits of the split policy.
+constexpr int32_t kMaxSplits = 128;       // splits per generation request
+constexpr int32_t kDefaultChunk = 512;    // keys per split before balancing
+constexpr int64_t kTargetDecodeItems = 2048;
+// Which specialised kernels this build dispatches to (the generic kernel covers the rest).
+constexpr bool kHaveFastDecode = false;
+constexpr bool kHaveFastPrefill = false;
+
+int validate_desc(const pkv_attn_desc* d, std::string& err);
+int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* plan, std::string& err);
+
+// Kernel selection for a validated desc (pure function of the desc).
+bool desc_fast_decode(const pkv_attn_desc& d);
+bool desc_fast_prefill(const pkv_attn_desc& d);
+
+// Decode split policy + workspace layout for a validated batch.
+void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* plan);
+size_t workspace_upper_bound(const pkv_attn_desc& d, int32_t max_num_requests, int32_t max_seq_len);
+
+inline int32_t io_bytes(int32_t dt) { return dt == PKV_FP32 ? 4 : dt == PKV_BF16 ? 2 : 1; }
+inline int32_t rot_dim(const pkv_attn_desc& d) { return d.rotary_dim ? d.rotary_dim : d.head_dim; }
+
+}  // namespace pkv

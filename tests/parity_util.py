@@ -1,0 +1,57 @@
+"""Shared checks for the GPU parity tests (HIP path vs the CPU oracle)."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import codecs
+
+# Attention bars.  bf16 io: max-abs 2e-2 and mean-abs 2e-3; fp8 cache: max-abs 6e-2.
+# fp32 io/cache is held to 1e-4.  Because outputs shrink as contexts grow, every case
+# must also pass a relative L2 error <= 1e-2 and a per-row cosine >= 0.999.
+BARS = {
+    ("fp32", "fp32"): dict(max_abs=1e-4, mean_abs=1e-5),
+    ("bf16", "bf16"): dict(max_abs=2e-2, mean_abs=2e-3),
+    ("bf16", "fp8_e4m3"): dict(max_abs=6e-2, mean_abs=6e-3),
+}
+REL_L2 = 1e-2
+MIN_COS = 0.999
+
+
+def io_values(bits: np.ndarray, io_dtype: str) -> np.ndarray:
+    return codecs.decode(bits, io_dtype)
+
+
+def compare_attention(got_bits: np.ndarray, ref: np.ndarray, shape, label: str = "") -> dict:
+    """got_bits: GPU output in io representation [rows, heads, D]; ref: oracle fp64."""
+    got = io_values(got_bits, shape.io_dtype)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite GPU outputs"
+    err = np.abs(got - ref)
+    bars = BARS[(shape.io_dtype, shape.kv_dtype)]
+    stats = dict(max_abs=float(err.max()), mean_abs=float(err.mean()),
+                 rel_l2=float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)))
+    g2 = got.reshape(-1, got.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    cos = np.sum(g2 * r2, axis=1) / np.maximum(np.linalg.norm(g2, axis=1) * np.linalg.norm(r2, axis=1), 1e-300)
+    stats["min_cos"] = float(cos.min())
+    msg = f"{label}: {stats}"
+    assert stats["max_abs"] <= bars["max_abs"], msg
+    assert stats["mean_abs"] <= bars["mean_abs"], msg
+    assert stats["rel_l2"] <= REL_L2, msg
+    assert stats["min_cos"] >= MIN_COS, msg
+    return stats
+
+
+def bits_of(arr: np.ndarray) -> np.ndarray:
+    return arr.view({4: np.uint32, 2: np.uint16, 1: np.uint8}[arr.dtype.itemsize])
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, label: str):
+    g, w = bits_of(np.ascontiguousarray(got)), bits_of(np.ascontiguousarray(want))
+    assert g.shape == w.shape, (label, g.shape, w.shape)
+    bad = np.nonzero(g != w)
+    n = bad[0].size
+    if n:
+        first = tuple(int(x[0]) for x in bad)
+        raise AssertionError(f"{label}: {n} of {g.size} elements differ; first at {first}: "
+                             f"got {int(g[first]):#x} want {int(w[first]):#x}")

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, at sizes the
+oracle finishes in seconds (several blocks, ragged tails, every workload shape)."""
+import numpy as np
+import pytest
+import torch
+
+from batch_util import as_crafted, copy_values, crafted
+from oracle import codecs as C
+from oracle import rope as OR
+from oracle import step as O
+from parity_util import assert_bits_equal, bits_of, compare_attention
+from workloads import synth as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from paged_kv_gqa_rope_amd import _lib, harness
+    _lib.lib()                       # raises if the library was not built
+    return harness
+
+
+def case(*a):
+    print("CASE", *a, flush=True)
+
+
+def sentinel(fmt):
+    return int(np.iinfo(O.BITS[fmt]).max)
+
+
+def run_step(H, batch, **kw):
+    st = H.PagedStep(batch, **kw)
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+def test_rope_table_matches_oracle(H):
+    from paged_kv_gqa_rope_amd import _lib as L
+    for base, rot, max_pos in [(1e4, 64, 64), (1e4, 128, 4200), (5e5, 128, 33000), (5e5, 32, 100)]:
+        case("rope", base, rot, max_pos)
+        t = torch.empty((max_pos, rot // 2, 2), dtype=torch.float64, device="cuda")
+        L.check(L.pkv_rope_cos_sin(base, rot, max_pos, t.data_ptr(), torch.cuda.current_stream().cuda_stream))
+        g = t.cpu().numpy()
+        c, s = OR.neox_tables(base, rot, max_pos)
+        # angles reach 3.3e4 rad, where one ulp of theta_j moves the angle by ~4e-12
+        assert np.max(np.abs(g[..., 0] - c)) <= 1e-11
+        assert np.max(np.abs(g[..., 1] - s)) <= 1e-11
+        exact = np.mean((g[..., 0] == c) & (g[..., 1] == s))
+        print(f"rope base={base} rot={rot} max_pos={max_pos}: {exact:.4f} of entries bit-identical")
+
+
+@pytest.mark.parametrize("k", W.SMALL_WORKLOADS)
+def test_small_workload_append_is_bit_exact(H, k):
+    b = W.small_workload(k)
+    case("append", b.label, b.shape.name)
+    st = run_step(H, b)
+    ref_q = np.concatenate([O.append_request(b, r, O.tables(b))[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    want = O.expected_pool(b, sentinel(b.shape.kv_dtype))
+    assert_bits_equal(bits_of(st.pool_host()), want, "pool (history + new tokens + untouched sentinel)")
+
+
+@pytest.mark.parametrize("k", W.SMALL_WORKLOADS)
+def test_small_workload_attention_matches_oracle(H, k):
+    b = W.small_workload(k)
+    case("attention", b.label, b.shape.name)
+    st = run_step(H, b)
+    ref = O.run(b)
+    stats = compare_attention(st.out_host(), ref["out"], b.shape, b.label)
+    print(b.label, stats)
+
+
+def test_full_tiny_workload(H):
+    b = W.workload(1)
+    case("full", b.label)
+    st = run_step(H, b)
+    ref = O.run(b)
+    assert_bits_equal(st.q_out_host(), ref["q_out"], "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(b.shape.kv_dtype)), "pool")
+    print(compare_attention(st.out_host(), ref["out"], b.shape, b.label))
+
+
+@pytest.mark.parametrize("k", [2, 4, 5])
+def test_outputs_are_bitwise_invariant_to_block_placement_and_reruns(H, k):
+    b = W.small_workload(k)
+    outs = []
+    for seed in (7, 8, 9):
+        other = W.make_batch(b.shape, ctx=[(int(n), int(s - n)) for n, s, t in
+                                          zip(b.context_lengths, b.sequence_lengths, b.request_types) if t == 0],
+                             gen_past=[int(s - 1) for s, t in zip(b.sequence_lengths, b.request_types) if t == 1],
+                             seed=seed, pool_blocks_min=b.num_pool_blocks + 5)
+        assert not np.array_equal(other.block_table, b.block_table)
+        pb = copy_values(b, as_crafted(b, table=other.block_table, pool_blocks=other.num_pool_blocks))
+        case("placement", b.label, seed)
+        st = run_step(H, pb)
+        outs.append(st.out_host().copy())
+        assert st.forward() == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(st.out_host()), bits_of(outs[-1])), "rerun differs"
+    for o in outs[1:]:
+        assert np.array_equal(bits_of(o), bits_of(outs[0])), "block placement changes the output"
+
+
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8_E4M3])
+def test_gqa_equals_mha_with_replicated_kv_heads(H, kv):
+    G = 4
+    gqa = W.Shape("gqa", 16, 4, 128, 64, W.BF16, kv, 5e5, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    mha = W.Shape("mha", 16, 16, 128, 64, W.BF16, kv, 5e5, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    src = W.make_batch(gqa, ctx=[(150, 64)], gen_past=[300, 77, 1000], seed=31)
+    a = as_crafted(src)
+    copy_values(src, a)
+    m = as_crafted(src, shape=mha)
+    R = range(src.num_requests)
+    rep = lambda x: np.repeat(x, G, axis=1)
+    m.set_values([src.new_q(r) for r in R], [rep(src.new_k(r)) for r in R], [rep(src.new_v(r)) for r in R],
+                 [rep(src.hist_k(r)) for r in R], [rep(src.hist_v(r)) for r in R])
+    case("gqa-vs-mha", kv)
+    og = run_step(H, a).out_host()
+    om = run_step(H, m).out_host()
+    ref = O.run(a)["out"]
+    compare_attention(og, ref, gqa, "gqa")
+    compare_attention(om, ref, mha, "mha")
+    d = np.abs(C.decode(og, W.BF16) - C.decode(om, W.BF16))
+    assert d.max() <= 2 ** -7 * np.abs(ref).max() + 1e-6
+
+
+def test_chunked_prefill_equals_unchunked(H):
+    sh = W.SHAPES[3]
+    full = W.make_batch(sh, ctx=[(200, 0)], seed=41)
+    st_full = run_step(H, full, fill_history=False)
+    table = full.block_table
+    parts, outs, pool = [(0, 128), (128, 192), (192, 200)], [], None
+    for lo, hi in parts:
+        c = W.Batch(sh, full.seed, np.array([0], np.int32), np.array([hi - lo], np.int32),
+                    np.array([hi], np.int32), table, full.num_pool_blocks)
+        cc = as_crafted(c)
+        cc.set_values([full.new_q(0)[lo:hi]], [full.new_k(0)[lo:hi]], [full.new_v(0)[lo:hi]],
+                      [full.new_k(0)[:0]], [full.new_v(0)[:0]])
+        case("chunk", lo, hi)
+        st = H.PagedStep(cc, fill_history=False, sentinel=pool is None)
+        if pool is not None:
+            st.pool = pool                       # earlier chunks' K/V are already in the cache
+        st.step()
+        torch.cuda.synchronize()
+        pool = st.pool
+        outs.append(st.out_host().copy())
+    got = np.concatenate(outs)
+    assert_bits_equal(bits_of(pool.cpu().view(torch.int16).numpy()), bits_of(st_full.pool.cpu().view(torch.int16).numpy()),
+                      "chunked cache")
+    ref = O.run(full)["out"]
+    compare_attention(got, ref, sh, "chunked")
+    diff = np.abs(C.decode(got, W.BF16) - C.decode(st_full.out_host(), W.BF16))
+    assert diff.max() <= 2 ** -7 * np.abs(ref).max() + 1e-6
+
+
+def test_zero_keys_average_exactly_the_visible_values(H):
+    # K = 0 makes every visible score equal, so each row must average V over
+    # positions 0..m: pins causal length, past offset and the block-table gather.
+    sh = W.Shape("zk", 8, 2, 128, 64, W.BF16, W.BF16, 1e4)
+    def val(t):
+        return np.float32((t % 16) / 4.0)
+    def fill(tag, r, rows, heads):
+        if tag in ("v", "hv"):
+            base = 0 if tag == "hv" else int(b_len[r][1])
+            x = np.array([val(base + i) for i in range(rows)], np.float32)[:, None, None] * np.ones((1, heads, 128), np.float32)
+            return (x.view(np.uint32) >> 16).astype(np.uint16)
+        if tag == "q":
+            rng = np.random.default_rng(r)
+            x = rng.standard_normal((rows, heads, 128)).astype(np.float32)
+            return (x.view(np.uint32) >> 16).astype(np.uint16)
+        return np.zeros((rows, heads, 128), np.uint16)
+    ctx, gen = [(100, 0), (70, 128), (1, 0)], [0, 63, 64, 700]
+    b_len = [(n, p) for n, p in ctx] + [(1, p) for p in gen]
+    b = crafted(sh, ctx=ctx, gen_past=gen, seed=5, fill=fill)
+    case("zero-keys")
+    out = C.decode(run_step(H, b).out_host(), W.BF16)
+    row = 0
+    for (n, p) in b_len:
+        for i in range(n):
+            m = p + i
+            want = np.mean([val(t) for t in range(m + 1)])
+            np.testing.assert_allclose(out[row], want, rtol=2 ** -8, atol=0, err_msg=f"row {row} m={m}")
+            row += 1
+
+
+def test_empty_batch_launches_nothing(H):
+    from paged_kv_gqa_rope_amd import _lib as L
+    sh = W.SHAPES[4]
+    b = W.make_batch(sh, seed=1)
+    lens = H._Lengths(b.request_types, b.context_lengths, b.sequence_lengths, np.zeros((0, 1), np.int32), 1, "cuda")
+    d = H.make_desc(sh)
+    s = torch.cuda.current_stream().cuda_stream
+    assert L.pkv_append_rope(d, lens.desc, None, 0, None, None, 0, None, 0, None, None, s) == 0
+    assert L.pkv_attention_forward(d, lens.desc, None, 0, None, None, None, 0, s) == 0

@@ -17,42 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 # ------------------------------------------------------------------ helpers
-class Crafted(W.Batch):
-    """A batch whose values are given explicitly (io representation)."""
-
-    def set_values(self, q, k, v, hk, hv):
-        self._vals = dict(q=q, k=k, v=v, hk=hk, hv=hv)
-        return self
-
-    def new_q(self, r):
-        return self._vals["q"][r]
-
-    def new_k(self, r):
-        return self._vals["k"][r]
-
-    def new_v(self, r):
-        return self._vals["v"][r]
-
-    def hist_k(self, r):
-        return self._vals["hk"][r]
-
-    def hist_v(self, r):
-        return self._vals["hv"][r]
-
-
-def crafted(shape, ctx=(), gen_past=(), seed=0, fill=None):
-    b = W.make_batch(shape, ctx=ctx, gen_past=gen_past, seed=seed)
-    cb = Crafted(**{f: getattr(b, f) for f in ("shape", "seed", "request_types", "context_lengths",
-                                                "sequence_lengths", "block_table", "num_pool_blocks", "label")})
-    H, Hkv, D = shape.num_heads, shape.num_kv_heads, shape.head_dim
-    n, p = b.context_lengths, b.past_lengths
-    fill = fill or (lambda tag, r, rows, heads: np.zeros((rows, heads, D), np.float32))
-    q = [fill("q", r, int(n[r]), H) for r in range(b.num_requests)]
-    k = [fill("k", r, int(n[r]), Hkv) for r in range(b.num_requests)]
-    v = [fill("v", r, int(n[r]), Hkv) for r in range(b.num_requests)]
-    hk = [fill("hk", r, int(p[r]), Hkv) for r in range(b.num_requests)]
-    hv = [fill("hv", r, int(p[r]), Hkv) for r in range(b.num_requests)]
-    return cb.set_values(q, k, v, hk, hv)
+from batch_util import Crafted, crafted  # noqa: E402
 
 
 def rand_unit(rng, shape):
