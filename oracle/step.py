@@ -119,13 +119,17 @@ def run(batch):
     }
 
 
+BITS = {codecs.FP32: np.uint32, codecs.BF16: np.uint16, codecs.FP8_E4M3: np.uint8}
+
+
 def expected_pool(batch, sentinel, include_new: bool = True, include_history: bool = True):
-    """The whole paged pool [nb, 2, T, Hkv, D] (cache representation) after the
-    history fill and the step's append; slots nobody writes hold ``sentinel``."""
+    """The whole paged pool [nb, 2, T, Hkv, D] as stored bit patterns (uint32 / uint16 /
+    uint8 for fp32 / bf16 / fp8) after the history fill and the step's append; slots
+    nobody writes hold the bit pattern ``sentinel``."""
     sh = batch.shape
     T = sh.tokens_per_block
-    pool = np.full((batch.num_pool_blocks, 2, T, sh.num_kv_heads, sh.head_dim), sentinel,
-                   dtype=codecs.storage_dtype(sh.kv_dtype))
+    bits = BITS[sh.kv_dtype]
+    pool = np.full((batch.num_pool_blocks, 2, T, sh.num_kv_heads, sh.head_dim), sentinel, dtype=bits)
     tabs = tables(batch)
     for r in range(batch.num_requests):
         p = int(batch.past_lengths[r])
@@ -142,6 +146,6 @@ def expected_pool(batch, sentinel, include_new: bool = True, include_history: bo
                 continue
             blk = batch.block_table[r, pos // T]
             slot = pos % T
-            pool[blk, 0, slot] = ks
-            pool[blk, 1, slot] = vs
+            pool[blk, 0, slot] = np.asarray(ks).view(bits)
+            pool[blk, 1, slot] = np.asarray(vs).view(bits)
     return pool
