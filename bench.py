@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark one step (RoPE + KV append, then attention) of the paged-KV GQA path.
+
+Prints ONE JSON line.  ``value`` is the whole-step throughput of the decode
+workload (64 generation requests, cached lengths 512..4096, 32 q heads = 32 KV
+heads, head_dim 128, 64-token blocks, bf16): algorithmic bytes of the step per
+second, inputs resident in HBM.  The prefill, mixed and fp8-decode workloads
+are reported under ``workloads``.  Kernel durations come from the library's own
+HIP events recorded on the launch stream over the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 2,3,4,5]
+                       [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak; tok/s"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+BYTES = {"fp32": 4, "bf16": 2, "fp8_e4m3": 1}
+HEADLINE = 2
+
+
+def algorithmic(batch) -> dict:
+    """Algorithmic work of one step (see the formulas in the design notes)."""
+    import numpy as np
+    sh = batch.shape
+    H, Hkv, D, T = sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.tokens_per_block
+    bio, bkv = BYTES[sh.io_dtype], BYTES[sh.kv_dtype]
+    gen = batch.request_types == 1
+    S = batch.sequence_lengths.astype(np.int64)
+    n = batch.context_lengths.astype(np.int64)
+    p = S - n
+    decode_bytes = int(np.sum(S[gen] * Hkv * D * 2 * bkv + H * D * 2 * bio + 4 * ((S[gen] + T - 1) // T)))
+    ctx = ~gen
+    ctx_flops = int(4 * D * H * np.sum(n[ctx] * p[ctx] + n[ctx] * (n[ctx] + 1) // 2))
+    N = int(n.sum())
+    R = sh.rot_dim
+    append_bytes = N * ((H + 2 * Hkv) * D * bio + H * D * bio + 2 * Hkv * D * bkv + (R // 2) * 16)
+    return dict(decode_bytes=decode_bytes, ctx_flops=ctx_flops, append_bytes=append_bytes, tokens=N,
+                gen_keys=int(S[gen].sum()), num_gen=int(gen.sum()), num_ctx=int(ctx.sum()))
+
+
+def describe(batch) -> str:
+    sh = batch.shape
+    import numpy as np
+    gen = batch.request_types == 1
+    parts = []
+    if (~gen).any():
+        parts.append(f"{int((~gen).sum())} context requests (n={sorted(set(batch.context_lengths[~gen].tolist()))}, "
+                     f"cached={sorted(set(batch.past_lengths[~gen].tolist()))})")
+    if gen.any():
+        parts.append(f"{int(gen.sum())} generation requests (cached {int(batch.past_lengths[gen].min())}.."
+                     f"{int(batch.past_lengths[gen].max())}, sum S={int(batch.sequence_lengths[gen].sum())})")
+    return (f"{sh.name}: " + " + ".join(parts) + f"; H={sh.num_heads} Hkv={sh.num_kv_heads} D={sh.head_dim} "
+            f"T={sh.tokens_per_block} io={sh.io_dtype} kv={sh.kv_dtype} rope_base={sh.rope_theta:g}")
+
+
+def run_workload(k: int, steps: int, warmup: int) -> dict:
+    import torch
+
+    from paged_kv_gqa_rope_amd import _lib as L
+    from paged_kv_gqa_rope_amd.harness import PagedStep
+    from workloads import synth as W
+
+    batch = W.workload(k)
+    t0 = time.time()
+    st = PagedStep(batch, sentinel=False)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    for _ in range(warmup):
+        st.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    beg, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L.check(L.pkv_kernel_timing_enable(True))
+    torch.cuda.synchronize()
+    beg.record(stream)
+    for _ in range(steps):
+        st.step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    timings = L.pkv_kernel_timings()
+    L.check(L.pkv_kernel_timing_enable(False))
+    ms_per_step = beg.elapsed_time(end) / steps
+    per_kernel: dict[str, list[float]] = {}
+    for name, ms in timings:
+        per_kernel.setdefault(name, []).append(ms)
+    kern = {n: dict(avg_us=1e3 * sum(v) / len(v), launches=len(v)) for n, v in per_kernel.items()}
+    w = algorithmic(batch)
+    step_bytes = w["append_bytes"] + w["decode_bytes"]
+    res = dict(workload=describe(batch), setup_s=round(setup_s, 2), ms_per_step=ms_per_step,
+               tok_per_s=w["tokens"] / (ms_per_step * 1e-3), kernels=kern, work=w)
+    if "decode_split" in kern:
+        t = (kern["decode_split"]["avg_us"] + kern.get("decode_combine", {"avg_us": 0.0})["avg_us"]) * 1e-6
+        res["decode_GBps"] = w["decode_bytes"] / t / 1e9
+        res["decode_split_GBps"] = w["decode_bytes"] / (kern["decode_split"]["avg_us"] * 1e-6) / 1e9
+    for name in ("prefill_mfma", "attn_generic_ctx"):
+        if name in kern:
+            res["prefill_TFLOPs"] = w["ctx_flops"] / (kern[name]["avg_us"] * 1e-6) / 1e12
+            res["prefill_kernel"] = name
+    if "append_rope" in kern:
+        res["append_GBps"] = w["append_bytes"] / (kern["append_rope"]["avg_us"] * 1e-6) / 1e9
+    res["step_GBps"] = step_bytes / (ms_per_step * 1e-3) / 1e9
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline_for(res: dict) -> dict:
+    kern = res["kernels"]
+    w = res["work"]
+    if "decode_split" in kern and w["decode_bytes"] > 0 and w["ctx_flops"] == 0:
+        ach = w["decode_bytes"] / (kern["decode_split"]["avg_us"] * 1e-6) / 1e9
+        return dict(kernel="decode_split", bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBS, traffic=None)
+    name = "prefill_mfma" if "prefill_mfma" in kern else "attn_generic_ctx"
+    ach = w["ctx_flops"] / (kern[name]["avg_us"] * 1e-6) / 1e12
+    return dict(kernel=name, bound="mfma", achieved=ach, peak=BF16_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=ach / BF16_DENSE_PEAK_TFLOPS, traffic=None)
+
+
+def cpu_baseline(k: int = HEADLINE, budget_s: float = 12.0) -> dict:
+    """The oracle (fp64 numpy, untuned) on a bounded sample of the decode workload."""
+    import numpy as np
+
+    from oracle import step as O
+    from workloads import synth as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    b = W.workload(k)
+    sh = b.shape
+    tabs = O.tables(b)
+    t0 = time.perf_counter()
+    done, kv_bytes = 0, 0
+    for r in range(b.num_requests):
+        O.attention_request(b, r, tabs)
+        S = int(b.sequence_lengths[r])
+        kv_bytes += S * sh.num_kv_heads * sh.head_dim * 2 * BYTES[sh.kv_dtype]
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=kv_bytes / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"append+attention of generation requests 0..{done - 1} of the {b.num_requests}-request "
+                       f"decode workload (all {sh.num_heads} heads), {el:.1f} s, fp64 numpy; "
+                       f"{done / el:.2f} requests/s")
+
+
+def copy_calibration(gib: float = 1.0, reps: int = 5):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": reps}),
+          file=sys.stderr)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="2,3,4,5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration()
+    ks = [int(x) for x in args.workloads.split(",") if x]
+    results = {}
+    for k in ks:
+        print(f"[bench] workload {k} ...", file=sys.stderr, flush=True)
+        results[k] = run_workload(k, args.steps, args.warmup)
+        print(f"[bench] workload {k}: {results[k]['ms_per_step']:.3f} ms/step "
+              f"{ {n: round(v['avg_us'], 1) for n, v in results[k]['kernels'].items()} }", file=sys.stderr, flush=True)
+    head_k = HEADLINE if HEADLINE in results else ks[0]
+    head = results[head_k]
+    line = {
+        "metric": METRIC,
+        "value": head["step_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block permutation)",
+        "config": {"workload": head["workload"], "tok_per_s": head["tok_per_s"],
+                   "decode_GBps": head.get("decode_GBps"), "pct_hbm_peak": 100 * head.get("decode_GBps", 0) / HBM_PEAK_GBS},
+        "roofline": roofline_for(head),
+    }
+    others = {}
+    for k, r in results.items():
+        if k == head_k:
+            continue
+        o = dict(workload=r["workload"], ms_per_step=r["ms_per_step"], tok_per_s=r["tok_per_s"],
+                 kernels_us={n: round(v["avg_us"], 2) for n, v in r["kernels"].items()})
+        for f in ("decode_GBps", "prefill_TFLOPs", "append_GBps", "prefill_kernel"):
+            if f in r:
+                o[f] = r[f]
+        if "decode_GBps" in r:
+            o["decode_pct_hbm_peak"] = 100 * r["decode_GBps"] / HBM_PEAK_GBS
+        if "prefill_TFLOPs" in r:
+            o["prefill_pct_bf16_peak"] = 100 * r["prefill_TFLOPs"] / BF16_DENSE_PEAK_TFLOPS
+        o["roofline"] = roofline_for(r)
+        others[f"workload_{k}"] = o
+    line["workloads"] = others
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -219,6 +219,8 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
   a.Hkv = desc->num_kv_heads;
   a.D = D;
   a.T = desc->tokens_per_block;
+  a.tshift = 0;
+  while ((1 << a.tshift) < a.T) ++a.tshift;
   a.mbps = batch->max_blocks_per_seq;
   a.num_blocks = batch->num_pool_blocks;
   const double scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0 / std::sqrt(static_cast<double>(D));

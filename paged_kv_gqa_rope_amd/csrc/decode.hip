@@ -37,7 +37,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTile = 64;          // keys per wave iteration
+constexpr int kTile = 32;          // keys per wave iteration
 constexpr int kD = 128;            // head_dim handled here
 constexpr int kVStride = 136;      // LDS row stride (bf16 elements) of a staged V tile
 
@@ -58,15 +58,24 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Registers of one 32-key tile in flight: K in MFMA A-operand layout (bf16: 2 key
+// blocks x 4 dim steps; fp8: the raw codes, 2 x 32 bytes) and V rows for the LDS copy.
 template <int KV>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnArgs a) {
+struct TileRegs {
+  uint4 k[2][4];
+  uint4 v[KV == F_BF16 ? 8 : 4];
+};
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, rg = blockIdx.z;
   const int r = a.req_begin + rg;
   const int S = a.seq_len[r];
   const int k0 = split * a.chunk;
   if (k0 >= S || split >= a.max_splits) return;               // uniform over the block
   const int kend = min(k0 + a.chunk, S);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
   const int G = a.H / a.Hkv;
   const int64_t row = static_cast<int64_t>(a.row_begin) + rg;
@@ -89,77 +98,94 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnArgs a) {
     }
   }
   const float xscale = a.scale_log2 * a.k_scale;
-
   float m_run = -INFINITY, l_run = 0.f;                         // for head li
   f32x4 o[8];                                                   // O[head lg*4+i][dim nb*16+li]
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = (kend - k0 + kTile - 1) / kTile;
+  const int tshift = a.tshift, tmask = a.T - 1;
+  const int last_blk = (kend - 1) >> tshift;
+  const int64_t blk_elems = 2 * static_cast<int64_t>(a.T) * kv_row;   // one block: K and V of T slots
   uint16_t* vt = vtile[wave];
-  for (int t = wave; t < ntiles; t += kWaves) {
-    const int tb = k0 + t * kTile;
-    // ---- K in A-operand layout: key tb + kb*16 + li, dims lg*32 .. lg*32+31
-    bf16x8 kf[4][4];
+
+  // Block IDs of a tile: tiles are 32-aligned and T is a power of two >= 16, so a tile
+  // lies in one block (T >= 32) or covers two (T = 16).  Read two tiles ahead.
+  auto fetch_ids = [&](int tile, int32_t (&raw)[2]) {
+    const int kb0 = (k0 + tile * kTile) >> tshift;
+    raw[0] = table[min(kb0, last_blk)];
+    raw[1] = table[min(kb0 + 1, last_blk)];
+  };
+  // Issue every load of tile `tile` (ids already resolved) into `R`.
+  auto issue = [&](int tile, const int32_t (&rawid)[2], TileRegs<KV>& R) {
+    const int tb = k0 + tile * kTile;
+    const int kb0 = tb >> tshift;
+    int32_t id0 = __builtin_amdgcn_readfirstlane(rawid[0]);
+    int32_t id1 = __builtin_amdgcn_readfirstlane(rawid[1]);
+    id0 = (id0 >= 0 && id0 < a.num_blocks) ? id0 : 0;
+    id1 = (id1 >= 0 && id1 < a.num_blocks) ? id1 : 0;
+    auto base_of = [&](int key) -> int64_t {                  // element offset of (block, K, slot)
+      const int32_t id = ((key >> tshift) == kb0) ? id0 : id1;
+      return static_cast<int64_t>(id) * blk_elems + static_cast<int64_t>(key & tmask) * kv_row +
+             static_cast<int64_t>(g) * kD;
+    };
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
       const int key = min(tb + kb * 16 + li, kend - 1);        // clamp: never read unwritten slots
-      int32_t blk = table[key / a.T];
-      blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-      const int64_t base = ((static_cast<int64_t>(blk) * 2) * a.T + key % a.T) * kv_row +
-                           static_cast<int64_t>(g) * kD + lg * 32;
       if constexpr (KV == F_BF16) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base);
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base_of(key) + lg * 32);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(p[ks]);
+        for (int ks = 0; ks < 4; ++ks) R.k[kb][ks] = p[ks];
       } else {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base);
-        const uint4 c0 = p[0], c1 = p[1];
-        kf[kb][0] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c0.x, c0.y)));
-        kf[kb][1] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c0.z, c0.w)));
-        kf[kb][2] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c1.x, c1.y)));
-        kf[kb][3] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(c1.z, c1.w)));
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base_of(key) + lg * 32);
+        R.k[kb][0] = p[0];
+        R.k[kb][1] = p[1];
       }
     }
-    // ---- V rows, coalesced: bf16 16 keys x 4 lanes... (16 lanes per 256-byte row)
-    uint4 vr[16];
-    if constexpr (KV == F_BF16) {
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int key = min(tb + it * 4 + lg, kend - 1);
-        int32_t blk = table[key / a.T];
-        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-        const int64_t base = ((static_cast<int64_t>(blk) * 2 + 1) * a.T + key % a.T) * kv_row +
-                             static_cast<int64_t>(g) * kD + li * 8;
-        vr[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base);
-      }
-    } else {
-      // 8 lanes x 16 codes per 128-byte row, 8 keys per load
+    const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
+    if constexpr (KV == F_BF16) {                              // 16 lanes per 256-byte row
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
+        const int key = min(tb + it * 4 + lg, kend - 1);
+        R.v[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base_of(key) + vofs + li * 8);
+      }
+    } else {                                                   // 8 lanes per 128-byte row
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
         const int key = min(tb + it * 8 + lane / 8, kend - 1);
-        int32_t blk = table[key / a.T];
-        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-        const int64_t base = ((static_cast<int64_t>(blk) * 2 + 1) * a.T + key % a.T) * kv_row +
-                             static_cast<int64_t>(g) * kD + (lane % 8) * 16;
-        const uint4 c = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base);
-        vr[2 * it] = e4m3x8_to_bf16x8(make_uint2(c.x, c.y));
-        vr[2 * it + 1] = e4m3x8_to_bf16x8(make_uint2(c.z, c.w));
+        R.v[it] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base_of(key) + vofs + (lane % 8) * 16);
       }
     }
-    // ---- scores S^T[key][head]: lane holds head li, keys tb + kb*16 + lg*4 + i
-    f32x4 sacc[4];
+  };
+  // Online-softmax update and O += P V for tile `tile` held in `R`.
+  auto compute = [&](int tile, const TileRegs<KV>& R) {
+    const int tb = k0 + tile * kTile;
+    bf16x8 kf[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (KV == F_BF16) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(R.k[kb][ks]);
+      } else {
+        kf[kb][0] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][0].x, R.k[kb][0].y)));
+        kf[kb][1] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][0].z, R.k[kb][0].w)));
+        kf[kb][2] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][1].x, R.k[kb][1].y)));
+        kf[kb][3] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][1].z, R.k[kb][1].w)));
+      }
+    }
+    // scores S^T[key][head]: lane holds head li, keys tb + kb*16 + lg*4 + i
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[ks], sacc[kb], 0, 0, 0);
     }
-    float x[16];
+    float x[8];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = tb + kb * 16 + lg * 4 + i;
@@ -172,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnArgs a) {
     const float alpha = exp2f(m_run - m_new);
     float lsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       x[e] = exp2f(x[e] - m_new);
       lsum += x[e];
     }
@@ -187,50 +213,66 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ah;
     }
-    // P as the A operand: row = head li, k-slot j <-> key 32*ks2 + (j/4)*16 + lg*4 + j%4
-    bf16x8 pa[2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint4 u;
-      uint32_t* w = reinterpret_cast<uint32_t*>(&u);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j0 = 2 * jj, j1 = 2 * jj + 1;
-        const float p0 = x[(2 * ks2 + j0 / 4) * 4 + j0 % 4];
-        const float p1 = x[(2 * ks2 + j1 / 4) * 4 + j1 % 4];
-        w[jj] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
-      }
-      pa[ks2] = as_bf16x8(u);
-    }
-    // ---- V tile into this wave's LDS region (row-major [key][dim])
+    // P as the A operand: row = head li, k-slot j <-> key (j/4)*16 + lg*4 + j%4
+    uint4 pu;
+    pu.x = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
+    pu.y = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
+    pu.z = f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16);
+    pu.w = f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16);
+    const bf16x8 pa = as_bf16x8(pu);
+    // V tile into this wave's LDS region (row-major [key][dim], bf16)
     wave_lds_fence();
     if constexpr (KV == F_BF16) {
 #pragma unroll
-      for (int it = 0; it < 16; ++it)
-        *reinterpret_cast<uint4*>(vt + (it * 4 + lg) * kVStride + li * 8) = vr[it];
+      for (int it = 0; it < 8; ++it)
+        *reinterpret_cast<uint4*>(vt + (it * 4 + lg) * kVStride + li * 8) = R.v[it];
     } else {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 4; ++it) {
         uint16_t* d = vt + (it * 8 + lane / 8) * kVStride + (lane % 8) * 16;
-        *reinterpret_cast<uint4*>(d) = vr[2 * it];
-        *reinterpret_cast<uint4*>(d + 8) = vr[2 * it + 1];
+        *reinterpret_cast<uint4*>(d) = e4m3x8_to_bf16x8(make_uint2(R.v[it].x, R.v[it].y));
+        *reinterpret_cast<uint4*>(d + 8) = e4m3x8_to_bf16x8(make_uint2(R.v[it].z, R.v[it].w));
       }
     }
     wave_lds_fence();
-    // ---- O += P V: B operand = V[keys][dims nb*16 .. +15] read transposed
+    // O += P V: B operand = V[keys][dims nb*16 .. +15] read transposed
+    const int krow = lg * 4 + li / 4;
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const int krow = ks2 * 32 + lg * 4 + li / 4;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const uint16_t* src = vt + krow * kVStride + nb * 16 + 4 * (li % 4);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 16 * kVStride));
-        const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                                   __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
-        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks2], as_bf16x8(u), o[nb], 0, 0, 0);
-      }
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint16_t* src = vt + krow * kVStride + nb * 16 + 4 * (li % 4);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 16 * kVStride));
+      const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                 __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u), o[nb], 0, 0, 0);
     }
+  };
+
+  // Software pipeline: tile t+4 is in flight while tile t is computed.
+  TileRegs<KV> ra, rb;
+  int32_t ids_a[2], ids_b[2];
+  int t = wave;
+  if (t < ntiles) {
+    fetch_ids(t, ids_a);
+    issue(t, ids_a, ra);
+    if (t + kWaves < ntiles) fetch_ids(t + kWaves, ids_b);
+  }
+  while (t < ntiles) {
+    int tn = t + kWaves;
+    if (tn < ntiles) {
+      issue(tn, ids_b, rb);
+      if (tn + kWaves < ntiles) fetch_ids(tn + kWaves, ids_a);
+    }
+    compute(t, ra);
+    t = tn;
+    if (t >= ntiles) break;
+    tn = t + kWaves;
+    if (tn < ntiles) {
+      issue(tn, ids_a, ra);
+      if (tn + kWaves < ntiles) fetch_ids(tn + kWaves, ids_b);
+    }
+    compute(t, rb);
+    t = tn;
   }
 
   // ---- merge the 4 waves' partial states, then write the chunk's (m, l, o)

@@ -37,6 +37,7 @@ struct AttnArgs {
   const int32_t* seq_len;
   const int32_t* table;
   int32_t B, N, H, Hkv, D, T, mbps;
+  int32_t tshift;                // log2(T)
   int64_t num_blocks;
   float scale_log2;         // softmax scale * log2(e)
   float k_scale, v_scale;   // dequantisation scales (1 unless fp8)

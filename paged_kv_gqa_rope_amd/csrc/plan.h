@@ -33,10 +33,10 @@ struct BatchPlan {
 
 // Numeric limits of the split policy.
 constexpr int32_t kMaxSplits = 128;       // splits per generation request
-constexpr int32_t kDefaultChunk = 512;    // keys per split before balancing
+constexpr int32_t kDefaultChunk = 1024;    // keys per split before balancing
 constexpr int64_t kTargetDecodeItems = 2048;
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
-constexpr bool kHaveFastDecode = false;
+constexpr bool kHaveFastDecode = true;
 constexpr bool kHaveFastPrefill = false;
 
 int validate_desc(const pkv_attn_desc* d, std::string& err);

@@ -196,3 +196,30 @@ def test_empty_batch_launches_nothing(H):
     s = torch.cuda.current_stream().cuda_stream
     assert L.pkv_append_rope(d, lens.desc, None, 0, None, None, 0, None, 0, None, None, s) == 0
     assert L.pkv_attention_forward(d, lens.desc, None, 0, None, None, None, 0, s) == 0
+
+
+# ------------------------------------------------------------------ decode kernel edges
+@pytest.mark.parametrize("T,G,kv", [(16, 1, W.BF16), (32, 2, W.BF16), (64, 4, W.FP8_E4M3), (128, 8, W.BF16),
+                                    (256, 16, W.BF16), (16, 8, W.FP8_E4M3), (64, 3, W.BF16)])
+def test_decode_lengths_blocks_and_groups(H, T, G, kv):
+    Hkv = 2
+    sh = W.Shape(f"dec-T{T}-G{G}", Hkv * G, Hkv, 128, T, W.BF16, kv, 1e4, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    # S = p + 1: a lone token, a partial tile, exact tile and chunk edges, a long tail
+    pasts = [0, 1, 15, 63, 64, 127, 511, 512, 1000, 2500]
+    b = W.make_batch(sh, gen_past=pasts, seed=T * 31 + G, pool_blocks_min=3)
+    case("decode", sh.name, kv)
+    st = run_step(H, b)
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(kv)), "pool")
+    compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
+
+
+def test_decode_fp8_saturating_values(H):
+    # values beyond 448 * scale saturate on write; the oracle reads the same codes
+    sh = W.Shape("fp8-sat", 8, 2, 128, 64, W.BF16, W.FP8_E4M3, 1e4, k_scale=2.0 ** -9, v_scale=2.0 ** -9)
+    b = W.make_batch(sh, gen_past=[200, 70], seed=3)
+    case("fp8-saturation")
+    st = run_step(H, b)
+    want = O.expected_pool(b, sentinel(W.FP8_E4M3))
+    assert np.any((want & 0x7F) == 0x7E), "expected some saturated codes"
+    assert_bits_equal(bits_of(st.pool_host()), want, "pool")
+    compare_attention(st.out_host(), O.run(b)["out"], sh, "fp8-sat")

@@ -171,7 +171,8 @@ def make_batch(shape: Shape, ctx=(), gen_past=(), seed: int = 0, pool_blocks_min
 SHAPES = {
     1: Shape("tiny-mixed-fp32", 4, 2, 64, 16, FP32, FP32, 1.0e4),
     2: Shape("decode-mha-bf16", 32, 32, 128, 64, BF16, BF16, 1.0e4),
-    3: Shape("prefill-gqa4-bf16", 32, 8, 128, 64, BF16, BF16, 5.0e5),
+    # one batch of 8 x 2048 prompt tokens: its token budget is its own size
+    3: Shape("prefill-gqa4-bf16", 32, 8, 128, 64, BF16, BF16, 5.0e5, max_num_tokens=16384),
     4: Shape("mixed-gqa8-bf16", 64, 8, 128, 64, BF16, BF16, 5.0e5),
     5: Shape("longdecode-gqa4-fp8kv", 32, 8, 128, 64, BF16, FP8_E4M3, 5.0e5,
              k_scale=2.0 ** -6, v_scale=2.0 ** -6),
