@@ -195,11 +195,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     const float m_new = fmaxf(m_run, tmax);                    // finite: key tb is always valid
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[e] = exp2f(x[e] - m_new);
+      x[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
       lsum += x[e];
     }
     lsum += __shfl_xor(lsum, 16, kWave);

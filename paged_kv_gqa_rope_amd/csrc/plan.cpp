@@ -66,7 +66,9 @@ bool desc_fast_decode(const pkv_attn_desc& d) {
 
 bool desc_fast_prefill(const pkv_attn_desc& d) {
   if (!kHaveFastPrefill) return false;
-  return d.io_dtype == PKV_BF16 && d.kv_dtype == PKV_BF16 && d.head_dim == 128;
+  const int32_t G = d.num_heads / d.num_kv_heads;
+  return d.io_dtype == PKV_BF16 && d.kv_dtype == PKV_BF16 && d.head_dim == 128 &&
+         (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
 int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* plan, std::string& err) {

@@ -37,7 +37,7 @@ constexpr int32_t kDefaultChunk = 1024;    // keys per split before balancing
 constexpr int64_t kTargetDecodeItems = 2048;
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
 constexpr bool kHaveFastDecode = true;
-constexpr bool kHaveFastPrefill = false;
+constexpr bool kHaveFastPrefill = true;
 
 int validate_desc(const pkv_attn_desc* d, std::string& err);
 int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* plan, std::string& err);

@@ -1,6 +1,272 @@
-// Context-phase MFMA kernel (placeholder launcher until it lands).
+// Context-phase (prefill / chunked prefill) attention on bf16 MFMA for gfx950.
+//
+// "TensorRT-LLM 1.0 study notes", 6.1-6.2: the context phase runs FlashAttention --
+// an outer loop over query tiles, an inner loop over key/value tiles staged in on-chip
+// memory, S = Q K^T and O += P V on the matrix units with fp32 accumulation, and an
+// online softmax that rescales the running output whenever the running maximum grows.
+// Rows are causal over the request's cached prefix plus its chunk ("TensorRT-LLM source
+// analysis report", 1.3, chunked context); K/V come from the paged pool through the
+// block table ("TensorRT-LLM source teardown part 1", KV cache manager interfaces).
+//
+// CDNA4 mapping:
+//  * one workgroup = one KV head's whole GQA group (G = 1, 2, 4 or 8) for a block of
+//    query positions: 8 waves, each owning 32 query rows of one query head, so every
+//    K/V tile staged in LDS feeds all G heads that share it;
+//  * the transposed products keep the softmax in-lane: S^T = K Q^T on
+//    v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims of K from LDS, B = Q^T held in
+//    registers), so lane l owns query l%32 and 16 keys per 32-key block, and the row
+//    max/sum need one cross-lane step (lanes l and l^32);
+//  * O^T = V^T P^T: B = P^T straight from the score accumulators (converted to bf16),
+//    A = V^T read from LDS with ds_read_b64_tr_b16;
+//  * 64-key tiles are double-buffered in LDS (global loads for tile t+1 are in flight
+//    while tile t is computed), block IDs are fetched two tiles ahead;
+//  * only tiles that cross the diagonal are masked, fully masked tiles are skipped, and
+//    the output rescale is skipped when no lane's running maximum moved.
+#include <math.h>
+
+#include "device_common.h"
 #include "kernels.h"
 
 namespace pkv {
-hipError_t launch_prefill(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kD = 128;
+constexpr int kTileK = 64;                 // keys per LDS tile
+constexpr int kKStride = 136;              // LDS row stride of K (272 B: b128 reads conflict-free)
+constexpr int kVStride = 144;              // LDS row stride of V (288 B: transposed reads conflict-free)
+constexpr int kKBuf = kTileK * kKStride;
+constexpr int kVBuf = kTileK * kVStride;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+template <int NW, int G>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(AttnArgs a) {
+  constexpr int RB = NW / G;               // 32-row blocks per workgroup
+  constexpr int ROWS = RB * 32;            // query positions per workgroup
+  constexpr int NT = NW * kWave;
+  const int g = blockIdx.y;
+  const int r = a.req_begin + blockIdx.z;
+  const int n = a.ctx_len[r];
+  const int ntq = (n + ROWS - 1) / ROWS;
+  if (static_cast<int>(blockIdx.x) >= ntq) return;                     // uniform
+  const int qtile = ntq - 1 - static_cast<int>(blockIdx.x);             // heaviest tiles first
+  const int S = a.seq_len[r];
+  const int past = S - n;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int l32 = lane % 32, lh = lane / 32;
+  const int h = g * G + wave % G;
+  const int q0 = qtile * ROWS + (wave / G) * 32;                        // first row of this wave
+  const bool wave_active = q0 < n;
+  const int qlast = min(q0 + 31, n - 1);                                // last valid row
+  const int wave_max_pos = past + qlast;
+  const int tile_rows_end = min(qtile * ROWS + ROWS, n);               // rows of the workgroup
+  const int kv_end = past + tile_rows_end;                              // keys 0 .. kv_end-1
+  const int ntiles = (kv_end + kTileK - 1) / kTileK;
+  const int64_t row0 = wave_prefix(a.ctx_len, r);                       // packed row of request r
+  const int tshift = a.tshift, tmask = a.T - 1;
+  const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;
+  const int64_t blk_elems = 2 * static_cast<int64_t>(a.T) * kv_row;
+  const int32_t* table = a.table + static_cast<int64_t>(r) * a.mbps;
+  const int last_blk = (S - 1) >> tshift;
+
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][kKBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][kVBuf];
+
+  // ---- Q^T (B operand): query q0 + l32, dims lh*64 + ks*8 + j for ks = 0..7
+  bf16x8 qf[8];
+  {
+    const int qi = min(q0 + l32, n - 1);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row0 + qi) * a.q_stride +
+                         static_cast<int64_t>(h) * kD + lh * 64;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + ks * 8));
+  }
+  const int my_pos = past + min(q0 + l32, n - 1);                       // this lane's query position
+  const float c = a.scale_log2;
+
+  // ---- cooperative tile loads: thread t moves the 16-byte chunk t%16 of K and V rows
+  //      t/16 and t/16 + 32 of the tile
+  static_assert(NT == 512, "tile split assumes 8 waves");
+  const int crow = threadIdx.x / 16;                    // rows crow and crow + 32 of the tile
+  const int ccol = (threadIdx.x % 16) * 8;
+  uint4 sk0, sk1, sv0, sv1;                            // staged 16-byte chunks of the next tile
+  int32_t ids_nxt0, ids_nxt1;
+  auto fetch_ids = [&](int tile, int32_t& i0, int32_t& i1) {
+    const int key0 = min(tile * kTileK + crow, S - 1);
+    const int key1 = min(tile * kTileK + crow + 32, S - 1);
+    i0 = table[min(key0 >> tshift, last_blk)];
+    i1 = table[min(key1 >> tshift, last_blk)];
+  };
+  auto row_ptr = [&](int key, int32_t id) {              // K row of (block id, slot of key), head g
+    id = (id >= 0 && id < a.num_blocks) ? id : 0;
+    return static_cast<const uint16_t*>(a.pool) + static_cast<int64_t>(id) * blk_elems +
+           static_cast<int64_t>(key & tmask) * kv_row + static_cast<int64_t>(g) * kD + ccol;
+  };
+  auto issue = [&](int tile, int32_t i0, int32_t i1) {
+    const int key0 = min(tile * kTileK + crow, S - 1);          // clamp: never read unwritten slots
+    const int key1 = min(tile * kTileK + crow + 32, S - 1);
+    const uint16_t* p0 = row_ptr(key0, i0);
+    const uint16_t* p1 = row_ptr(key1, i1);
+    sk0 = *reinterpret_cast<const uint4*>(p0);
+    sk1 = *reinterpret_cast<const uint4*>(p1);
+    sv0 = *reinterpret_cast<const uint4*>(p0 + a.T * kv_row);
+    sv1 = *reinterpret_cast<const uint4*>(p1 + a.T * kv_row);
+  };
+  auto commit = [&](int buf) {
+    *reinterpret_cast<uint4*>(&kbuf[buf][crow * kKStride + ccol]) = sk0;
+    *reinterpret_cast<uint4*>(&kbuf[buf][(crow + 32) * kKStride + ccol]) = sk1;
+    *reinterpret_cast<uint4*>(&vbuf[buf][crow * kVStride + ccol]) = sv0;
+    *reinterpret_cast<uint4*>(&vbuf[buf][(crow + 32) * kVStride + ccol]) = sv1;
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;      // raw-score max of query l32; this lane's partial sum
+  f32x16 o[4];                               // O^T[dim blk*32 + (i/4)*8 + lh*4 + i%4][query l32]
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
+
+  {
+    int32_t i0, i1;
+    fetch_ids(0, i0, i1);
+    issue(0, i0, i1);
+  }
+  if (ntiles > 1) fetch_ids(1, ids_nxt0, ids_nxt1);
+  commit(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      issue(t + 1, ids_nxt0, ids_nxt1);
+      if (t + 2 < ntiles) fetch_ids(t + 2, ids_nxt0, ids_nxt1);
+    }
+    const int kb0 = t * kTileK;
+    if (wave_active && kb0 <= wave_max_pos) {
+      const uint16_t* kt = kbuf[buf];
+      const uint16_t* vt = vbuf[buf];
+      // ---- S^T = K Q^T: two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        const uint16_t* kr = kt + (kb * 32 + l32) * kKStride + lh * 64;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(kr + ks * 8));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        }
+      }
+      // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
+      if (kb0 + kTileK - 1 > past + q0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb0 + kb * 32 + (i / 4) * 8 + lh * 4 + (i % 4);
+            s[kb][i] = key <= my_pos ? s[kb][i] : -INFINITY;
+          }
+      }
+      // ---- online softmax (raw-score domain; exp2 of (s - m) * c)
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float m_new = fmaxf(m_run, tmax);
+      if (__any(m_new > m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * c;
+      // P^T as four B operands (16 keys each): slot j of step ks2 is s[ks2/2][(ks2%2)*8 + j]
+      bf16x8 pb[4];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) {
+        const int kb = ks2 / 2, i0 = (ks2 % 2) * 8;
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc));
+          l_run += p[j];
+        }
+        pb[ks2] = as_bf16x8(make_uint4(f32_to_bf16(p[0]) | (f32_to_bf16(p[1]) << 16),
+                                       f32_to_bf16(p[2]) | (f32_to_bf16(p[3]) << 16),
+                                       f32_to_bf16(p[4]) | (f32_to_bf16(p[5]) << 16),
+                                       f32_to_bf16(p[6]) | (f32_to_bf16(p[7]) << 16)));
+      }
+      // ---- O^T += V^T P^T over four 16-key steps
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) {
+        // source rows for the transposed read: keys ks2*16 + lh*4 + (lane%16)/4 (+8)
+        const int krow = ks2 * 16 + lh * 4 + (lane % 16) / 4;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int dcol = b * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
+          const uint16_t* src = vt + krow * kVStride + dcol;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * kVStride));
+          const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                     __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[ks2], o[b], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane owns query l32 and dims blk*32 + (i/4)*8 + lh*4 + i%4
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float inv = 1.f / l_tot;
+  const int qi = q0 + l32;
+  if (qi >= n) return;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (row0 + qi) * static_cast<int64_t>(a.H) * kD +
+                 static_cast<int64_t>(h) * kD;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = b * 32 + i4 * 8 + lh * 4;
+      const uint32_t w0 = f32_to_bf16(o[b][i4 * 4 + 0] * inv) | (f32_to_bf16(o[b][i4 * 4 + 1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16(o[b][i4 * 4 + 2] * inv) | (f32_to_bf16(o[b][i4 * 4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+    }
+}
+
+template <int NW, int G>
+hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  constexpr int ROWS = (NW / G) * 32;
+  const dim3 grid((a.max_n + ROWS - 1) / ROWS, a.Hkv, a.req_end - a.req_begin);
+  hipLaunchKernelGGL((prefill_kernel<NW, G>), grid, dim3(NW * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
+  switch (a.H / a.Hkv) {
+    case 1: return launch_t<8, 1>(a, s);
+    case 2: return launch_t<8, 2>(a, s);
+    case 4: return launch_t<8, 4>(a, s);
+    case 8: return launch_t<8, 8>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 }  // namespace pkv

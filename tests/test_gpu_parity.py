@@ -223,3 +223,18 @@ def test_decode_fp8_saturating_values(H):
     assert np.any((want & 0x7F) == 0x7E), "expected some saturated codes"
     assert_bits_equal(bits_of(st.pool_host()), want, "pool")
     compare_attention(st.out_host(), O.run(b)["out"], sh, "fp8-sat")
+
+
+# ------------------------------------------------------------------ context kernel edges
+@pytest.mark.parametrize("T,G", [(64, 1), (16, 2), (32, 4), (128, 8), (256, 4), (64, 16)])
+def test_context_chunks_blocks_and_groups(H, T, G):
+    Hkv = 2
+    sh = W.Shape(f"ctx-T{T}-G{G}", Hkv * G, Hkv, 128, T, W.BF16, W.BF16, 5e5)
+    # ragged chunk lengths on block-aligned cached prefixes, a 1-token prompt, and a
+    # chunk that starts mid-way through a long prefix; then two generation requests
+    ctx = [(1, 0), (31, 0), (100, T * 2), (65, 0), (257, T * 5)]
+    b = W.make_batch(sh, ctx=ctx, gen_past=[40, 300], seed=T + G, pool_blocks_min=2)
+    case("context", sh.name)
+    st = run_step(H, b)
+    assert_bits_equal(st.q_out_host(), O.run(b)["q_out"], "q_out")
+    compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
