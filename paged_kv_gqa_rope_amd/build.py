@@ -22,7 +22,9 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU forms stay disabled in all device code.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # private arrays stay in registers; LDS is laid out by hand
+          "-mllvm", "-disable-promote-alloca-to-lds"]
 PER_FILE = {
     # the append's bit-exact recipe: no fused multiply-add anywhere in that file
     "append.hip": ["-ffp-contract=off"],

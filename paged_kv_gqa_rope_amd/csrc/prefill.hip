@@ -10,8 +10,9 @@
 //
 // CDNA4 mapping:
 //  * one workgroup = one KV head's whole GQA group (G = 1, 2, 4 or 8) for a block of
-//    query positions: 8 waves, each owning 32 query rows of one query head, so every
-//    K/V tile staged in LDS feeds all G heads that share it;
+//    query positions: 4 waves (8 when G = 8), each owning 32 query rows of one query
+//    head, so every K/V tile staged in LDS feeds all G heads that share it; two
+//    workgroups share a CU so one's softmax overlaps the other's MFMAs;
 //  * the transposed products keep the softmax in-lane: S^T = K Q^T on
 //    v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims of K from LDS, B = Q^T held in
 //    registers), so lane l owns query l%32 and 16 keys per 32-key block, and the row
@@ -43,6 +44,13 @@ constexpr int kKBuf = kTileK * kKStride;
 constexpr int kVBuf = kTileK * kVStride;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 
 template <int NW, int G>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -92,38 +100,59 @@ void prefill_kernel(AttnArgs a) {
   const float c = a.scale_log2;
 
   // ---- cooperative tile loads: thread t moves the 16-byte chunk t%16 of K and V rows
-  //      t/16 and t/16 + 32 of the tile
-  static_assert(NT == 512, "tile split assumes 8 waves");
-  const int crow = threadIdx.x / 16;                    // rows crow and crow + 32 of the tile
+  //      t/16 + u*NT/16 of the tile
+  constexpr int KCH = (kTileK * 16) / NT;              // 16-byte chunks of K (and of V) per thread
+  static_assert(KCH == 2 || KCH == 4, "4 or 8 waves per workgroup");
   const int ccol = (threadIdx.x % 16) * 8;
-  uint4 sk0, sk1, sv0, sv1;                            // staged 16-byte chunks of the next tile
-  int32_t ids_nxt0, ids_nxt1;
-  auto fetch_ids = [&](int tile, int32_t& i0, int32_t& i1) {
-    const int key0 = min(tile * kTileK + crow, S - 1);
-    const int key1 = min(tile * kTileK + crow + 32, S - 1);
-    i0 = table[min(key0 >> tshift, last_blk)];
-    i1 = table[min(key1 >> tshift, last_blk)];
+  const int crow0 = threadIdx.x / 16;                  // chunk u covers tile row crow0 + u*NT/16
+  // staged 16-byte chunks of the next tile and the block IDs of the tile after it, in
+  // named registers (indexable arrays here end up in scratch memory)
+  uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+  int32_t in0 = 0, in1 = 0, in2 = 0, in3 = 0;
+  auto key_of = [&](int tile, int u) { return min(tile * kTileK + crow0 + u * (NT / 16), S - 1); };
+  auto id_of = [&](int tile, int u) { return table[min(key_of(tile, u) >> tshift, last_blk)]; };
+  auto fetch_ids = [&](int tile) {
+    in0 = id_of(tile, 0);
+    in1 = id_of(tile, 1);
+    if constexpr (KCH == 4) {
+      in2 = id_of(tile, 2);
+      in3 = id_of(tile, 3);
+    }
   };
-  auto row_ptr = [&](int key, int32_t id) {              // K row of (block id, slot of key), head g
-    id = (id >= 0 && id < a.num_blocks) ? id : 0;
+  auto chunk_ptr = [&](int tile, int u, int32_t id) {  // K chunk; its V chunk is T rows later
+    id = (id >= 0 && id < a.num_blocks) ? id : 0;       // clamped key: never an unwritten slot
     return static_cast<const uint16_t*>(a.pool) + static_cast<int64_t>(id) * blk_elems +
-           static_cast<int64_t>(key & tmask) * kv_row + static_cast<int64_t>(g) * kD + ccol;
+           static_cast<int64_t>(key_of(tile, u) & tmask) * kv_row + static_cast<int64_t>(g) * kD + ccol;
   };
-  auto issue = [&](int tile, int32_t i0, int32_t i1) {
-    const int key0 = min(tile * kTileK + crow, S - 1);          // clamp: never read unwritten slots
-    const int key1 = min(tile * kTileK + crow + 32, S - 1);
-    const uint16_t* p0 = row_ptr(key0, i0);
-    const uint16_t* p1 = row_ptr(key1, i1);
+  const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
+  auto issue = [&](int tile) {
+    const uint16_t* p0 = chunk_ptr(tile, 0, in0);
+    const uint16_t* p1 = chunk_ptr(tile, 1, in1);
     sk0 = *reinterpret_cast<const uint4*>(p0);
     sk1 = *reinterpret_cast<const uint4*>(p1);
-    sv0 = *reinterpret_cast<const uint4*>(p0 + a.T * kv_row);
-    sv1 = *reinterpret_cast<const uint4*>(p1 + a.T * kv_row);
+    sv0 = *reinterpret_cast<const uint4*>(p0 + vofs);
+    sv1 = *reinterpret_cast<const uint4*>(p1 + vofs);
+    if constexpr (KCH == 4) {
+      const uint16_t* p2 = chunk_ptr(tile, 2, in2);
+      const uint16_t* p3 = chunk_ptr(tile, 3, in3);
+      sk2 = *reinterpret_cast<const uint4*>(p2);
+      sk3 = *reinterpret_cast<const uint4*>(p3);
+      sv2 = *reinterpret_cast<const uint4*>(p2 + vofs);
+      sv3 = *reinterpret_cast<const uint4*>(p3 + vofs);
+    }
   };
   auto commit = [&](int buf) {
-    *reinterpret_cast<uint4*>(&kbuf[buf][crow * kKStride + ccol]) = sk0;
-    *reinterpret_cast<uint4*>(&kbuf[buf][(crow + 32) * kKStride + ccol]) = sk1;
-    *reinterpret_cast<uint4*>(&vbuf[buf][crow * kVStride + ccol]) = sv0;
-    *reinterpret_cast<uint4*>(&vbuf[buf][(crow + 32) * kVStride + ccol]) = sv1;
+    constexpr int RS = NT / 16;                         // rows between chunks
+    *reinterpret_cast<uint4*>(&kbuf[buf][crow0 * kKStride + ccol]) = sk0;
+    *reinterpret_cast<uint4*>(&kbuf[buf][(crow0 + RS) * kKStride + ccol]) = sk1;
+    *reinterpret_cast<uint4*>(&vbuf[buf][crow0 * kVStride + ccol]) = sv0;
+    *reinterpret_cast<uint4*>(&vbuf[buf][(crow0 + RS) * kVStride + ccol]) = sv1;
+    if constexpr (KCH == 4) {
+      *reinterpret_cast<uint4*>(&kbuf[buf][(crow0 + 2 * RS) * kKStride + ccol]) = sk2;
+      *reinterpret_cast<uint4*>(&kbuf[buf][(crow0 + 3 * RS) * kKStride + ccol]) = sk3;
+      *reinterpret_cast<uint4*>(&vbuf[buf][(crow0 + 2 * RS) * kVStride + ccol]) = sv2;
+      *reinterpret_cast<uint4*>(&vbuf[buf][(crow0 + 3 * RS) * kVStride + ccol]) = sv3;
+    }
   };
 
   float m_run = -INFINITY, l_run = 0.f;      // raw-score max of query l32; this lane's partial sum
@@ -133,20 +162,17 @@ void prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
-  {
-    int32_t i0, i1;
-    fetch_ids(0, i0, i1);
-    issue(0, i0, i1);
-  }
-  if (ntiles > 1) fetch_ids(1, ids_nxt0, ids_nxt1);
+  fetch_ids(0);
+  issue(0);
+  if (ntiles > 1) fetch_ids(1);
   commit(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) {
-      issue(t + 1, ids_nxt0, ids_nxt1);
-      if (t + 2 < ntiles) fetch_ids(t + 2, ids_nxt0, ids_nxt1);
+      issue(t + 1);
+      if (t + 2 < ntiles) fetch_ids(t + 2);
     }
     const int kb0 = t * kTileK;
     if (wave_active && kb0 <= wave_max_pos) {
@@ -167,13 +193,12 @@ void prefill_kernel(AttnArgs a) {
       }
       // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
       if (kb0 + kTileK - 1 > past + q0) {
+        const int lim = my_pos - kb0 - lh * 4;                 // key offset kb*32+(i/4)*8+i%4 <= lim
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb0 + kb * 32 + (i / 4) * 8 + lh * 4 + (i % 4);
-            s[kb][i] = key <= my_pos ? s[kb][i] : -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            s[kb][i] = (kb * 32 + (i / 4) * 8 + (i % 4) <= lim) ? s[kb][i] : -INFINITY;
       }
       // ---- online softmax (raw-score domain; exp2 of (s - m) * c)
       float tmax = -INFINITY;
@@ -204,10 +229,8 @@ void prefill_kernel(AttnArgs a) {
           p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc));
           l_run += p[j];
         }
-        pb[ks2] = as_bf16x8(make_uint4(f32_to_bf16(p[0]) | (f32_to_bf16(p[1]) << 16),
-                                       f32_to_bf16(p[2]) | (f32_to_bf16(p[3]) << 16),
-                                       f32_to_bf16(p[4]) | (f32_to_bf16(p[5]) << 16),
-                                       f32_to_bf16(p[6]) | (f32_to_bf16(p[7]) << 16)));
+        pb[ks2] = as_bf16x8(make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                                       pack_bf16(p[6], p[7])));
       }
       // ---- O^T += V^T P^T over four 16-key steps
 #pragma unroll
@@ -243,14 +266,15 @@ void prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d = b * 32 + i4 * 8 + lh * 4;
-      const uint32_t w0 = f32_to_bf16(o[b][i4 * 4 + 0] * inv) | (f32_to_bf16(o[b][i4 * 4 + 1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16(o[b][i4 * 4 + 2] * inv) | (f32_to_bf16(o[b][i4 * 4 + 3] * inv) << 16);
+      const uint32_t w0 = pack_bf16(o[b][i4 * 4 + 0] * inv, o[b][i4 * 4 + 1] * inv);
+      const uint32_t w1 = pack_bf16(o[b][i4 * 4 + 2] * inv, o[b][i4 * 4 + 3] * inv);
       *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
     }
 }
 
 template <int NW, int G>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  static_assert(NW % G == 0, "a workgroup holds whole query groups");
   constexpr int ROWS = (NW / G) * 32;
   const dim3 grid((a.max_n + ROWS - 1) / ROWS, a.Hkv, a.req_end - a.req_begin);
   hipLaunchKernelGGL((prefill_kernel<NW, G>), grid, dim3(NW * kWave), 0, s, a);
@@ -261,9 +285,9 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
   switch (a.H / a.Hkv) {
-    case 1: return launch_t<8, 1>(a, s);
-    case 2: return launch_t<8, 2>(a, s);
-    case 4: return launch_t<8, 4>(a, s);
+    case 1: return launch_t<4, 1>(a, s);
+    case 2: return launch_t<4, 2>(a, s);
+    case 4: return launch_t<4, 4>(a, s);
     case 8: return launch_t<8, 8>(a, s);
     default: return hipErrorNotSupported;
   }
