@@ -68,7 +68,9 @@ struct TileRegs {
 
 template <int KV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
-  const int split = blockIdx.x, g = blockIdx.y, rg = blockIdx.z;
+  // KV head fastest: the workgroups of every head of one (request, chunk) run side by
+  // side, so together they read each block's K and V rows as contiguous memory.
+  const int g = blockIdx.x, split = blockIdx.y, rg = blockIdx.z;
   const int r = a.req_begin + rg;
   const int S = a.seq_len[r];
   const int k0 = split * a.chunk;
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.max_splits, a.Hkv, a.req_end - a.req_begin);
+  const dim3 grid(a.Hkv, a.max_splits, a.req_end - a.req_begin);
   if (a.kv_fmt == F_FP8)
     hipLaunchKernelGGL(decode_split_kernel<F_FP8>, grid, dim3(kThreads), 0, s, a);
   else

@@ -39,8 +39,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kD = 128;
 constexpr int kTileK = 64;                 // keys per LDS tile
 constexpr int kKStride = 136;              // LDS row stride of K (272 B: b128 reads conflict-free)
-constexpr int kVStride = 144;              // LDS row stride of V (288 B: transposed reads conflict-free)
+constexpr int kVStride = 160;              // LDS row stride of V (320 B: the 4 rows of a transposed read hit disjoint banks)
 constexpr int kKBuf = kTileK * kKStride;
+constexpr float kLazyLog2 = 8.f;           // rescale only when the maximum grows by > 2^8
+constexpr int kXcds = 8;                   // MI355X accelerator complex dies
 constexpr int kVBuf = kTileK * kVStride;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -58,12 +60,27 @@ void prefill_kernel(AttnArgs a) {
   constexpr int RB = NW / G;               // 32-row blocks per workgroup
   constexpr int ROWS = RB * 32;            // query positions per workgroup
   constexpr int NT = NW * kWave;
-  const int g = blockIdx.y;
-  const int r = a.req_begin + blockIdx.z;
+  // XCD-aware placement: workgroups go to the 8 XCDs round-robin by linear ID, so when
+  // the (request, KV head) pairs split evenly, linear ID L runs on XCD L % 8 and takes
+  // that XCD's (L / 8)-th item; all query tiles of one pair then share one L2.
+  const int nq = a.max_n > 0 ? (a.max_n + ROWS - 1) / ROWS : 1;   // query tiles of the longest chunk
+  const int np = a.Hkv * (a.req_end - a.req_begin);                 // (request, KV head) pairs
+  const int L = blockIdx.x;
+  int pair, qt;
+  if (np % kXcds == 0) {
+    const int j = L / kXcds;
+    pair = (j / nq) * kXcds + L % kXcds;
+    qt = j % nq;
+  } else {
+    pair = L / nq;
+    qt = L % nq;
+  }
+  const int g = pair % a.Hkv;
+  const int r = a.req_begin + pair / a.Hkv;
   const int n = a.ctx_len[r];
   const int ntq = (n + ROWS - 1) / ROWS;
-  if (static_cast<int>(blockIdx.x) >= ntq) return;                     // uniform
-  const int qtile = ntq - 1 - static_cast<int>(blockIdx.x);             // heaviest tiles first
+  if (qt >= ntq) return;                                            // uniform
+  const int qtile = ntq - 1 - qt;                                   // heaviest tiles first
   const int S = a.seq_len[r];
   const int past = S - n;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -178,18 +195,26 @@ void prefill_kernel(AttnArgs a) {
     if (wave_active && kb0 <= wave_max_pos) {
       const uint16_t* kt = kbuf[buf];
       const uint16_t* vt = vbuf[buf];
-      // ---- S^T = K Q^T: two 32-key blocks
+      // ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K
+      //      operands read from LDS one step ahead
       f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
+      const uint16_t* kr0 = kt + l32 * kKStride + lh * 64;
+      const uint16_t* kr1 = kr0 + 32 * kKStride;
+      bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(kr0));
+      bf16x8 kc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-        const uint16_t* kr = kt + (kb * 32 + l32) * kKStride + lh * 64;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(kr + ks * 8));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 na = ka, nc = kc;
+        if (ks < 7) {
+          na = as_bf16x8(*reinterpret_cast<const uint4*>(kr0 + (ks + 1) * 8));
+          nc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1 + (ks + 1) * 8));
         }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s[1], 0, 0, 0);
+        ka = na;
+        kc = nc;
       }
       // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
       if (kb0 + kTileK - 1 > past + q0) {
@@ -207,8 +232,12 @@ void prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run, tmax);
-      if (__any(m_new > m_run)) {
+      // Lazy rescaling: the running maximum used as the exponent offset only moves when a
+      // score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough
+      // in fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first
+      // tile always sets it (m_run starts at -inf).
+      if (__any((tmax - m_run) * c > kLazyLog2)) {
+        const float m_new = fmaxf(m_run, tmax);
         const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
         l_run *= alpha;
 #pragma unroll
@@ -276,7 +305,8 @@ template <int NW, int G>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   static_assert(NW % G == 0, "a workgroup holds whole query groups");
   constexpr int ROWS = (NW / G) * 32;
-  const dim3 grid((a.max_n + ROWS - 1) / ROWS, a.Hkv, a.req_end - a.req_begin);
+  const int nq = (a.max_n + ROWS - 1) / ROWS;
+  const dim3 grid(nq * a.Hkv * (a.req_end - a.req_begin));
   hipLaunchKernelGGL((prefill_kernel<NW, G>), grid, dim3(NW * kWave), 0, s, a);
   return hipGetLastError();
 }
