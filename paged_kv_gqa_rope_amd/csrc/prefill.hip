@@ -48,6 +48,7 @@ constexpr int kVBuf = kTileK * kVStride;
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -122,13 +123,16 @@ void prefill_kernel(AttnArgs a) {
   static_assert(KCH == 2 || KCH == 4, "4 or 8 waves per workgroup");
   const int ccol = (threadIdx.x % 16) * 8;
   const int crow0 = threadIdx.x / 16;                  // chunk u covers tile row crow0 + u*NT/16
-  // staged 16-byte chunks of the next tile and the block IDs of the tile after it, in
-  // named registers (indexable arrays here end up in scratch memory)
-  uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+  // Two register stages (tiles t+1 and t+2 in flight) and the block IDs of the tile
+  // after those, all in named registers (indexable arrays here end up in scratch).
+  struct Stage {
+    u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
+  };
+  Stage st0, st1;
   int32_t in0 = 0, in1 = 0, in2 = 0, in3 = 0;
-  auto key_of = [&](int tile, int u) { return min(tile * kTileK + crow0 + u * (NT / 16), S - 1); };
-  auto id_of = [&](int tile, int u) { return table[min(key_of(tile, u) >> tshift, last_blk)]; };
-  auto fetch_ids = [&](int tile) {
+  auto key_of = [&](int tile, int u) __attribute__((always_inline)) { return min(tile * kTileK + crow0 + u * (NT / 16), S - 1); };
+  auto id_of = [&](int tile, int u) __attribute__((always_inline)) { return table[min(key_of(tile, u) >> tshift, last_blk)]; };
+  auto fetch_ids = [&](int tile) __attribute__((always_inline)) {
     in0 = id_of(tile, 0);
     in1 = id_of(tile, 1);
     if constexpr (KCH == 4) {
@@ -136,39 +140,39 @@ void prefill_kernel(AttnArgs a) {
       in3 = id_of(tile, 3);
     }
   };
-  auto chunk_ptr = [&](int tile, int u, int32_t id) {  // K chunk; its V chunk is T rows later
+  auto chunk_ptr = [&](int tile, int u, int32_t id) __attribute__((always_inline)) {  // K chunk; its V chunk is T rows later
     id = (id >= 0 && id < a.num_blocks) ? id : 0;       // clamped key: never an unwritten slot
     return static_cast<const uint16_t*>(a.pool) + static_cast<int64_t>(id) * blk_elems +
            static_cast<int64_t>(key_of(tile, u) & tmask) * kv_row + static_cast<int64_t>(g) * kD + ccol;
   };
   const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
-  auto issue = [&](int tile) {
+  auto issue = [&](int tile, Stage& q) __attribute__((always_inline)) {
     const uint16_t* p0 = chunk_ptr(tile, 0, in0);
     const uint16_t* p1 = chunk_ptr(tile, 1, in1);
-    sk0 = *reinterpret_cast<const uint4*>(p0);
-    sk1 = *reinterpret_cast<const uint4*>(p1);
-    sv0 = *reinterpret_cast<const uint4*>(p0 + vofs);
-    sv1 = *reinterpret_cast<const uint4*>(p1 + vofs);
+    q.k0 = *reinterpret_cast<const u32x4*>(p0);
+    q.k1 = *reinterpret_cast<const u32x4*>(p1);
+    q.v0 = *reinterpret_cast<const u32x4*>(p0 + vofs);
+    q.v1 = *reinterpret_cast<const u32x4*>(p1 + vofs);
     if constexpr (KCH == 4) {
       const uint16_t* p2 = chunk_ptr(tile, 2, in2);
       const uint16_t* p3 = chunk_ptr(tile, 3, in3);
-      sk2 = *reinterpret_cast<const uint4*>(p2);
-      sk3 = *reinterpret_cast<const uint4*>(p3);
-      sv2 = *reinterpret_cast<const uint4*>(p2 + vofs);
-      sv3 = *reinterpret_cast<const uint4*>(p3 + vofs);
+      q.k2 = *reinterpret_cast<const u32x4*>(p2);
+      q.k3 = *reinterpret_cast<const u32x4*>(p3);
+      q.v2 = *reinterpret_cast<const u32x4*>(p2 + vofs);
+      q.v3 = *reinterpret_cast<const u32x4*>(p3 + vofs);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, const Stage& q) __attribute__((always_inline)) {
     constexpr int RS = NT / 16;                         // rows between chunks
-    *reinterpret_cast<uint4*>(&kbuf[buf][crow0 * kKStride + ccol]) = sk0;
-    *reinterpret_cast<uint4*>(&kbuf[buf][(crow0 + RS) * kKStride + ccol]) = sk1;
-    *reinterpret_cast<uint4*>(&vbuf[buf][crow0 * kVStride + ccol]) = sv0;
-    *reinterpret_cast<uint4*>(&vbuf[buf][(crow0 + RS) * kVStride + ccol]) = sv1;
+    *reinterpret_cast<u32x4*>(&kbuf[buf][crow0 * kKStride + ccol]) = q.k0;
+    *reinterpret_cast<u32x4*>(&kbuf[buf][(crow0 + RS) * kKStride + ccol]) = q.k1;
+    *reinterpret_cast<u32x4*>(&vbuf[buf][crow0 * kVStride + ccol]) = q.v0;
+    *reinterpret_cast<u32x4*>(&vbuf[buf][(crow0 + RS) * kVStride + ccol]) = q.v1;
     if constexpr (KCH == 4) {
-      *reinterpret_cast<uint4*>(&kbuf[buf][(crow0 + 2 * RS) * kKStride + ccol]) = sk2;
-      *reinterpret_cast<uint4*>(&kbuf[buf][(crow0 + 3 * RS) * kKStride + ccol]) = sk3;
-      *reinterpret_cast<uint4*>(&vbuf[buf][(crow0 + 2 * RS) * kVStride + ccol]) = sv2;
-      *reinterpret_cast<uint4*>(&vbuf[buf][(crow0 + 3 * RS) * kVStride + ccol]) = sv3;
+      *reinterpret_cast<u32x4*>(&kbuf[buf][(crow0 + 2 * RS) * kKStride + ccol]) = q.k2;
+      *reinterpret_cast<u32x4*>(&kbuf[buf][(crow0 + 3 * RS) * kKStride + ccol]) = q.k3;
+      *reinterpret_cast<u32x4*>(&vbuf[buf][(crow0 + 2 * RS) * kVStride + ccol]) = q.v2;
+      *reinterpret_cast<u32x4*>(&vbuf[buf][(crow0 + 3 * RS) * kVStride + ccol]) = q.v3;
     }
   };
 
@@ -179,108 +183,126 @@ void prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
+  // Tile t is computed from LDS buffer t%2 while tiles t+1 and t+2 are in flight in
+  // the two register stages; the loop is unrolled by two so each half uses fixed
+  // stages (tile t+1 sits in the stage the other half filled).
+#define PKV_PREFILL_TILE(T_, BUF_) \
+  do { \
+    const int kb0 = (T_) * kTileK; \
+    if (wave_active && kb0 <= wave_max_pos) { \
+      const uint16_t* kt = kbuf[BUF_]; \
+      const uint16_t* vt = vbuf[BUF_]; \
+      /* ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K */ \
+      /* operands read from LDS one step ahead */ \
+      f32x16 s[2]; \
+_Pragma("unroll") \
+      for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f; \
+      const uint16_t* kr0 = kt + l32 * kKStride + lh * 64; \
+      const uint16_t* kr1 = kr0 + 32 * kKStride; \
+      bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(kr0)); \
+      bf16x8 kc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1)); \
+_Pragma("unroll") \
+      for (int ks = 0; ks < 8; ++ks) { \
+        bf16x8 na = ka, nc = kc; \
+        if (ks < 7) { \
+          na = as_bf16x8(*reinterpret_cast<const uint4*>(kr0 + (ks + 1) * 8)); \
+          nc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1 + (ks + 1) * 8)); \
+        } \
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[0], 0, 0, 0); \
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s[1], 0, 0, 0); \
+        ka = na; \
+        kc = nc; \
+      } \
+      /* ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys) */ \
+      if (kb0 + kTileK - 1 > past + q0) { \
+        const int lim = my_pos - kb0 - lh * 4;                 /* key offset kb*32+(i/4)*8+i%4 <= lim */ \
+_Pragma("unroll") \
+        for (int kb = 0; kb < 2; ++kb) \
+_Pragma("unroll") \
+          for (int i = 0; i < 16; ++i) \
+            s[kb][i] = (kb * 32 + (i / 4) * 8 + (i % 4) <= lim) ? s[kb][i] : -INFINITY; \
+      } \
+      /* ---- online softmax (raw-score domain; exp2 of (s - m) * c) */ \
+      float tmax = -INFINITY; \
+_Pragma("unroll") \
+      for (int kb = 0; kb < 2; ++kb) \
+_Pragma("unroll") \
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]); \
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)); \
+      /* Lazy rescaling: the running maximum used as the exponent offset only moves when a */ \
+      /* score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough */ \
+      /* in fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first */ \
+      /* tile always sets it (m_run starts at -inf). */ \
+      if (__any((tmax - m_run) * c > kLazyLog2)) { \
+        const float m_new = fmaxf(m_run, tmax); \
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c); \
+        l_run *= alpha; \
+_Pragma("unroll") \
+        for (int b = 0; b < 4; ++b) \
+_Pragma("unroll") \
+          for (int i = 0; i < 16; ++i) o[b][i] *= alpha; \
+        m_run = m_new; \
+      } \
+      const float mc = m_run * c; \
+      /* P^T as four B operands (16 keys each): slot j of step ks2 is s[ks2/2][(ks2%2)*8 + j] */ \
+      bf16x8 pb[4]; \
+_Pragma("unroll") \
+      for (int ks2 = 0; ks2 < 4; ++ks2) { \
+        const int kb = ks2 / 2, i0 = (ks2 % 2) * 8; \
+        float p[8]; \
+_Pragma("unroll") \
+        for (int j = 0; j < 8; ++j) { \
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc)); \
+          l_run += p[j]; \
+        } \
+        pb[ks2] = as_bf16x8(make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), \
+                                       pack_bf16(p[6], p[7]))); \
+      } \
+      /* ---- O^T += V^T P^T over four 16-key steps */ \
+_Pragma("unroll") \
+      for (int ks2 = 0; ks2 < 4; ++ks2) { \
+        /* source rows for the transposed read: keys ks2*16 + lh*4 + (lane%16)/4 (+8) */ \
+        const int krow = ks2 * 16 + lh * 4 + (lane % 16) / 4; \
+_Pragma("unroll") \
+        for (int b = 0; b < 4; ++b) { \
+          const int dcol = b * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4); \
+          const uint16_t* src = vt + krow * kVStride + dcol; \
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src)); \
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * kVStride)); \
+          const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y, \
+                                     __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y); \
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[ks2], o[b], 0, 0, 0); \
+        } \
+      } \
+    } \
+  } while (0)
   fetch_ids(0);
-  issue(0);
-  if (ntiles > 1) fetch_ids(1);
-  commit(0);
+  issue(0, st0);
+  if (ntiles > 1) {
+    fetch_ids(1);
+    issue(1, st1);
+  }
+  if (ntiles > 2) fetch_ids(2);
+  commit(0, st0);
   __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      issue(t + 1);
-      if (t + 2 < ntiles) fetch_ids(t + 2);
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 2 < ntiles) {                     // even tile: st0 free, st1 holds tile t+1
+      issue(t + 2, st0);
+      if (t + 3 < ntiles) fetch_ids(t + 3);
     }
-    const int kb0 = t * kTileK;
-    if (wave_active && kb0 <= wave_max_pos) {
-      const uint16_t* kt = kbuf[buf];
-      const uint16_t* vt = vbuf[buf];
-      // ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K
-      //      operands read from LDS one step ahead
-      f32x16 s[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
-      const uint16_t* kr0 = kt + l32 * kKStride + lh * 64;
-      const uint16_t* kr1 = kr0 + 32 * kKStride;
-      bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(kr0));
-      bf16x8 kc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1));
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 na = ka, nc = kc;
-        if (ks < 7) {
-          na = as_bf16x8(*reinterpret_cast<const uint4*>(kr0 + (ks + 1) * 8));
-          nc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1 + (ks + 1) * 8));
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s[1], 0, 0, 0);
-        ka = na;
-        kc = nc;
-      }
-      // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
-      if (kb0 + kTileK - 1 > past + q0) {
-        const int lim = my_pos - kb0 - lh * 4;                 // key offset kb*32+(i/4)*8+i%4 <= lim
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            s[kb][i] = (kb * 32 + (i / 4) * 8 + (i % 4) <= lim) ? s[kb][i] : -INFINITY;
-      }
-      // ---- online softmax (raw-score domain; exp2 of (s - m) * c)
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      // Lazy rescaling: the running maximum used as the exponent offset only moves when a
-      // score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough
-      // in fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first
-      // tile always sets it (m_run starts at -inf).
-      if (__any((tmax - m_run) * c > kLazyLog2)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = m_run * c;
-      // P^T as four B operands (16 keys each): slot j of step ks2 is s[ks2/2][(ks2%2)*8 + j]
-      bf16x8 pb[4];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) {
-        const int kb = ks2 / 2, i0 = (ks2 % 2) * 8;
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc));
-          l_run += p[j];
-        }
-        pb[ks2] = as_bf16x8(make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                                       pack_bf16(p[6], p[7])));
-      }
-      // ---- O^T += V^T P^T over four 16-key steps
-#pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) {
-        // source rows for the transposed read: keys ks2*16 + lh*4 + (lane%16)/4 (+8)
-        const int krow = ks2 * 16 + lh * 4 + (lane % 16) / 4;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int dcol = b * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-          const uint16_t* src = vt + krow * kVStride + dcol;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * kVStride));
-          const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                                     __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[ks2], o[b], 0, 0, 0);
-        }
-      }
+    PKV_PREFILL_TILE(t, 0);
+    if (t + 1 < ntiles) commit(1, st1);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 3 < ntiles) {                     // odd tile: st1 free, st0 holds tile t+2
+      issue(t + 3, st1);
+      if (t + 4 < ntiles) fetch_ids(t + 4);
     }
-    if (t + 1 < ntiles) commit(buf ^ 1);
+    PKV_PREFILL_TILE(t + 1, 1);
+    if (t + 2 < ntiles) commit(0, st0);
     __syncthreads();
   }
+#undef PKV_PREFILL_TILE
 
   // ---- normalise and store: lane owns query l32 and dims blk*32 + (i/4)*8 + lh*4 + i%4
   if (!wave_active) return;
