@@ -7,7 +7,7 @@
 // (get_buffers).  RoPE is the GPT-NeoX variant named in "TensorRT-LLM source analysis
 // report", 1.1; rotation of pairs (j, j + R/2) is the reading documented in pkv.h.
 //
-// Memory-bound: each workgroup owns kAppendTokens tokens of one request and spreads
+// Memory-bound: each workgroup owns a few consecutive packed rows (tokens) and spreads
 // the (head, 8-element group) tasks of those tokens over its 256 threads, so every
 // load and store is a 16-byte access and neighbouring lanes touch neighbouring bytes.
 // Arithmetic is fp64 with contraction off and one rounding per stored element, so the
@@ -19,7 +19,43 @@ namespace pkv {
 namespace {
 
 constexpr int kAppendThreads = 256;
-constexpr int kAppendTokens = 4;
+constexpr int kMaxTokensPerWg = 8;
+constexpr int kFlatMaxRequests = 4096;
+
+// 8 raw io elements as loaded (bf16: one 16-byte vector; fp32: two)
+struct Raw8 {
+  uint4 a, b;
+};
+
+template <int F>
+__device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {
+  Raw8 r;
+  if constexpr (F == F_BF16) {
+    r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    r.b = make_uint4(0, 0, 0, 0);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+    r.a = p[0];
+    r.b = p[1];
+  }
+  return r;
+}
+
+template <int F>
+__device__ __forceinline__ void widen8(const Raw8& r, double (&x)[8]) {
+  if constexpr (F == F_BF16) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = static_cast<double>(bf16_to_f32(w[i] & 0xFFFFu));
+      x[2 * i + 1] = static_cast<double>(bf16_to_f32(w[i] >> 16));
+    }
+  } else {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = static_cast<double>(__uint_as_float(w[i]));
+  }
+}
 
 template <int F>
 __device__ __forceinline__ void load8(const void* base, int64_t off, double (&x)[8]) {
@@ -51,7 +87,7 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const double (&y
   } else if constexpr (F == F_BF16) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f64_to_bf16(y[2 * i]) | (f64_to_bf16(y[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = f64x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     uint32_t w[2] = {0u, 0u};
@@ -62,8 +98,8 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const double (&y
 }
 
 // y1 = x1*c - x2*s, y2 = x2*c + x1*s: two fp64 products and one add/subtract each.
-__device__ __forceinline__ void rotate8(const double (&x1)[8], const double (&x2)[8],
-                                        const double2* __restrict__ cs, double (&y1)[8], double (&y2)[8]) {
+__device__ __forceinline__ void rotate8(const double (&x1)[8], const double (&x2)[8], const double2 (&cs)[8],
+                                        double (&y1)[8], double (&y2)[8]) {
 #pragma clang fp contract(off)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -77,79 +113,186 @@ __device__ __forceinline__ void rotate8(const double (&x1)[8], const double (&x2
   }
 }
 
-__device__ __forceinline__ int64_t pool_off(const AppendArgs& a, int32_t blk, int which, int slot, int g) {
-  return ((static_cast<int64_t>(blk) * 2 + which) * a.T + slot) * static_cast<int64_t>(a.Hkv) * a.D +
-         static_cast<int64_t>(g) * a.D;
-}
+// Where one token goes: its packed row, request, absolute position and pool slot.
+struct TokenSlot {
+  int64_t row;
+  int32_t r, m, blk, slot;      // blk < 0: table entry out of range (skip the K/V store)
+};
 
+// One (token, task) unit of work.  Tasks of a token: rotation groups of 8 pairs for
+// every q and k head, pass-through groups of 8 dims past the rotary part, and groups of
+// 8 v dims.  Loads of a task are issued before any of its arithmetic.
+constexpr int kHeadsPerRotTask = 4;
+
+// One (token, task) unit of work.  Tasks of a token, in order: rotation tasks (one
+// group of 8 pairs for up to kHeadsPerRotTask q/k heads, so the table slice is read
+// once for all of them), pass-through groups of 8 dims past the rotary part, and
+// groups of 8 v dims.  A task's loads are all issued before its arithmetic.
 template <int IO, int KV, bool ROPE>
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
-  const int r = blockIdx.y;
-  const int n = a.ctx_len[r];
-  const int tok0 = blockIdx.x * kAppendTokens;
-  if (tok0 >= n) return;                                   // uniform over the block
-  const int64_t row0 = block_prefix(a.ctx_len, r);
-  const int past = a.seq_len[r] - n;
-  const int Hq = a.q ? a.H : 0;
+__device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot& tk, int t, int Hq,
+                                            const void* __restrict__ q, const void* __restrict__ k,
+                                            const void* __restrict__ v, const double* __restrict__ cs_base,
+                                            void* __restrict__ q_out, void* __restrict__ pool) {
   const int R = ROPE ? a.R : 0;
   const int half = R / 2;
-  const int rg = R / 16;                                   // rotation tasks per q/k head
-  const int pg = (a.D - R) / 8;                            // pass-through tasks per q/k head
-  const int vg = a.D / 8;                                  // tasks per v head
+  const int rg = R / 16, pg = (a.D - R) / 8, vg = a.D / 8;
   const int qk = Hq + a.Hkv;
-  const int per_tok = qk * (rg + pg) + a.Hkv * vg;
-  const int ntok = min(kAppendTokens, n - tok0);
-  for (int task = threadIdx.x; task < ntok * per_tok; task += kAppendThreads) {
-    const int it = task / per_tok;
-    int t = task - it * per_tok;
-    const int i = tok0 + it;
-    const int64_t row = row0 + i;
-    const int m = past + i;
-    if (row >= a.N || m < 0) continue;
-    const int64_t lblk = m / a.T;
-    const int slot = m % a.T;
-    const int32_t blk = lblk < a.mbps ? a.table[static_cast<int64_t>(r) * a.mbps + lblk] : -1;
-    const bool blk_ok = blk >= 0 && blk < a.num_blocks;
-    double x1[8], x2[8], y1[8], y2[8];
-    if (t < qk * rg) {                                      // rotated pair group
-      const int head = t / rg, j0 = (t % rg) * 8;
-      const bool isq = head < Hq;
-      const void* src = isq ? a.q : a.k;
-      const int64_t off = isq ? row * a.q_stride + static_cast<int64_t>(head) * a.D
-                              : row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
-      if (m >= a.max_pos) continue;
-      load8<IO>(src, off + j0, x1);
-      load8<IO>(src, off + j0 + half, x2);
-      const double2* cs = reinterpret_cast<const double2*>(a.cos_sin) + static_cast<int64_t>(m) * half + j0;
-      rotate8(x1, x2, cs, y1, y2);
-      if (isq) {
-        const int64_t o = row * a.H * a.D + static_cast<int64_t>(head) * a.D;
-        store8<IO>(a.q_out, o + j0, y1, 1.0);
-        store8<IO>(a.q_out, o + j0 + half, y2, 1.0);
-      } else if (blk_ok) {
-        const int64_t o = pool_off(a, blk, 0, slot, head - Hq);
-        store8<KV>(a.pool, o + j0, y1, a.inv_k_scale);
-        store8<KV>(a.pool, o + j0 + half, y2, a.inv_k_scale);
+  const int nhc = (qk + kHeadsPerRotTask - 1) / kHeadsPerRotTask;
+  auto pool_off = [&](int which, int g) {
+    return ((static_cast<int64_t>(tk.blk) * 2 + which) * a.T + tk.slot) * static_cast<int64_t>(a.Hkv) * a.D +
+           static_cast<int64_t>(g) * a.D;
+  };
+  auto head_src = [&](int head, const void*& src, int64_t& off) {
+    const bool isq = head < Hq;
+    src = isq ? q : k;
+    off = isq ? tk.row * a.q_stride + static_cast<int64_t>(head) * a.D
+              : tk.row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
+  };
+  if (t < nhc * rg) {                                       // rotated pair groups
+    if (tk.m >= a.max_pos) return;
+    const int hc = t / rg, j0 = (t % rg) * 8;
+    const int h0 = hc * kHeadsPerRotTask;
+    const int nh = min(kHeadsPerRotTask, qk - h0);
+    Raw8 r1[kHeadsPerRotTask], r2[kHeadsPerRotTask];
+#pragma unroll
+    for (int u = 0; u < kHeadsPerRotTask; ++u) {
+      if (u < nh) {
+        const void* src;
+        int64_t off;
+        head_src(h0 + u, src, off);
+        r1[u] = load_raw8<IO>(src, off + j0);
+        r2[u] = load_raw8<IO>(src, off + j0 + half);
       }
-    } else if (t < qk * (rg + pg)) {                        // dimensions past the rotary part
-      t -= qk * rg;
-      const int head = t / pg, j = R + (t % pg) * 8;
-      const bool isq = head < Hq;
-      const void* src = isq ? a.q : a.k;
-      const int64_t off = isq ? row * a.q_stride + static_cast<int64_t>(head) * a.D
-                              : row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
-      load8<IO>(src, off + j, x1);
-      if (isq) {
-        store8<IO>(a.q_out, row * a.H * a.D + static_cast<int64_t>(head) * a.D + j, x1, 1.0);
-      } else if (blk_ok) {
-        store8<KV>(a.pool, pool_off(a, blk, 0, slot, head - Hq) + j, x1, a.inv_k_scale);
-      }
-    } else {                                                // values, not rotated
-      t -= qk * (rg + pg);
-      const int g = t / vg, j = (t % vg) * 8;
-      load8<IO>(a.v, row * a.kv_stride + static_cast<int64_t>(g) * a.D + j, x1);
-      if (blk_ok) store8<KV>(a.pool, pool_off(a, blk, 1, slot, g) + j, x1, a.inv_v_scale);
     }
+    const double2* cs = reinterpret_cast<const double2*>(cs_base) + static_cast<int64_t>(tk.m) * half + j0;
+    double2 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = cs[i];
+#pragma unroll
+    for (int u = 0; u < kHeadsPerRotTask; ++u) {
+      if (u >= nh) break;
+      const int head = h0 + u;
+      double x1[8], x2[8], y1[8], y2[8];
+      widen8<IO>(r1[u], x1);
+      widen8<IO>(r2[u], x2);
+      rotate8(x1, x2, c, y1, y2);
+      if (head < Hq) {
+        const int64_t o = tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D;
+        store8<IO>(q_out, o + j0, y1, 1.0);
+        store8<IO>(q_out, o + j0 + half, y2, 1.0);
+      } else if (tk.blk >= 0) {
+        const int64_t o = pool_off(0, head - Hq);
+        store8<KV>(pool, o + j0, y1, a.inv_k_scale);
+        store8<KV>(pool, o + j0 + half, y2, a.inv_k_scale);
+      }
+    }
+  } else if (t < nhc * rg + qk * pg) {                      // dimensions past the rotary part
+    t -= nhc * rg;
+    const int head = t / pg, j = R + (t % pg) * 8;
+    const void* src;
+    int64_t off;
+    head_src(head, src, off);
+    double x[8];
+    load8<IO>(src, off + j, x);
+    if (head < Hq)
+      store8<IO>(q_out, tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D + j, x, 1.0);
+    else if (tk.blk >= 0)
+      store8<KV>(pool, pool_off(0, head - Hq) + j, x, a.inv_k_scale);
+  } else {                                                  // values, not rotated
+    t -= nhc * rg + qk * pg;
+    const int g = t / vg, j = (t % vg) * 8;
+    double x[8];
+    load8<IO>(v, tk.row * a.kv_stride + static_cast<int64_t>(g) * a.D + j, x);
+    if (tk.blk >= 0) store8<KV>(pool, pool_off(1, g) + j, x, a.inv_v_scale);
+  }
+}
+
+__device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row, int r, int i) {
+  TokenSlot tk;
+  tk.row = row;
+  tk.r = r;
+  tk.m = a.seq_len[r] - a.ctx_len[r] + i;
+  const int64_t lblk = tk.m / a.T;
+  int32_t blk = (tk.m >= 0 && lblk < a.mbps) ? a.table[static_cast<int64_t>(r) * a.mbps + lblk] : -1;
+  tk.blk = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  tk.slot = tk.m % a.T;
+  return tk;
+}
+
+// FLAT: the grid walks the packed rows, tokens_per_wg consecutive rows per workgroup,
+// and each workgroup finds the rows' requests through an LDS prefix scan of the
+// context lengths (batches of at most kFlatMaxRequests requests).  Otherwise the grid
+// is (row tile, request), for any batch size.
+template <int IO, int KV, bool ROPE, bool FLAT>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, int tokens_per_wg) {
+  __shared__ int32_t s_cu[kFlatMaxRequests + 1];
+  __shared__ TokenSlot s_tok[kMaxTokensPerWg];
+  const int Hq = a.q ? a.H : 0;
+  int ntok;
+  if constexpr (FLAT) {
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * tokens_per_wg;
+    if (row0 >= a.N) return;                               // uniform
+    ntok = static_cast<int>(min<int64_t>(tokens_per_wg, a.N - row0));
+    // inclusive scan of ctx_len into s_cu[1..B] (s_cu[0] = 0), chunked per thread
+    const int B = a.B;
+    const int per = (B + kAppendThreads - 1) / kAppendThreads;
+    const int b0 = threadIdx.x * per, b1 = min(b0 + per, B);
+    int32_t local = 0;
+    for (int b = b0; b < b1; ++b) local += a.ctx_len[b];
+    __shared__ int32_t s_part[kAppendThreads];
+    s_part[threadIdx.x] = local;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int32_t run = 0;
+      for (int w = 0; w < kAppendThreads; ++w) {
+        const int32_t x = s_part[w];
+        s_part[w] = run;
+        run += x;
+      }
+      s_cu[0] = 0;
+    }
+    __syncthreads();
+    int32_t run = s_part[threadIdx.x];
+    for (int b = b0; b < b1; ++b) {
+      run += a.ctx_len[b];
+      s_cu[b + 1] = run;
+    }
+    __syncthreads();
+    if (threadIdx.x < ntok) {
+      const int64_t row = row0 + threadIdx.x;
+      int lo = 0, hi = B - 1;                              // request r: s_cu[r] <= row < s_cu[r+1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (s_cu[mid] <= row) lo = mid; else hi = mid - 1;
+      }
+      s_tok[threadIdx.x] = make_slot(a, row, lo, static_cast<int>(row - s_cu[lo]));
+    }
+  } else {
+    const int r = blockIdx.y;
+    const int n = a.ctx_len[r];
+    const int tok0 = blockIdx.x * tokens_per_wg;
+    if (tok0 >= n) return;                                 // uniform
+    const int64_t rowr = block_prefix(a.ctx_len, r);
+    ntok = min(tokens_per_wg, n - tok0);
+    if (threadIdx.x < ntok)
+      s_tok[threadIdx.x] = make_slot(a, rowr + tok0 + threadIdx.x, r, tok0 + threadIdx.x);
+  }
+  __syncthreads();
+  const int R = ROPE ? a.R : 0;
+  const int per_tok = ((Hq + a.Hkv + kHeadsPerRotTask - 1) / kHeadsPerRotTask) * (R / 16) +
+                      (Hq + a.Hkv) * ((a.D - R) / 8) + a.Hkv * (a.D / 8);
+  const int total = ntok * per_tok;
+  const void* __restrict__ q = a.q;
+  const void* __restrict__ k = a.k;
+  const void* __restrict__ v = a.v;
+  const double* __restrict__ cs = a.cos_sin;
+  void* __restrict__ q_out = a.q_out;
+  void* __restrict__ pool = a.pool;
+  for (int task = threadIdx.x; task < total; task += kAppendThreads) {
+    const int it = task / per_tok;
+    const TokenSlot tk = s_tok[it];
+    if (tk.row >= a.N || tk.m < 0) continue;
+    append_task<IO, KV, ROPE>(a, tk, task - it * per_tok, Hq, q, k, v, cs, q_out, pool);
   }
 }
 
@@ -170,11 +313,22 @@ __global__ void rope_table_kernel(double base, int R, int max_pos, double* __res
 
 template <int IO, int KV>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
-  const dim3 grid((a.max_n + kAppendTokens - 1) / kAppendTokens, a.B);
-  if (a.rope)
-    hipLaunchKernelGGL((append_kernel<IO, KV, true>), grid, dim3(kAppendThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((append_kernel<IO, KV, false>), grid, dim3(kAppendThreads), 0, s, a);
+  // enough workgroups to fill the chip: about N / 512 tokens each, at most 8
+  int64_t want = a.N / 512;
+  const int tpw = static_cast<int>(want < 1 ? 1 : want > kMaxTokensPerWg ? kMaxTokensPerWg : want);
+  if (a.B <= kFlatMaxRequests) {
+    const dim3 grid(static_cast<unsigned>((a.N + tpw - 1) / tpw));
+    if (a.rope)
+      hipLaunchKernelGGL((append_kernel<IO, KV, true, true>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+    else
+      hipLaunchKernelGGL((append_kernel<IO, KV, false, true>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+  } else {
+    const dim3 grid((a.max_n + tpw - 1) / tpw, a.B);
+    if (a.rope)
+      hipLaunchKernelGGL((append_kernel<IO, KV, true, false>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+    else
+      hipLaunchKernelGGL((append_kernel<IO, KV, false, false>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+  }
   return hipGetLastError();
 }
 

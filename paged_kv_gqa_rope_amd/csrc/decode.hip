@@ -20,7 +20,7 @@
 //   * an fp8 cache is dequantised to bf16 on load (exact: every e4m3 value is a
 //     bf16 value); k_scale folds into the softmax scale and v_scale into the
 //     combine, so the pass works on raw codes times one.
-// Pass 2, one wave per (request, query head): M = max m_s, L = sum 2^(m_s-M) l_s,
+// Pass 2, one workgroup per (request, query head): M = max m_s, L = sum 2^(m_s-M) l_s,
 // O = sum 2^(m_s-M) o_s / L in a fixed order (no atomics: bitwise reproducible).
 #include <math.h>
 
@@ -311,26 +311,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-__global__ __launch_bounds__(kWave) void decode_combine_kernel(AttnArgs a) {
-  const int h = blockIdx.x, rg = blockIdx.y, lane = threadIdx.x;
+// One workgroup of kD threads per (generation request, query head).  Thread s < ns
+// first loads split s's (m, l); a fixed-shape tree gives M = max m and L = sum 2^(m-M) l;
+// then thread d sums 2^(m_s-M) o_s[d] over the splits in order, eight loads in flight.
+__global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
+  static_assert(kD >= 128, "one thread per split needs kD >= kMaxSplits");
+  const int h = blockIdx.x, rg = blockIdx.y, t = threadIdx.x;
   const int r = a.req_begin + rg;
   const int S = a.seq_len[r];
   const int ns = min((S + a.chunk - 1) / a.chunk, a.max_splits);
   const int64_t base = (static_cast<int64_t>(rg) * a.H + h) * a.max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2f(a.ws_ml[(base + s) * 2] - M);
-    L += w * a.ws_ml[(base + s) * 2 + 1];
-    o0 += w * a.ws_o[(base + s) * kD + lane];
-    o1 += w * a.ws_o[(base + s) * kD + lane + kWave];
+  __shared__ float s_w[kD];
+  __shared__ float s_red[kD / kWave];
+  const float m_t = t < ns ? a.ws_ml[(base + t) * 2] : -INFINITY;
+  const float l_t = t < ns ? a.ws_ml[(base + t) * 2 + 1] : 0.f;
+  float M = wave_max(m_t);
+  if (t % kWave == 0) s_red[t / kWave] = M;
+  __syncthreads();
+  M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kD / kWave; ++w) M = fmaxf(M, s_red[w]);
+  const float w_t = t < ns ? exp2f(m_t - M) : 0.f;
+  s_w[t] = w_t;
+  float L = wave_sum(w_t * l_t);
+  __syncthreads();
+  if (t % kWave == 0) s_red[t / kWave] = L;
+  __syncthreads();
+  L = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kD / kWave; ++w) L += s_red[w];
+  float o = 0.f;
+  const float* op = a.ws_o + base * kD + t;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = op[static_cast<int64_t>(s + u) * kD];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o += s_w[s + u] * v[u];
   }
-  const float inv = a.v_scale / L;
+  for (; s < ns; ++s) o += s_w[s] * op[static_cast<int64_t>(s) * kD];
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(a.row_begin) + rg) * a.H * kD +
                   static_cast<int64_t>(h) * kD;
-  out[lane] = static_cast<uint16_t>(f32_to_bf16(o0 * inv));
-  out[lane + kWave] = static_cast<uint16_t>(f32_to_bf16(o1 * inv));
+  out[t] = static_cast<uint16_t>(f32_to_bf16(o * (a.v_scale / L)));
 }
 
 }  // namespace
@@ -346,7 +369,7 @@ hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.H, a.req_end - a.req_begin);
-  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kD), 0, s, a);
   return hipGetLastError();
 }
 

@@ -43,6 +43,30 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
   return sign | static_cast<uint32_t>(q);
 }
 
+// fp64 -> bf16, the same rounding as f64_to_bf16 by another route: round to fp32 with
+// round-to-odd (truncate, then set the lowest bit if anything was dropped) and round
+// that to bf16 to nearest-even in hardware.  fp32 keeps 16 more bits than bf16 (>= 2
+// are needed), so the two roundings compose to a single nearest-even rounding
+// (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums: proved
+// algorithms using rounding to odd").  Returns a pair packed as lo | hi << 16.
+__device__ __forceinline__ float f64_to_f32_odd(double x) {
+  const float f = static_cast<float>(x);                    // nearest-even
+  const double back = static_cast<double>(f);
+  uint32_t b = __float_as_uint(f);
+  if (back != x) {                                          // inexact (or NaN)
+    if (fabs(back) > fabs(x)) b -= 1;                       // step back toward zero: truncation
+    b |= 1u;                                                // sticky bit
+  }
+  return __uint_as_float(b);
+}
+
+typedef float pkv_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pkv_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f64x2_to_bf16x2(double lo, double hi) {
+  const pkv_f32x2 v = {f64_to_f32_odd(lo), f64_to_f32_odd(hi)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, pkv_bf16x2));
+}
+
 // fp64 -> OCP E4M3 in one rounding (nearest-even), saturating finite overflow and
 // infinities to +-448.  Kept part: exponent and top 3 fraction bits; 49 bits dropped.
 __device__ __forceinline__ uint32_t f64_to_e4m3(double x) {

@@ -238,3 +238,25 @@ def test_context_chunks_blocks_and_groups(H, T, G):
     st = run_step(H, b)
     assert_bits_equal(st.q_out_host(), O.run(b)["q_out"], "q_out")
     compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
+
+
+def test_fp64_to_bf16_store_edge_values(H):
+    # fp32 io into a bf16 cache: every stored element is one fp64 -> bf16 rounding.
+    # History values hit exact bf16 ties (both parities), fp32 subnormals, values at the
+    # bf16 overflow boundary and signed zeros; the oracle's codec decides every bit.
+    sh = W.Shape("cvt", 2, 1, 128, 16, W.FP32, W.BF16, 1e4)
+    rng = np.random.default_rng(77)
+    ties = (np.arange(1, 257, dtype=np.uint32) << 16 | 0x8000).view(np.float32)            # x.5 ulp, both parities
+    special = np.array([0.0, -0.0, 1e-39, -1e-39, 3e-45, 1.17549435e-38, 3.3895314e38, 3.3961e38, 3.4e38, -3.4e38,
+                        1.0000001, 0.99999994, 65504.0, 2.0 ** -133, 1.5 * 2.0 ** -133], np.float32)
+    pool_vals = np.concatenate([ties, -ties, special,
+                                rng.standard_normal(4000).astype(np.float32) * np.exp2(rng.integers(-130, 120, 4000)).astype(np.float32)])
+    def fill(tag, r, rows, heads):
+        if tag in ("hk", "hv"):
+            n = rows * heads * 128
+            return np.resize(pool_vals if tag == "hk" else pool_vals[::-1], n).reshape(rows, heads, 128).astype(np.float32)
+        return rng.standard_normal((rows, heads, 128)).astype(np.float32)
+    b = crafted(sh, gen_past=[40, 3], seed=8, fill=fill)
+    case("fp64->bf16 store edges")
+    st = run_step(H, b)
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(W.BF16)), "bf16 pool")
