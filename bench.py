@@ -117,17 +117,33 @@ def run_workload(k: int, steps: int, warmup: int) -> dict:
     return res
 
 
-def roofline_for(res: dict) -> dict:
+def measured_traffic(kernel: str, k: int):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/pmc_traffic.json),
+    or None when absent or when the kernel's sources changed since the measurement."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    entry = json.load(open(path)).get("kernels", {}).get(f"{kernel}@{k}")
+    if not entry:
+        return None
+    h = hashlib.sha256()
+    for f in entry["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return entry["hbm_bytes_per_launch"] if h.hexdigest() == entry["sha256"] else None
+
+
+def roofline_for(res: dict, k: int) -> dict:
     kern = res["kernels"]
     w = res["work"]
     if "decode_split" in kern and w["decode_bytes"] > 0 and w["ctx_flops"] == 0:
         ach = w["decode_bytes"] / (kern["decode_split"]["avg_us"] * 1e-6) / 1e9
         return dict(kernel="decode_split", bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=ach / HBM_PEAK_GBS, traffic=None)
+                    frac=ach / HBM_PEAK_GBS, traffic=measured_traffic("decode_split", k))
     name = "prefill_mfma" if "prefill_mfma" in kern else "attn_generic_ctx"
     ach = w["ctx_flops"] / (kern[name]["avg_us"] * 1e-6) / 1e12
     return dict(kernel=name, bound="mfma", achieved=ach, peak=BF16_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=ach / BF16_DENSE_PEAK_TFLOPS, traffic=None)
+                frac=ach / BF16_DENSE_PEAK_TFLOPS, traffic=measured_traffic(name, k))
 
 
 def cpu_baseline(k: int = HEADLINE, budget_s: float = 12.0) -> dict:
@@ -216,7 +232,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) values, seeded lengths and block permutation)",
         "config": {"workload": head["workload"], "tok_per_s": head["tok_per_s"],
                    "decode_GBps": head.get("decode_GBps"), "pct_hbm_peak": 100 * head.get("decode_GBps", 0) / HBM_PEAK_GBS},
-        "roofline": roofline_for(head),
+        "roofline": roofline_for(head, head_k),
     }
     others = {}
     for k, r in results.items():
@@ -231,7 +247,7 @@ def main() -> int:
             o["decode_pct_hbm_peak"] = 100 * r["decode_GBps"] / HBM_PEAK_GBS
         if "prefill_TFLOPs" in r:
             o["prefill_pct_bf16_peak"] = 100 * r["prefill_TFLOPs"] / BF16_DENSE_PEAK_TFLOPS
-        o["roofline"] = roofline_for(r)
+        o["roofline"] = roofline_for(r, k)
         others[f"workload_{k}"] = o
     line["workloads"] = others
     if not args.no_cpu_baseline:
