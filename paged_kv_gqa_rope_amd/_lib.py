@@ -10,7 +10,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# PKV_LIB_PATH selects another build of the same library (for A/B measurements)
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1

@@ -9,21 +9,25 @@
 // block table ("TensorRT-LLM source teardown part 1", KV cache manager interfaces).
 //
 // CDNA4 mapping:
-//  * one workgroup = one KV head's whole GQA group (G = 1, 2, 4 or 8) for a block of
-//    query positions: 4 waves (8 when G = 8), each owning 32 query rows of one query
-//    head, so every K/V tile staged in LDS feeds all G heads that share it; two
-//    workgroups share a CU so one's softmax overlaps the other's MFMAs;
+//  * one workgroup = one KV head's whole GQA group (G = 1, 2, 4 or 8 query heads) for a
+//    block of query positions: NW waves, each owning 32 query rows of one query head,
+//    so every K/V tile staged in LDS feeds NW waves (all G heads that share it);
+//  * K/V tiles (64 keys x 128 dims each) travel from the pool straight into LDS with
+//    global_load_lds_dwordx4 (no register staging, no LDS store instructions) through
+//    a ring of NS stages, so NS-1 tiles are in flight while one is computed; each
+//    16-byte chunk is placed at an XOR-swizzled position so that the reads below are
+//    free of bank conflicts without padding;
 //  * the transposed products keep the softmax in-lane: S^T = K Q^T on
 //    v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims of K from LDS, B = Q^T held in
 //    registers), so lane l owns query l%32 and 16 keys per 32-key block, and the row
 //    max/sum need one cross-lane step (lanes l and l^32);
 //  * O^T = V^T P^T: B = P^T straight from the score accumulators (converted to bf16),
 //    A = V^T read from LDS with ds_read_b64_tr_b16;
-//  * 64-key tiles are double-buffered in LDS (global loads for tile t+1 are in flight
-//    while tile t is computed), block IDs are fetched two tiles ahead;
 //  * only tiles that cross the diagonal are masked, fully masked tiles are skipped, and
-//    the output rescale is skipped when no lane's running maximum moved.
+//    the output rescale is skipped unless some lane's running maximum grew by > 2^8.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -32,35 +36,70 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 128;
-constexpr int kTileK = 64;                 // keys per LDS tile
-constexpr int kKStride = 136;              // LDS row stride of K (272 B: b128 reads conflict-free)
-constexpr int kVStride = 160;              // LDS row stride of V (320 B: the 4 rows of a transposed read hit disjoint banks)
-constexpr int kKBuf = kTileK * kKStride;
-constexpr float kLazyLog2 = 8.f;           // rescale only when the maximum grows by > 2^8
-constexpr int kXcds = 8;                   // MI355X accelerator complex dies
-constexpr int kVBuf = kTileK * kVStride;
+constexpr int kTileK = 64;                     // keys per LDS tile
+constexpr int kRowBytes = kD * 2;              // one key's K (or V) row of one KV head
+constexpr int kTileBytes = kTileK * kRowBytes; // 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;    // K tile, then V tile
+constexpr int kChunksPerStage = kStageBytes / 1024;   // 1 KB per wave-wide 16-byte load
+constexpr float kLazyLog2 = 8.f;               // rescale only when the maximum grows by > 2^8
+constexpr int kXcds = 8;                       // MI355X accelerator complex dies
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+// LDS swizzles: 16-byte chunk c of tile row r sits at chunk position c ^ f(r).
+//  K is read with ds_read_b128, 16 lanes per phase on 16 rows at one chunk: f = r & 15
+//  spreads them over all 64 banks.  V is read with ds_read_b64_tr_b16, each phase on 4
+//  rows x 4 neighbouring chunks: f = (r & 3) << 2 puts the 4 rows in different chunk groups.
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// s_waitcnt immediate for vmcnt(n) that leaves the other counters unconstrained
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ const lds_u32x4* lds_at(uint32_t byte) {
+  return reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(byte));
+}
 
-template <int NW, int G>
+// ds_read_b64_tr_b16 issued as inline asm: the compiler would otherwise wait for every
+// outstanding global-to-LDS tile load before it (it cannot tell the stages apart).  The
+// results are only valid after lds_wait() has been passed them.
+template <int OFF>
+__device__ __forceinline__ s16x4 tr_read(uint32_t addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// wait for all LDS reads of this wave; the operands tie the values read to the wait
+__device__ __forceinline__ void lds_wait(s16x4& a0, s16x4& a1, s16x4& a2, s16x4& a3, s16x4& a4, s16x4& a5,
+                                         s16x4& a6, s16x4& a7) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
+}
+
+// BT: a cache block holds a whole number of 64-key tiles (tokens_per_block >= 64), so a
+// tile sits in one block and its address is scalar.  Otherwise a tile spans 64/T <= 4
+// blocks and each lane picks its row's block among the tile's (scalar) block IDs.
+template <int NW, int G, int NS, bool BT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(AttnArgs a) {
   constexpr int RB = NW / G;               // 32-row blocks per workgroup
   constexpr int ROWS = RB * 32;            // query positions per workgroup
-  constexpr int NT = NW * kWave;
+  constexpr int LPW = kChunksPerStage / NW;   // 1 KB loads per wave per tile
+  static_assert(kChunksPerStage % NW == 0, "whole loads per wave");
+  static_assert(NS >= 2, "at least double buffering");
   // XCD-aware placement: workgroups go to the 8 XCDs round-robin by linear ID, so when
   // the (request, KV head) pairs split evenly, linear ID L runs on XCD L % 8 and takes
   // that XCD's (L / 8)-th item; all query tiles of one pair then share one L2.
@@ -97,13 +136,15 @@ void prefill_kernel(AttnArgs a) {
   const int ntiles = (kv_end + kTileK - 1) / kTileK;
   const int64_t row0 = wave_prefix(a.ctx_len, r);                       // packed row of request r
   const int tshift = a.tshift, tmask = a.T - 1;
-  const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;
-  const int64_t blk_elems = 2 * static_cast<int64_t>(a.T) * kv_row;
-  const int32_t* table = a.table + static_cast<int64_t>(r) * a.mbps;
+  // The block table is read-only here: reading it through the constant address space keeps
+  // its uniform reads on the scalar unit although the tile loads write memory (LDS).
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(r) * a.mbps);
   const int last_blk = (S - 1) >> tshift;
 
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][kKBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][kVBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * kStageBytes];
+  const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) unsigned char*)(ring)));
 
   // ---- Q^T (B operand): query q0 + l32, dims lh*64 + ks*8 + j for ks = 0..7
   bf16x8 qf[8];
@@ -112,197 +153,247 @@ void prefill_kernel(AttnArgs a) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row0 + qi) * a.q_stride +
                          static_cast<int64_t>(h) * kD + lh * 64;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + ks * 8));
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + ks * 8));
   }
   const int my_pos = past + min(q0 + l32, n - 1);                       // this lane's query position
   const float c = a.scale_log2;
 
-  // ---- cooperative tile loads: thread t moves the 16-byte chunk t%16 of K and V rows
-  //      t/16 + u*NT/16 of the tile
-  constexpr int KCH = (kTileK * 16) / NT;              // 16-byte chunks of K (and of V) per thread
-  static_assert(KCH == 2 || KCH == 4, "4 or 8 waves per workgroup");
-  const int ccol = (threadIdx.x % 16) * 8;
-  const int crow0 = threadIdx.x / 16;                  // chunk u covers tile row crow0 + u*NT/16
-  // Two register stages (tiles t+1 and t+2 in flight) and the block IDs of the tile
-  // after those, all in named registers (indexable arrays here end up in scratch).
-  struct Stage {
-    u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
+  // ---- tile loads: wave w moves the 1 KB chunks q = w*LPW + j of a stage (K tile: q < 16,
+  //      V tile: q >= 16); chunk q holds tile rows 4*(q%16) .. +3 and lane i lands at row
+  //      4*(q%16) + i/16, chunk position i%16, so it fetches that row's chunk (i%16) ^ f(row).
+  const uint32_t kvrb = static_cast<uint32_t>(a.Hkv) * kRowBytes;   // bytes per token row
+  const uint32_t vofs = static_cast<uint32_t>(a.T) * kvrb;          // V half of a block
+  const int64_t blk_bytes = 2 * static_cast<int64_t>(vofs);
+  const char* pool_g = static_cast<const char*>(a.pool) + static_cast<int64_t>(g) * kRowBytes;
+  auto ld_row = [&](int j) __attribute__((always_inline)) { return 4 * ((wave * LPW + j) % 16) + lane / 16; };
+  auto ld_isv = [&](int j) __attribute__((always_inline)) { return wave * LPW + j >= 16; };   // uniform
+  auto ld_col = [&](int j) __attribute__((always_inline)) {                                   // byte column
+    const int rr = ld_row(j);
+    return static_cast<uint32_t>(((lane % 16) ^ (ld_isv(j) ? swz_v(rr) : swz_k(rr))) * 16);
   };
-  Stage st0, st1;
-  int32_t in0 = 0, in1 = 0, in2 = 0, in3 = 0;
-  auto key_of = [&](int tile, int u) __attribute__((always_inline)) { return min(tile * kTileK + crow0 + u * (NT / 16), S - 1); };
-  auto id_of = [&](int tile, int u) __attribute__((always_inline)) { return table[min(key_of(tile, u) >> tshift, last_blk)]; };
-  auto fetch_ids = [&](int tile) __attribute__((always_inline)) {
-    in0 = id_of(tile, 0);
-    in1 = id_of(tile, 1);
-    if constexpr (KCH == 4) {
-      in2 = id_of(tile, 2);
-      in3 = id_of(tile, 3);
+  auto ld_dst = [&](int j) __attribute__((always_inline)) {                                   // uniform
+    const int qc = wave * LPW + j;
+    return (qc >= 16 ? kTileBytes : 0) + (qc % 16) * 1024;
+  };
+  // full-tile byte offsets inside a block (BT) -- constant across tiles
+  uint32_t off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) off[j] = (ld_isv(j) ? vofs : 0u) + ld_row(j) * kvrb + ld_col(j);
+
+  struct Ids {
+    int32_t i0, i1, i2, i3;
+  };
+  // block IDs of a tile: BT -> its one block; else its 64/T blocks (clamped to the last)
+  auto fetch = [&](int tile, Ids& x) __attribute__((always_inline)) {
+    const int b0 = __builtin_amdgcn_readfirstlane((tile * kTileK) >> tshift);
+    x.i0 = __builtin_amdgcn_readfirstlane(table[min(b0, last_blk)]);
+    if constexpr (!BT) {
+      x.i1 = __builtin_amdgcn_readfirstlane(table[min(b0 + 1, last_blk)]);
+      x.i2 = __builtin_amdgcn_readfirstlane(table[min(b0 + 2, last_blk)]);
+      x.i3 = __builtin_amdgcn_readfirstlane(table[min(b0 + 3, last_blk)]);
     }
   };
-  auto chunk_ptr = [&](int tile, int u, int32_t id) __attribute__((always_inline)) {  // K chunk; its V chunk is T rows later
-    id = (id >= 0 && id < a.num_blocks) ? id : 0;       // clamped key: never an unwritten slot
-    return static_cast<const uint16_t*>(a.pool) + static_cast<int64_t>(id) * blk_elems +
-           static_cast<int64_t>(key_of(tile, u) & tmask) * kv_row + static_cast<int64_t>(g) * kD + ccol;
-  };
-  const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
-  auto issue = [&](int tile, Stage& q) __attribute__((always_inline)) {
-    const uint16_t* p0 = chunk_ptr(tile, 0, in0);
-    const uint16_t* p1 = chunk_ptr(tile, 1, in1);
-    q.k0 = *reinterpret_cast<const u32x4*>(p0);
-    q.k1 = *reinterpret_cast<const u32x4*>(p1);
-    q.v0 = *reinterpret_cast<const u32x4*>(p0 + vofs);
-    q.v1 = *reinterpret_cast<const u32x4*>(p1 + vofs);
-    if constexpr (KCH == 4) {
-      const uint16_t* p2 = chunk_ptr(tile, 2, in2);
-      const uint16_t* p3 = chunk_ptr(tile, 3, in3);
-      q.k2 = *reinterpret_cast<const u32x4*>(p2);
-      q.k3 = *reinterpret_cast<const u32x4*>(p3);
-      q.v2 = *reinterpret_cast<const u32x4*>(p2 + vofs);
-      q.v3 = *reinterpret_cast<const u32x4*>(p3 + vofs);
-    }
-  };
-  auto commit = [&](int buf, const Stage& q) __attribute__((always_inline)) {
-    constexpr int RS = NT / 16;                         // rows between chunks
-    *reinterpret_cast<u32x4*>(&kbuf[buf][crow0 * kKStride + ccol]) = q.k0;
-    *reinterpret_cast<u32x4*>(&kbuf[buf][(crow0 + RS) * kKStride + ccol]) = q.k1;
-    *reinterpret_cast<u32x4*>(&vbuf[buf][crow0 * kVStride + ccol]) = q.v0;
-    *reinterpret_cast<u32x4*>(&vbuf[buf][(crow0 + RS) * kVStride + ccol]) = q.v1;
-    if constexpr (KCH == 4) {
-      *reinterpret_cast<u32x4*>(&kbuf[buf][(crow0 + 2 * RS) * kKStride + ccol]) = q.k2;
-      *reinterpret_cast<u32x4*>(&kbuf[buf][(crow0 + 3 * RS) * kKStride + ccol]) = q.k3;
-      *reinterpret_cast<u32x4*>(&vbuf[buf][(crow0 + 2 * RS) * kVStride + ccol]) = q.v2;
-      *reinterpret_cast<u32x4*>(&vbuf[buf][(crow0 + 3 * RS) * kVStride + ccol]) = q.v3;
+  auto valid_id = [&](int32_t id) __attribute__((always_inline)) { return (id >= 0 && id < a.num_blocks) ? id : 0; };
+  // Keys past S-1 (only in the tile that holds key S-1) are fetched from key S-1 instead:
+  // never an unwritten slot, and their scores are masked anyway.
+  auto issue = [&](int tile, int slot, const Ids& x) __attribute__((always_inline)) {
+    unsigned char* st = ring + slot * kStageBytes;
+    const int lim = S - 1 - tile * kTileK;                             // last tile row with a key
+    if constexpr (BT) {
+      const char* base = pool_g + static_cast<int64_t>(valid_id(x.i0)) * blk_bytes +
+                         static_cast<int64_t>((tile * kTileK) & tmask) * kvrb;
+      if (lim >= kTileK - 1) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+          const char* p = base + off[j];
+          __builtin_amdgcn_global_load_lds(p, (lds_void*)(st + ld_dst(j)), 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+          const uint32_t o = (ld_isv(j) ? vofs : 0u) + min(ld_row(j), lim) * kvrb + ld_col(j);
+          const char* p = base + o;
+          __builtin_amdgcn_global_load_lds(p, (lds_void*)(st + ld_dst(j)), 16, 0, 0);
+        }
+      }
+    } else {
+      const int b0 = (tile * kTileK) >> tshift;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int key = min(tile * kTileK + ld_row(j), S - 1);
+        const int sb = (key >> tshift) - b0;                          // 0 .. 64/T - 1
+        const int32_t id = valid_id(sb == 0 ? x.i0 : sb == 1 ? x.i1 : sb == 2 ? x.i2 : x.i3);
+        const char* p = pool_g + static_cast<int64_t>(id) * blk_bytes + (ld_isv(j) ? vofs : 0u) +
+                        static_cast<uint32_t>(key & tmask) * kvrb + ld_col(j);
+        __builtin_amdgcn_global_load_lds(p, (lds_void*)(st + ld_dst(j)), 16, 0, 0);
+      }
     }
   };
 
+  // ---- LDS read addresses (bytes, relative to a stage), constant across tiles
+  //  K: lane reads row kb*32 + l32, chunk lh*8 + ks -> position (lh*8 ^ f(l32)) ^ ks
+  uint32_t kofs[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kofs[ks] = l32 * kRowBytes + (((lh * 8) ^ swz_k(l32)) ^ ks) * 16;
+  //  V^T: lane reads 8 bytes at row ks2*16 + hi*8 + lh*4 + (lane%16)/4, dims b*32 +
+  //  ((lane/16)%2)*16 + 4*(lane%4): chunk b*4 + cl, stored at position ((b ^ xv) * 4) + cl
+  uint32_t vrd[4];
+  {
+    const int xv = (lane % 16) / 4;                                     // row & 3, so f = xv << 2
+    const int cl = ((lane / 16) % 2) * 2 + (lane % 4) / 2;
+    const uint32_t lp = kTileBytes + (lh * 4 + xv) * kRowBytes + cl * 16 + (lane % 2) * 8;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) vrd[b] = lp + ((b ^ xv) * 4) * 16;
+  }
+
   float m_run = -INFINITY, l_run = 0.f;      // raw-score max of query l32; this lane's partial sum
+  const bf16x2 kOnes = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   f32x16 o[4];                               // O^T[dim blk*32 + (i/4)*8 + lh*4 + i%4][query l32]
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
 
-  // Tile t is computed from LDS buffer t%2 while tiles t+1 and t+2 are in flight in
-  // the two register stages; the loop is unrolled by two so each half uses fixed
-  // stages (tile t+1 sits in the stage the other half filled).
-#define PKV_PREFILL_TILE(T_, BUF_) \
-  do { \
-    const int kb0 = (T_) * kTileK; \
-    if (wave_active && kb0 <= wave_max_pos) { \
-      const uint16_t* kt = kbuf[BUF_]; \
-      const uint16_t* vt = vbuf[BUF_]; \
-      /* ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K */ \
-      /* operands read from LDS one step ahead */ \
-      f32x16 s[2]; \
-_Pragma("unroll") \
-      for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f; \
-      const uint16_t* kr0 = kt + l32 * kKStride + lh * 64; \
-      const uint16_t* kr1 = kr0 + 32 * kKStride; \
-      bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(kr0)); \
-      bf16x8 kc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1)); \
-_Pragma("unroll") \
-      for (int ks = 0; ks < 8; ++ks) { \
-        bf16x8 na = ka, nc = kc; \
-        if (ks < 7) { \
-          na = as_bf16x8(*reinterpret_cast<const uint4*>(kr0 + (ks + 1) * 8)); \
-          nc = as_bf16x8(*reinterpret_cast<const uint4*>(kr1 + (ks + 1) * 8)); \
-        } \
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[0], 0, 0, 0); \
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s[1], 0, 0, 0); \
-        ka = na; \
-        kc = nc; \
-      } \
-      /* ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys) */ \
-      if (kb0 + kTileK - 1 > past + q0) { \
-        const int lim = my_pos - kb0 - lh * 4;                 /* key offset kb*32+(i/4)*8+i%4 <= lim */ \
-_Pragma("unroll") \
-        for (int kb = 0; kb < 2; ++kb) \
-_Pragma("unroll") \
-          for (int i = 0; i < 16; ++i) \
-            s[kb][i] = (kb * 32 + (i / 4) * 8 + (i % 4) <= lim) ? s[kb][i] : -INFINITY; \
-      } \
-      /* ---- online softmax (raw-score domain; exp2 of (s - m) * c) */ \
-      float tmax = -INFINITY; \
-_Pragma("unroll") \
-      for (int kb = 0; kb < 2; ++kb) \
-_Pragma("unroll") \
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]); \
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)); \
-      /* Lazy rescaling: the running maximum used as the exponent offset only moves when a */ \
-      /* score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough */ \
-      /* in fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first */ \
-      /* tile always sets it (m_run starts at -inf). */ \
-      if (__any((tmax - m_run) * c > kLazyLog2)) { \
-        const float m_new = fmaxf(m_run, tmax); \
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c); \
-        l_run *= alpha; \
-_Pragma("unroll") \
-        for (int b = 0; b < 4; ++b) \
-_Pragma("unroll") \
-          for (int i = 0; i < 16; ++i) o[b][i] *= alpha; \
-        m_run = m_new; \
-      } \
-      const float mc = m_run * c; \
-      /* P^T as four B operands (16 keys each): slot j of step ks2 is s[ks2/2][(ks2%2)*8 + j] */ \
-      bf16x8 pb[4]; \
-_Pragma("unroll") \
-      for (int ks2 = 0; ks2 < 4; ++ks2) { \
-        const int kb = ks2 / 2, i0 = (ks2 % 2) * 8; \
-        float p[8]; \
-_Pragma("unroll") \
-        for (int j = 0; j < 8; ++j) { \
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc)); \
-          l_run += p[j]; \
-        } \
-        pb[ks2] = as_bf16x8(make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), \
-                                       pack_bf16(p[6], p[7]))); \
-      } \
-      /* ---- O^T += V^T P^T over four 16-key steps */ \
-_Pragma("unroll") \
-      for (int ks2 = 0; ks2 < 4; ++ks2) { \
-        /* source rows for the transposed read: keys ks2*16 + lh*4 + (lane%16)/4 (+8) */ \
-        const int krow = ks2 * 16 + lh * 4 + (lane % 16) / 4; \
-_Pragma("unroll") \
-        for (int b = 0; b < 4; ++b) { \
-          const int dcol = b * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4); \
-          const uint16_t* src = vt + krow * kVStride + dcol; \
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src)); \
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * kVStride)); \
-          const uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y, \
-                                     __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y); \
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[ks2], o[b], 0, 0, 0); \
-        } \
-      } \
-    } \
-  } while (0)
-  fetch_ids(0);
-  issue(0, st0);
-  if (ntiles > 1) {
-    fetch_ids(1);
-    issue(1, st1);
-  }
-  if (ntiles > 2) fetch_ids(2);
-  commit(0, st0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 2 < ntiles) {                     // even tile: st0 free, st1 holds tile t+1
-      issue(t + 2, st0);
-      if (t + 3 < ntiles) fetch_ids(t + 3);
+  auto compute = [&](int t, int slot) __attribute__((always_inline)) {
+    const int kb0 = t * kTileK;
+    if (!(wave_active && kb0 <= wave_max_pos)) return;
+    const uint32_t sbase = ring_b + static_cast<uint32_t>(slot * kStageBytes);
+    uint32_t ka_[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka_[ks] = sbase + kofs[ks];
+    // ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K operands
+    //      read one step ahead
+    f32x16 s[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
+    auto kread = [&](int kb, int ks) __attribute__((always_inline)) {
+      return as_bf16x8(*lds_at(ka_[ks] + kb * 32 * kRowBytes));
+    };
+    bf16x8 ka = kread(0, 0), kc = kread(1, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 na = ka, nc = kc;
+      if (ks < 7) {
+        na = kread(0, ks + 1);
+        nc = kread(1, ks + 1);
+      }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s[1], 0, 0, 0);
+      ka = na;
+      kc = nc;
     }
-    PKV_PREFILL_TILE(t, 0);
-    if (t + 1 < ntiles) commit(1, st1);
-    __syncthreads();
-    if (t + 1 >= ntiles) break;
-    if (t + 3 < ntiles) {                     // odd tile: st1 free, st0 holds tile t+2
-      issue(t + 3, st1);
-      if (t + 4 < ntiles) fetch_ids(t + 4);
+    // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
+    if (kb0 + kTileK - 1 > past + q0) {
+      const int lim = my_pos - kb0 - lh * 4;                 // key offset kb*32+(i/4)*8+i%4 <= lim
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = (kb * 32 + (i / 4) * 8 + (i % 4) <= lim) ? s[kb][i] : -INFINITY;
     }
-    PKV_PREFILL_TILE(t + 1, 1);
-    if (t + 2 < ntiles) commit(0, st0);
-    __syncthreads();
+    // ---- online softmax (raw-score domain; exp2 of (s - m) * c)
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    // Lazy rescaling: the running maximum used as the exponent offset only moves when a
+    // score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough in
+    // fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first tile
+    // always sets it (m_run starts at -inf).
+    if (__any((tmax - m_run) * c > kLazyLog2)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+    // P^T as four B operands (16 keys each): slot j of step ks2 is s[ks2/2][(ks2%2)*8 + j]
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) {
+      const int kb = ks2 / 2, i0 = (ks2 % 2) * 8;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc));
+      const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]), w2 = pack_bf16(p[4], p[5]),
+                     w3 = pack_bf16(p[6], p[7]);
+      // The row sum takes the same bf16-rounded P that enters the product, two keys per
+      // dot2.  Its operands are the scalar words: fed lanes of the packed vector, hipcc
+      // emitted v_dot2c_f32_bf16 on the vector's first register four times.
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, l_run, false);
+      pb[ks2] = as_bf16x8(u32x4{w0, w1, w2, w3});
+    }
+    // ---- O^T += V^T P^T over four 16-key steps; the V^T operands of step ks2+1 are read
+    //      while the MFMAs of step ks2 run
+    uint32_t va_[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) va_[b] = sbase + vrd[b];
+    s16x4 vr[2][8];
+    auto vread = [&](auto KS2, s16x4* d) __attribute__((always_inline)) {
+      constexpr int base = decltype(KS2)::value * 16 * kRowBytes;
+      d[0] = tr_read<base>(va_[0]);
+      d[1] = tr_read<base + 8 * kRowBytes>(va_[0]);
+      d[2] = tr_read<base>(va_[1]);
+      d[3] = tr_read<base + 8 * kRowBytes>(va_[1]);
+      d[4] = tr_read<base>(va_[2]);
+      d[5] = tr_read<base + 8 * kRowBytes>(va_[2]);
+      d[6] = tr_read<base>(va_[3]);
+      d[7] = tr_read<base + 8 * kRowBytes>(va_[3]);
+      lds_wait(d[0], d[1], d[2], d[3], d[4], d[5], d[6], d[7]);
+    };
+    auto pv = [&](int ks2, const s16x4* d) __attribute__((always_inline)) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const u32x4 u = {__builtin_bit_cast(uint2, d[2 * b]).x, __builtin_bit_cast(uint2, d[2 * b]).y,
+                         __builtin_bit_cast(uint2, d[2 * b + 1]).x, __builtin_bit_cast(uint2, d[2 * b + 1]).y};
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[ks2], o[b], 0, 0, 0);
+      }
+    };
+    vread(std::integral_constant<int, 0>(), vr[0]);
+    vread(std::integral_constant<int, 1>(), vr[1]);
+    pv(0, vr[0]);
+    vread(std::integral_constant<int, 2>(), vr[0]);
+    pv(1, vr[1]);
+    vread(std::integral_constant<int, 3>(), vr[1]);
+    pv(2, vr[0]);
+    pv(3, vr[1]);
+  };
+
+  // ---- the ring: tile t lives in stage t % NS.  Iteration t waits for this wave's loads of
+  //      tile t (the NS-2 later tiles may stay in flight), meets the other waves at the
+  //      barrier -- after which tile t is complete in LDS and stage (t-1) % NS is no longer
+  //      read -- refills that stage with tile t+NS-1 and computes tile t.  Past the last tile
+  //      the loads repeat it, so every iteration has the same loads in flight.
+  const int tl = ntiles - 1;
+  {
+    Ids x[NS - 1];
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) fetch(min(u, tl), x[u]);
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(min(u, tl), u, x[u]);
   }
-#undef PKV_PREFILL_TILE
+  Ids nx;
+  fetch(min(NS - 1, tl), nx);
+  int slot = 0, fill = NS - 1;
+  for (int t = 0; t < ntiles; ++t) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPW));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(t + NS - 1, tl), fill, nx);
+    fetch(min(t + NS, tl), nx);
+    compute(t, slot);
+    slot = slot == NS - 1 ? 0 : slot + 1;
+    fill = fill == NS - 1 ? 0 : fill + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may still target this workgroup's LDS at exit
 
   // ---- normalise and store: lane owns query l32 and dims blk*32 + (i/4)*8 + lh*4 + i%4
   if (!wave_active) return;
@@ -323,24 +414,28 @@ _Pragma("unroll") \
     }
 }
 
-template <int NW, int G>
+template <int NW, int G, int NS>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   static_assert(NW % G == 0, "a workgroup holds whole query groups");
   constexpr int ROWS = (NW / G) * 32;
   const int nq = (a.max_n + ROWS - 1) / ROWS;
   const dim3 grid(nq * a.Hkv * (a.req_end - a.req_begin));
-  hipLaunchKernelGGL((prefill_kernel<NW, G>), grid, dim3(NW * kWave), 0, s, a);
+  if (a.T % kTileK == 0)   // tokens_per_block is a power of two: whole tiles per block
+    hipLaunchKernelGGL((prefill_kernel<NW, G, NS, true>), grid, dim3(NW * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<NW, G, NS, false>), grid, dim3(NW * kWave), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
+  if (a.T < 16) return hipErrorNotSupported;   // a 64-key tile spans at most 4 blocks
   switch (a.H / a.Hkv) {
-    case 1: return launch_t<4, 1>(a, s);
-    case 2: return launch_t<4, 2>(a, s);
-    case 4: return launch_t<4, 4>(a, s);
-    case 8: return launch_t<8, 8>(a, s);
+    case 1: return launch_t<8, 1, 4>(a, s);
+    case 2: return launch_t<8, 2, 4>(a, s);
+    case 4: return launch_t<8, 4, 4>(a, s);
+    case 8: return launch_t<8, 8, 4>(a, s);
     default: return hipErrorNotSupported;
   }
 }
