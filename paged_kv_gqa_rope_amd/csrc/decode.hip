@@ -43,6 +43,11 @@ constexpr int kVStride = 136;      // LDS row stride (bf16 elements) of a staged
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// 16 bytes of the cache.  A K load covers only part of each 128-byte line (the MFMA
+// operand layout), the neighbouring parts come from the next loads through the caches:
+// no nontemporal hint here (with it every partial access went to memory on its own).
+__device__ __forceinline__ uint4 load_kv(const void* p) { return *static_cast<const uint4*>(p); }
+
 // 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
   const float2 a = e4m3x2_to_f32(c.x), b = e4m3x2_hi_to_f32(c.x);
@@ -82,7 +87,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int G = a.H / a.Hkv;
   const int64_t row = static_cast<int64_t>(a.row_begin) + rg;
   const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
-  const int32_t* table = a.table + static_cast<int64_t>(r) * a.mbps;
+  // The block table is read-only here: reading it through the constant address space
+  // keeps its (wave-uniform) reads on the scalar unit, out of the vector-load queue.
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(r) * a.mbps);
 
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
 
@@ -114,9 +122,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Block IDs of a tile: tiles are 32-aligned and T is a power of two >= 16, so a tile
   // lies in one block (T >= 32) or covers two (T = 16).  Read two tiles ahead.
   auto fetch_ids = [&](int tile, int32_t (&raw)[2]) {
-    const int kb0 = (k0 + tile * kTile) >> tshift;
-    raw[0] = table[min(kb0, last_blk)];
-    raw[1] = table[min(kb0 + 1, last_blk)];
+    const int kb0 = __builtin_amdgcn_readfirstlane((k0 + tile * kTile) >> tshift);
+    raw[0] = __builtin_amdgcn_readfirstlane(table[min(kb0, last_blk)]);
+    raw[1] = __builtin_amdgcn_readfirstlane(table[min(kb0 + 1, last_blk)]);
   };
   // Issue every load of tile `tile` (ids already resolved) into `R`.
   auto issue = [&](int tile, const int32_t (&rawid)[2], TileRegs<KV>& R) {
@@ -137,11 +145,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if constexpr (KV == F_BF16) {
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base_of(key) + lg * 32);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) R.k[kb][ks] = p[ks];
+        for (int ks = 0; ks < 4; ++ks) R.k[kb][ks] = load_kv(p + ks);
       } else {
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base_of(key) + lg * 32);
-        R.k[kb][0] = p[0];
-        R.k[kb][1] = p[1];
+        R.k[kb][0] = load_kv(p);
+        R.k[kb][1] = load_kv(p + 1);
       }
     }
     const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
@@ -149,13 +157,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int key = min(tb + it * 4 + lg, kend - 1);
-        R.v[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base_of(key) + vofs + li * 8);
+        R.v[it] = load_kv(static_cast<const uint16_t*>(a.pool) + base_of(key) + vofs + li * 8);
       }
     } else {                                                   // 8 lanes per 128-byte row
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int key = min(tb + it * 8 + lane / 8, kend - 1);
-        R.v[it] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base_of(key) + vofs + (lane % 8) * 16);
+        R.v[it] = load_kv(static_cast<const uint8_t*>(a.pool) + base_of(key) + vofs + (lane % 8) * 16);
       }
     }
   };
@@ -250,31 +258,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Software pipeline: tile t+4 is in flight while tile t is computed.
+  // Software pipeline: tile t+4 is in flight while tile t is computed.  Loads and ID
+  // fetches run unconditionally (past the wave's last tile they repeat the chunk's last
+  // tile), so every path has the same loads in flight and the compiler's wait before a
+  // tile's compute covers that tile only, not the one issued after it.
   TileRegs<KV> ra, rb;
   int32_t ids_a[2], ids_b[2];
+  const int tl = ntiles - 1;
   int t = wave;
-  if (t < ntiles) {
-    fetch_ids(t, ids_a);
-    issue(t, ids_a, ra);
-    if (t + kWaves < ntiles) fetch_ids(t + kWaves, ids_b);
-  }
-  while (t < ntiles) {
-    int tn = t + kWaves;
-    if (tn < ntiles) {
-      issue(tn, ids_b, rb);
-      if (tn + kWaves < ntiles) fetch_ids(tn + kWaves, ids_a);
-    }
+  fetch_ids(min(t, tl), ids_a);
+  issue(min(t, tl), ids_a, ra);
+  fetch_ids(min(t + kWaves, tl), ids_b);
+  for (; t < ntiles; t += 2 * kWaves) {
+    issue(min(t + kWaves, tl), ids_b, rb);
+    fetch_ids(min(t + 2 * kWaves, tl), ids_a);
     compute(t, ra);
-    t = tn;
-    if (t >= ntiles) break;
-    tn = t + kWaves;
-    if (tn < ntiles) {
-      issue(tn, ids_a, ra);
-      if (tn + kWaves < ntiles) fetch_ids(tn + kWaves, ids_b);
-    }
-    compute(t, rb);
-    t = tn;
+    issue(min(t + 2 * kWaves, tl), ids_a, ra);
+    fetch_ids(min(t + 3 * kWaves, tl), ids_b);
+    if (t + kWaves < ntiles) compute(t + kWaves, rb);
   }
 
   // ---- merge the 4 waves' partial states, then write the chunk's (m, l, o)

@@ -155,8 +155,10 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   p->ws_ml_off = p->ws_o_off = p->ws_bytes = 0;
   if (!p->fast_decode) return;
   // Split-KV policy: start from kDefaultChunk keys per split, halve while the grid
-  // has fewer than kTargetDecodeItems (request, kv head, split) items, then double
-  // until no request needs more than kMaxSplits splits.  Deterministic in the lengths.
+  // has fewer than kTargetDecodeItems (request, kv head, split) items and a split still
+  // streams more than kMinChunkBytes of one KV head's K and V (shorter splits spend more
+  // of their time starting up and merging than streaming), then double until no request
+  // needs more than kMaxSplits splits.  Deterministic in the lengths.
   const int64_t T = d.tokens_per_block;
   auto count = [&](int64_t c, int64_t* max_s) {
     int64_t tot = 0, mx = 0;
@@ -168,7 +170,8 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
     *max_s = mx;
     return tot * d.num_kv_heads;
   };
-  const int64_t lo = std::max<int64_t>(64, T);
+  const int64_t key_bytes = 2 * static_cast<int64_t>(d.head_dim) * (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+  const int64_t lo = std::max<int64_t>(std::max<int64_t>(64, T), kMinChunkBytes / key_bytes);
   int64_t c = std::max<int64_t>(kDefaultChunk, T), mx = 0;
   while (count(c, &mx) < kTargetDecodeItems && c > lo) c /= 2;
   int64_t items = count(c, &mx);

@@ -34,7 +34,8 @@ struct BatchPlan {
 // Numeric limits of the split policy.
 constexpr int32_t kMaxSplits = 128;       // splits per generation request
 constexpr int32_t kDefaultChunk = 1024;    // keys per split before balancing
-constexpr int64_t kTargetDecodeItems = 2048;
+constexpr int64_t kTargetDecodeItems = 4096; // (request, kv head, split) items to aim for
+constexpr int64_t kMinChunkBytes = 256 << 10;  // one KV head's K and V per split, at least
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
 constexpr bool kHaveFastDecode = true;
 constexpr bool kHaveFastPrefill = true;
