@@ -41,12 +41,20 @@ constexpr int kTile = 32;          // keys per wave iteration
 constexpr int kD = 128;            // head_dim handled here
 constexpr int kVStride = 136;      // LDS row stride (bf16 elements) of a staged V tile
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// 16 bytes of the cache.  A K load covers only part of each 128-byte line (the MFMA
-// operand layout), the neighbouring parts come from the next loads through the caches:
-// no nontemporal hint here (with it every partial access went to memory on its own).
-__device__ __forceinline__ uint4 load_kv(const void* p) { return *static_cast<const uint4*>(p); }
+// 16 bytes of the cache, streamed.  Every K/V byte is read once per step and every load
+// instruction covers whole rows (whole 128-byte lines), so the loads carry the
+// nontemporal hint: lines are not kept for reuse that will not come.
+__device__ __forceinline__ uint4 load_kv(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// K tile in LDS: 16-byte chunk c of key row r sits at chunk position c ^ (r & 15), so the
+// 16 rows one MFMA operand read touches at one chunk fall on 16 distinct bank groups.
+__device__ __forceinline__ int kpos(int r, int c) { return c ^ (r & 15); }
 
 // 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
@@ -63,11 +71,11 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Registers of one 32-key tile in flight: K in MFMA A-operand layout (bf16: 2 key
-// blocks x 4 dim steps; fp8: the raw codes, 2 x 32 bytes) and V rows for the LDS copy.
+// Registers of one 32-key tile in flight: K and V rows as loaded (16 lanes per bf16
+// row, 8 lanes per fp8 row), copied to LDS at compute time.
 template <int KV>
 struct TileRegs {
-  uint4 k[2][4];
+  uint4 k[KV == F_BF16 ? 8 : 4];
   uint4 v[KV == F_BF16 ? 8 : 4];
 };
 
@@ -93,16 +101,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(r) * a.mbps);
 
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
 
-  // B operand Q^T: head n = li, dims lg*32 + ks*8 + j (the dim order inside a
+  // B operand Q^T: head n = li, dims ks*32 + lg*8 + j (the dim order inside a
   // contraction is free as long as K uses the same one).
   bf16x8 qf[4];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
-                         static_cast<int64_t>(g * G + min(li, G - 1)) * kD + lg * 32;
+                         static_cast<int64_t>(g * G + min(li, G - 1)) * kD + lg * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 8);
+      uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 32);
       if (li >= G) u = make_uint4(0, 0, 0, 0);
       qf[ks] = as_bf16x8(u);
     }
@@ -118,6 +127,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int last_blk = (kend - 1) >> tshift;
   const int64_t blk_elems = 2 * static_cast<int64_t>(a.T) * kv_row;   // one block: K and V of T slots
   uint16_t* vt = vtile[wave];
+  uint16_t* kt = ktile[wave];
 
   // Block IDs of a tile: tiles are 32-aligned and T is a power of two >= 16, so a tile
   // lies in one block (T >= 32) or covers two (T = 16).  Read two tiles ahead.
@@ -139,17 +149,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       return static_cast<int64_t>(id) * blk_elems + static_cast<int64_t>(key & tmask) * kv_row +
              static_cast<int64_t>(g) * kD;
     };
+    if constexpr (KV == F_BF16) {                              // 16 lanes per 256-byte row
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(tb + kb * 16 + li, kend - 1);        // clamp: never read unwritten slots
-      if constexpr (KV == F_BF16) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pool) + base_of(key) + lg * 32);
+      for (int it = 0; it < 8; ++it) {
+        const int key = min(tb + it * 4 + lg, kend - 1);        // clamp: never read unwritten slots
+        R.k[it] = load_kv(static_cast<const uint16_t*>(a.pool) + base_of(key) + li * 8);
+      }
+    } else {                                                   // 8 lanes per 128-byte row
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) R.k[kb][ks] = load_kv(p + ks);
-      } else {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.pool) + base_of(key) + lg * 32);
-        R.k[kb][0] = load_kv(p);
-        R.k[kb][1] = load_kv(p + 1);
+      for (int it = 0; it < 4; ++it) {
+        const int key = min(tb + it * 8 + lane / 8, kend - 1);
+        R.k[it] = load_kv(static_cast<const uint8_t*>(a.pool) + base_of(key) + (lane % 8) * 16);
       }
     }
     const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
@@ -170,19 +180,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Online-softmax update and O += P V for tile `tile` held in `R`.
   auto compute = [&](int tile, const TileRegs<KV>& R) {
     const int tb = k0 + tile * kTile;
-    bf16x8 kf[2][4];
+    // K and V rows into this wave's LDS tiles (bf16; an fp8 cache is dequantised here)
+    wave_lds_fence();
+    if constexpr (KV == F_BF16) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (KV == F_BF16) {
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + lg;
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, li) * 8) = R.k[it];
+        *reinterpret_cast<uint4*>(vt + row * kVStride + li * 8) = R.v[it];
+      }
+    } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = as_bf16x8(R.k[kb][ks]);
-      } else {
-        kf[kb][0] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][0].x, R.k[kb][0].y)));
-        kf[kb][1] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][0].z, R.k[kb][0].w)));
-        kf[kb][2] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][1].x, R.k[kb][1].y)));
-        kf[kb][3] = as_bf16x8(e4m3x8_to_bf16x8(make_uint2(R.k[kb][1].z, R.k[kb][1].w)));
+      for (int it = 0; it < 4; ++it) {
+        const int row = it * 8 + lane / 8, c0 = (lane % 8) * 2;
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) = e4m3x8_to_bf16x8(make_uint2(R.k[it].x, R.k[it].y));
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) =
+            e4m3x8_to_bf16x8(make_uint2(R.k[it].z, R.k[it].w));
+        uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
+        *reinterpret_cast<uint4*>(d) = e4m3x8_to_bf16x8(make_uint2(R.v[it].x, R.v[it].y));
+        *reinterpret_cast<uint4*>(d + 8) = e4m3x8_to_bf16x8(make_uint2(R.v[it].z, R.v[it].w));
       }
     }
+    wave_lds_fence();
+    // A operand K: lane (li, lg) of step ks holds key kb*16 + li, dims ks*32 + lg*8 .. +7
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int row = kb * 16 + li;
+        kf[kb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + row * kD + kpos(row, ks * 4 + lg) * 8));
+      }
     // scores S^T[key][head]: lane holds head li, keys tb + kb*16 + lg*4 + i
     f32x4 sacc[2];
 #pragma unroll
@@ -230,21 +258,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     pu.z = f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16);
     pu.w = f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16);
     const bf16x8 pa = as_bf16x8(pu);
-    // V tile into this wave's LDS region (row-major [key][dim], bf16)
-    wave_lds_fence();
-    if constexpr (KV == F_BF16) {
-#pragma unroll
-      for (int it = 0; it < 8; ++it)
-        *reinterpret_cast<uint4*>(vt + (it * 4 + lg) * kVStride + li * 8) = R.v[it];
-    } else {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        uint16_t* d = vt + (it * 8 + lane / 8) * kVStride + (lane % 8) * 16;
-        *reinterpret_cast<uint4*>(d) = e4m3x8_to_bf16x8(make_uint2(R.v[it].x, R.v[it].y));
-        *reinterpret_cast<uint4*>(d + 8) = e4m3x8_to_bf16x8(make_uint2(R.v[it].z, R.v[it].w));
-      }
-    }
-    wave_lds_fence();
     // O += P V: B operand = V[keys][dims nb*16 .. +15] read transposed
     const int krow = lg * 4 + li / 4;
 #pragma unroll
