@@ -56,13 +56,13 @@ __device__ __forceinline__ uint4 load_kv(const void* p) {
 // 16 rows one MFMA operand read touches at one chunk fall on 16 distinct bank groups.
 __device__ __forceinline__ int kpos(int r, int c) { return c ^ (r & 15); }
 
-// 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly (every e4m3 value is a bf16 value):
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes per instruction.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
-  const float2 a = e4m3x2_to_f32(c.x), b = e4m3x2_hi_to_f32(c.x);
-  const float2 d = e4m3x2_to_f32(c.y), e = e4m3x2_hi_to_f32(c.y);
-  auto hi = [](float x) { return __float_as_uint(x) >> 16; };  // exact: e4m3 fits bf16
-  return make_uint4(hi(a.x) | (hi(a.y) << 16), hi(b.x) | (hi(b.y) << 16), hi(d.x) | (hi(d.y) << 16),
-                    hi(e.x) | (hi(e.y) << 16));
+  auto lo = [](uint32_t w) { return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)); };
+  auto hi = [](uint32_t w) { return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)); };
+  return make_uint4(lo(c.x), hi(c.x), lo(c.y), hi(c.y));
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
