@@ -63,17 +63,37 @@ def describe(batch) -> str:
         parts.append(f"{int(gen.sum())} generation requests (cached {int(batch.past_lengths[gen].min())}.."
                      f"{int(batch.past_lengths[gen].max())}, sum S={int(batch.sequence_lengths[gen].sum())})")
     return (f"{sh.name}: " + " + ".join(parts) + f"; H={sh.num_heads} Hkv={sh.num_kv_heads} D={sh.head_dim} "
-            f"T={sh.tokens_per_block} io={sh.io_dtype} kv={sh.kv_dtype} rope_base={sh.rope_theta:g}")
+            f"T={sh.tokens_per_block} io={sh.io_dtype} kv={sh.kv_dtype} rope_base={sh.rope_theta:g}"
+            + (f" rope={sh.rope_style} rotary_dim={sh.rot_dim}" if sh.rope_style != "neox" or sh.rot_dim != sh.head_dim
+               else ""))
 
 
-def run_workload(k: int, steps: int, warmup: int) -> dict:
+def variant_batch(name: str):
+    """Batches of the variant measurements: a workload at full size with one change."""
+    import dataclasses
+
+    from workloads import synth as W
+    if name == "gptj3":          # workload 3 with RoPE on interleaved pairs over the whole head
+        sh = dataclasses.replace(W.SHAPES[3], rope_style="gptj")
+        return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-gptj")
+    if name == "gptj3-half":     # interleaved pairs on the first half of each head (R = D/2)
+        sh = dataclasses.replace(W.SHAPES[3], rope_style="gptj", rotary_dim=64)
+        return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-gptj-half")
+    raise KeyError(name)
+
+
+VARIANTS = ("gptj3", "gptj3-half")
+
+
+def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:
     import torch
 
     from paged_kv_gqa_rope_amd import _lib as L
     from paged_kv_gqa_rope_amd.harness import PagedStep
     from workloads import synth as W
 
-    batch = W.workload(k)
+    if batch is None:
+        batch = W.workload(k)
     t0 = time.time()
     st = PagedStep(batch, sentinel=False)
     torch.cuda.synchronize()
@@ -197,6 +217,8 @@ def main() -> int:
     ap.add_argument("--workloads", default="2,3,4,5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--variants", default=",".join(VARIANTS),
+                    help="comma-separated variant measurements (empty for none): " + ", ".join(VARIANTS))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -250,6 +272,20 @@ def main() -> int:
         o["roofline"] = roofline_for(r, k)
         others[f"workload_{k}"] = o
     line["workloads"] = others
+    variants = {}
+    for name in [x for x in args.variants.split(",") if x]:
+        print(f"[bench] variant {name} ...", file=sys.stderr, flush=True)
+        r = run_workload(0, args.steps, args.warmup, batch=variant_batch(name))
+        print(f"[bench] variant {name}: {r['ms_per_step']:.3f} ms/step "
+              f"{ {n: round(v['avg_us'], 1) for n, v in r['kernels'].items()} }", file=sys.stderr, flush=True)
+        o = dict(workload=r["workload"], ms_per_step=r["ms_per_step"], tok_per_s=r["tok_per_s"],
+                 kernels_us={n: round(v["avg_us"], 2) for n, v in r["kernels"].items()})
+        for f in ("decode_GBps", "prefill_TFLOPs", "append_GBps", "prefill_kernel"):
+            if f in r:
+                o[f] = r[f]
+        variants[name] = o
+    if variants:
+        line["variants"] = variants
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline()

@@ -69,7 +69,7 @@ enum { PKV_FP32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* OCP E4M3: bias 7, max 448
 /* host_request_types values ([REPORT] 1.1: context vs generation phase) */
 enum { PKV_REQ_CONTEXT = 0, PKV_REQ_GENERATION = 1 };
 /* rotary embedding styles ([REPORT] 1.1 names GPT-NeoX among the RoPE variants) */
-enum { PKV_ROPE_NONE = 0, PKV_ROPE_NEOX = 1 };
+enum { PKV_ROPE_NONE = 0, PKV_ROPE_NEOX = 1, PKV_ROPE_GPTJ = 2 };
 
 /*
  * Per-layer attention description ([REPORT] 1.1 attention parameters; [TEARDOWN]
@@ -84,7 +84,11 @@ enum { PKV_ROPE_NONE = 0, PKV_ROPE_NEOX = 1 };
  *                             each q and new k head by angle pos * theta_j, where R =
  *                             rotary_dim (0 means head_dim; otherwise a multiple of 16,
  *                             <= head_dim) and the table gives cos/sin; dims >= R are
- *                             copied.  PKV_ROPE_NONE stores k as given.
+ *                             copied.  PKV_ROPE_GPTJ rotates the interleaved pairs
+ *                             (2j, 2j + 1), j < R/2, by the same angles (same table);
+ *                             the source analysis report, 1.1, lists the RoPE variants
+ *                             (GPT-NeoX, ChatGLM, CogVLM) that differ in this pairing
+ *                             and in R.  PKV_ROPE_NONE stores k as given.
  *   softmax_scale           : <= 0 means 1/sqrt(head_dim).
  *   k_scale_quant_orig,
  *   v_scale_quant_orig      : fp8 cache only: real value = scale * stored e4m3 value.

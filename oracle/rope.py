@@ -1,4 +1,5 @@
-"""Rotary position embedding, GPT-NeoX ("rotate half") form.  TEST INFRASTRUCTURE.
+"""Rotary position embedding: GPT-NeoX ("rotate half") and interleaved-pair forms.
+TEST INFRASTRUCTURE.
 
 "TensorRT-LLM source analysis report", section 1.1, lists rotary_embedding
 among the attention parameters and names GPT-NeoX among the RoPE variants; it
@@ -14,6 +15,12 @@ Readings taken (no page states them):
   each output as two fp64 products and one fp64 add/subtract (numpy evaluates
   them as separate IEEE operations, no fused multiply-add);
 * applied to every query head and every new key head; values are not rotated.
+
+The same section lists further RoPE variants by name (ChatGLM, CogVLM) without a
+formula.  The plainest layout they differ by is the pairing: the interleaved form
+rotates (x_{2j}, x_{2j+1}) by the same angle m * theta_j (the GPT-J layout; applied to
+a leading part of the head, R < D, it is the layout of the ChatGLM models).  Same
+tables, same fp64 arithmetic.
 """
 from __future__ import annotations
 
@@ -44,3 +51,26 @@ def rope_neox(x: np.ndarray, positions: np.ndarray, cos_t: np.ndarray, sin_t: np
     y[..., :half] = x1 * c - x2 * s
     y[..., half:rot_dim] = x2 * c + x1 * s
     return y
+
+
+def rope_gptj(x: np.ndarray, positions: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray,
+              rot_dim: int) -> np.ndarray:
+    """Interleaved pairs: rotate (x_{2j}, x_{2j+1}) by m * theta_j, j < rot_dim/2."""
+    x = np.asarray(x, dtype=np.float64)
+    c = cos_t[positions][:, None, :]
+    s = sin_t[positions][:, None, :]
+    x1 = x[..., 0:rot_dim:2]
+    x2 = x[..., 1:rot_dim:2]
+    y = x.copy()
+    y[..., 0:rot_dim:2] = x1 * c - x2 * s
+    y[..., 1:rot_dim:2] = x2 * c + x1 * s
+    return y
+
+
+def rope_apply(style: str, x, positions, cos_t, sin_t, rot_dim: int):
+    """style 'neox' (pairs j, j + R/2) or 'gptj' (pairs 2j, 2j + 1)."""
+    if style == "neox":
+        return rope_neox(x, positions, cos_t, sin_t, rot_dim)
+    if style == "gptj":
+        return rope_gptj(x, positions, cos_t, sin_t, rot_dim)
+    raise ValueError(f"unknown RoPE style {style!r}")

@@ -32,7 +32,7 @@ import numpy as np
 
 from . import codecs
 from .attention import attend
-from .rope import neox_tables, rope_neox
+from .rope import neox_tables, rope_apply
 
 
 def io_decode(batch, bits) -> np.ndarray:
@@ -62,8 +62,8 @@ def append_request(batch, r: int, tabs, rope: bool = True):
     if rope:
         cos_t, sin_t = tabs
         q = io_decode(batch, batch.new_q(r))
-        q_out = codecs.encode(rope_neox(q, pos, cos_t, sin_t, sh.rot_dim), sh.io_dtype)
-        k = rope_neox(k, pos, cos_t, sin_t, sh.rot_dim)
+        q_out = codecs.encode(rope_apply(sh.rope_style, q, pos, cos_t, sin_t, sh.rot_dim), sh.io_dtype)
+        k = rope_apply(sh.rope_style, k, pos, cos_t, sin_t, sh.rot_dim)
     k_store = codecs.encode(k, sh.kv_dtype, sh.k_scale)
     v_store = codecs.encode(v, sh.kv_dtype, sh.v_scale)
     return q_out, k_store, v_store

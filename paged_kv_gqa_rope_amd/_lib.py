@@ -25,7 +25,7 @@ PKV_ERR_HIP = -8
 
 PKV_FP32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_REQ_CONTEXT, PKV_REQ_GENERATION = 0, 1
-PKV_ROPE_NONE, PKV_ROPE_NEOX = 0, 1
+PKV_ROPE_NONE, PKV_ROPE_NEOX, PKV_ROPE_GPTJ = 0, 1, 2
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 

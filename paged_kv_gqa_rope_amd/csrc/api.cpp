@@ -142,7 +142,7 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, 
   if ((rc = check_rows(k, kv_row_stride, static_cast<int64_t>(Hkv) * D, desc->io_dtype, "k")) != PKV_OK) return rc;
   if ((rc = check_rows(v, kv_row_stride, static_cast<int64_t>(Hkv) * D, desc->io_dtype, "v")) != PKV_OK) return rc;
   if (!aligned16(kv_pool)) return set_err(PKV_ERR_INVALID_ARG, "kv_pool must be 16-byte aligned");
-  if (desc->rope_style == PKV_ROPE_NEOX) {
+  if (desc->rope_style != PKV_ROPE_NONE) {
     if (!rope_cos_sin) return set_err(PKV_ERR_INVALID_ARG, "rope_cos_sin is NULL");
     if (!aligned16(rope_cos_sin)) return set_err(PKV_ERR_INVALID_ARG, "rope_cos_sin must be 16-byte aligned");
     if (rope_max_pos < plan.max_S)
@@ -176,7 +176,8 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, 
   a.inv_v_scale = fp8 ? 1.0 / static_cast<double>(desc->v_scale_quant_orig) : 1.0;
   a.io_fmt = fmt_of(desc->io_dtype);
   a.kv_fmt = fmt_of(desc->kv_dtype);
-  a.rope = desc->rope_style == PKV_ROPE_NEOX;
+  a.rope = desc->rope_style == PKV_ROPE_NEOX ? pkv::kRopeNeox
+           : desc->rope_style == PKV_ROPE_GPTJ ? pkv::kRopeGptj : pkv::kRopeNone;
   a.max_n = plan.max_n;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed("append_rope", s, [&] { return pkv::launch_append(a, s); });

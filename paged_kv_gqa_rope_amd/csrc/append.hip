@@ -12,6 +12,8 @@
 // load and store is a 16-byte access and neighbouring lanes touch neighbouring bytes.
 // Arithmetic is fp64 with contraction off and one rounding per stored element, so the
 // stored bits depend only on the inputs and the table.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -128,14 +130,18 @@ constexpr int kHeadsPerRotTask = 4;
 // group of 8 pairs for up to kHeadsPerRotTask q/k heads, so the table slice is read
 // once for all of them), pass-through groups of 8 dims past the rotary part, and
 // groups of 8 v dims.  A task's loads are all issued before its arithmetic.
-template <int IO, int KV, bool ROPE>
+template <int IO, int KV, int RS>
 __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot& tk, int t, int Hq,
                                             const void* __restrict__ q, const void* __restrict__ k,
                                             const void* __restrict__ v, const double* __restrict__ cs_base,
                                             void* __restrict__ q_out, void* __restrict__ pool) {
-  const int R = ROPE ? a.R : 0;
+  const int R = RS != kRopeNone ? a.R : 0;
   const int half = R / 2;
   const int rg = R / 16, pg = (a.D - R) / 8, vg = a.D / 8;
+  // element offsets of a task's 8 pairs: rotate-half -> first elements at j0, partners
+  // at j0 + R/2; interleaved -> 16 consecutive elements from 2*j0 (pairs (2j, 2j+1))
+  auto off_a = [&](int j0) { return RS == kRopeGptj ? 2 * j0 : j0; };
+  auto off_b = [&](int j0) { return RS == kRopeGptj ? 2 * j0 + 8 : j0 + half; };
   const int qk = Hq + a.Hkv;
   const int nhc = (qk + kHeadsPerRotTask - 1) / kHeadsPerRotTask;
   auto pool_off = [&](int which, int g) {
@@ -160,8 +166,8 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
         const void* src;
         int64_t off;
         head_src(h0 + u, src, off);
-        r1[u] = load_raw8<IO>(src, off + j0);
-        r2[u] = load_raw8<IO>(src, off + j0 + half);
+        r1[u] = load_raw8<IO>(src, off + off_a(j0));
+        r2[u] = load_raw8<IO>(src, off + off_b(j0));
       }
     }
     const double2* cs = reinterpret_cast<const double2*>(cs_base) + static_cast<int64_t>(tk.m) * half + j0;
@@ -173,17 +179,46 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
       if (u >= nh) break;
       const int head = h0 + u;
       double x1[8], x2[8], y1[8], y2[8];
-      widen8<IO>(r1[u], x1);
-      widen8<IO>(r2[u], x2);
+      if constexpr (RS == kRopeGptj) {                    // de-interleave the 16 elements
+        double e0[8], e1[8];
+        widen8<IO>(r1[u], e0);
+        widen8<IO>(r2[u], e1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x1[i] = e0[2 * i];
+          x2[i] = e0[2 * i + 1];
+          x1[i + 4] = e1[2 * i];
+          x2[i + 4] = e1[2 * i + 1];
+        }
+      } else {
+        widen8<IO>(r1[u], x1);
+        widen8<IO>(r2[u], x2);
+      }
       rotate8(x1, x2, c, y1, y2);
+      double s1[8], s2[8];                                // the two stored groups of 8
+      if constexpr (RS == kRopeGptj) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s1[2 * i] = y1[i];
+          s1[2 * i + 1] = y2[i];
+          s2[2 * i] = y1[i + 4];
+          s2[2 * i + 1] = y2[i + 4];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          s1[i] = y1[i];
+          s2[i] = y2[i];
+        }
+      }
       if (head < Hq) {
         const int64_t o = tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D;
-        store8<IO>(q_out, o + j0, y1, 1.0);
-        store8<IO>(q_out, o + j0 + half, y2, 1.0);
+        store8<IO>(q_out, o + off_a(j0), s1, 1.0);
+        store8<IO>(q_out, o + off_b(j0), s2, 1.0);
       } else if (tk.blk >= 0) {
         const int64_t o = pool_off(0, head - Hq);
-        store8<KV>(pool, o + j0, y1, a.inv_k_scale);
-        store8<KV>(pool, o + j0 + half, y2, a.inv_k_scale);
+        store8<KV>(pool, o + off_a(j0), s1, a.inv_k_scale);
+        store8<KV>(pool, o + off_b(j0), s2, a.inv_k_scale);
       }
     }
   } else if (t < nhc * rg + qk * pg) {                      // dimensions past the rotary part
@@ -223,7 +258,7 @@ __device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row,
 // and each workgroup finds the rows' requests through an LDS prefix scan of the
 // context lengths (batches of at most kFlatMaxRequests requests).  Otherwise the grid
 // is (row tile, request), for any batch size.
-template <int IO, int KV, bool ROPE, bool FLAT>
+template <int IO, int KV, int RS, bool FLAT>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, int tokens_per_wg) {
   __shared__ int32_t s_cu[kFlatMaxRequests + 1];
   __shared__ TokenSlot s_tok[kMaxTokensPerWg];
@@ -278,7 +313,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
       s_tok[threadIdx.x] = make_slot(a, rowr + tok0 + threadIdx.x, r, tok0 + threadIdx.x);
   }
   __syncthreads();
-  const int R = ROPE ? a.R : 0;
+  const int R = RS != kRopeNone ? a.R : 0;
   const int per_tok = ((Hq + a.Hkv + kHeadsPerRotTask - 1) / kHeadsPerRotTask) * (R / 16) +
                       (Hq + a.Hkv) * ((a.D - R) / 8) + a.Hkv * (a.D / 8);
   const int total = ntok * per_tok;
@@ -292,7 +327,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
     const int it = task / per_tok;
     const TokenSlot tk = s_tok[it];
     if (tk.row >= a.N || tk.m < 0) continue;
-    append_task<IO, KV, ROPE>(a, tk, task - it * per_tok, Hq, q, k, v, cs, q_out, pool);
+    append_task<IO, KV, RS>(a, tk, task - it * per_tok, Hq, q, k, v, cs, q_out, pool);
   }
 }
 
@@ -316,19 +351,19 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
   // enough workgroups to fill the chip: about N / 512 tokens each, at most 8
   int64_t want = a.N / 512;
   const int tpw = static_cast<int>(want < 1 ? 1 : want > kMaxTokensPerWg ? kMaxTokensPerWg : want);
-  if (a.B <= kFlatMaxRequests) {
-    const dim3 grid(static_cast<unsigned>((a.N + tpw - 1) / tpw));
-    if (a.rope)
-      hipLaunchKernelGGL((append_kernel<IO, KV, true, true>), grid, dim3(kAppendThreads), 0, s, a, tpw);
-    else
-      hipLaunchKernelGGL((append_kernel<IO, KV, false, true>), grid, dim3(kAppendThreads), 0, s, a, tpw);
-  } else {
-    const dim3 grid((a.max_n + tpw - 1) / tpw, a.B);
-    if (a.rope)
-      hipLaunchKernelGGL((append_kernel<IO, KV, true, false>), grid, dim3(kAppendThreads), 0, s, a, tpw);
-    else
-      hipLaunchKernelGGL((append_kernel<IO, KV, false, false>), grid, dim3(kAppendThreads), 0, s, a, tpw);
-  }
+  auto go = [&](auto rs) {
+    constexpr int RS = decltype(rs)::value;
+    if (a.B <= kFlatMaxRequests) {
+      const dim3 grid(static_cast<unsigned>((a.N + tpw - 1) / tpw));
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+    } else {
+      const dim3 grid((a.max_n + tpw - 1) / tpw, a.B);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+    }
+  };
+  if (a.rope == kRopeNeox) go(std::integral_constant<int, kRopeNeox>());
+  else if (a.rope == kRopeGptj) go(std::integral_constant<int, kRopeGptj>());
+  else go(std::integral_constant<int, kRopeNone>());
   return hipGetLastError();
 }
 

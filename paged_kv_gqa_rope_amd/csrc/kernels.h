@@ -8,6 +8,8 @@ namespace pkv {
 
 // element formats of io tensors and the KV pool
 enum : int { F_FP32 = 0, F_BF16 = 1, F_FP8 = 2 };
+// rotary pairing of the append: none, (j, j + R/2), (2j, 2j + 1)
+enum : int { kRopeNone = 0, kRopeNeox = 1, kRopeGptj = 2 };
 
 struct AppendArgs {
   const void* q;            // may be null (then q_out is null)
@@ -24,7 +26,7 @@ struct AppendArgs {
   int32_t B, N, H, Hkv, D, T, R, mbps;
   int64_t num_blocks;
   double inv_k_scale, inv_v_scale;   // fp8 cache: 1/scale; otherwise 1
-  int32_t io_fmt, kv_fmt, rope;
+  int32_t io_fmt, kv_fmt, rope;   // rope: kRopeNone / kRopeNeox / kRopeGptj
   int32_t max_n;            // largest n_r (grid extent)
 };
 

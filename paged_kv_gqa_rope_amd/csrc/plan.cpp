@@ -40,8 +40,8 @@ int validate_desc(const pkv_attn_desc* d, std::string& err) {
     return fail(err, PKV_ERR_UNSUPPORTED, "io_dtype=%lld (supported: FP32, BF16)", d->io_dtype);
   if (d->kv_dtype != PKV_FP32 && d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3)
     return fail(err, PKV_ERR_UNSUPPORTED, "kv_dtype=%lld (supported: FP32, BF16, FP8_E4M3)", d->kv_dtype);
-  if (d->rope_style != PKV_ROPE_NONE && d->rope_style != PKV_ROPE_NEOX)
-    return fail(err, PKV_ERR_UNSUPPORTED, "rope_style=%lld (supported: NONE, NEOX)", d->rope_style);
+  if (d->rope_style != PKV_ROPE_NONE && d->rope_style != PKV_ROPE_NEOX && d->rope_style != PKV_ROPE_GPTJ)
+    return fail(err, PKV_ERR_UNSUPPORTED, "rope_style=%lld (supported: NONE, NEOX, GPTJ)", d->rope_style);
   if (d->rotary_dim < 0 || d->rotary_dim > d->head_dim)
     return fail(err, PKV_ERR_INVALID_ARG, "rotary_dim=%lld outside [0, head_dim=%lld]", d->rotary_dim, d->head_dim);
   if (d->rotary_dim % 16)

@@ -35,7 +35,8 @@ def make_desc(shape, rope: bool = True, max_num_tokens: int | None = None) -> L.
     d.tokens_per_block = shape.tokens_per_block
     d.io_dtype = DTYPE_CODE[shape.io_dtype]
     d.kv_dtype = DTYPE_CODE[shape.kv_dtype]
-    d.rope_style = L.PKV_ROPE_NEOX if rope else L.PKV_ROPE_NONE
+    style = {"neox": L.PKV_ROPE_NEOX, "gptj": L.PKV_ROPE_GPTJ}[getattr(shape, "rope_style", "neox")]
+    d.rope_style = style if rope else L.PKV_ROPE_NONE
     d.rotary_dim = shape.rotary_dim
     d.softmax_scale = 0.0
     d.k_scale_quant_orig = shape.k_scale

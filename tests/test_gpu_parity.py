@@ -1,5 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, at sizes the
 oracle finishes in seconds (several blocks, ragged tails, every workload shape)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -72,6 +74,21 @@ def test_small_workload_attention_matches_oracle(H, k):
     ref = O.run(b)
     stats = compare_attention(st.out_host(), ref["out"], b.shape, b.label)
     print(b.label, stats)
+
+
+@pytest.mark.parametrize("k,rot", [(1, 0), (1, 32), (3, 0), (3, 64), (4, 64), (5, 128)])
+def test_interleaved_rope_append_and_attention(H, k, rot):
+    """RoPE on interleaved pairs (2j, 2j+1), whole head or a leading part of it."""
+    sh = dataclasses.replace(W.SHAPES[k], rope_style="gptj", rotary_dim=rot)
+    b = W.small_workload(k, shape=sh)
+    case("gptj rope", b.label, sh.name, "rotary_dim", rot)
+    st = run_step(H, b)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(sh.kv_dtype)), "pool")
+    stats = compare_attention(st.out_host(), O.run(b)["out"], sh, b.label)
+    print(b.label, "gptj", rot, stats)
 
 
 def test_full_tiny_workload(H):

@@ -97,6 +97,58 @@ def test_rope_frequency_ladder():
         assert math.isclose(math.atan2(y[0, 0, rot // 2], y[0, 0, 0]), 1.0, rel_tol=1e-15)
 
 
+@pytest.mark.parametrize("rot,D", [(128, 128), (64, 128), (32, 64)])
+def test_rope_gptj_is_complex_multiplication_on_interleaved_pairs(rot, D):
+    rng = np.random.default_rng(20)
+    base = 1e4
+    x = rand_unit(rng, (30, 2, D))
+    pos = rng.integers(0, 9000, 30)
+    cos_t, sin_t = R.neox_tables(base, rot, 9000)
+    y = R.rope_gptj(x, pos, cos_t, sin_t, rot)
+    z = x[..., 0:rot:2] + 1j * x[..., 1:rot:2]
+    ang = pos[:, None].astype(np.float64) * R.neox_inv_freq(base, rot)[None, :]
+    w = z * np.exp(1j * ang)[:, None, :]
+    assert np.allclose(y[..., 0:rot:2], w.real, rtol=0, atol=1e-12)
+    assert np.allclose(y[..., 1:rot:2], w.imag, rtol=0, atol=1e-12)
+    assert np.array_equal(y[..., rot:], x[..., rot:])         # dims past the rotary part pass through
+    assert np.array_equal(R.rope_gptj(x, np.zeros(30, int), cos_t, sin_t, rot), x)
+
+
+def test_rope_gptj_pairs_are_2j_and_2j_plus_1():
+    rot = 64
+    cos_t, sin_t = R.neox_tables(1e4, rot, 10)
+    for j in (0, 1, 6, 31, 32, 63):
+        x = np.zeros((1, 1, rot)); x[0, 0, j] = 1.0
+        y = R.rope_gptj(x, np.array([7]), cos_t, sin_t, rot)
+        nz = set(np.nonzero(np.abs(y[0, 0]) > 1e-15)[0].tolist())
+        assert nz <= {j, j ^ 1} and j in nz
+
+
+def test_rope_gptj_is_neox_on_deinterleaved_dims():
+    # reordering the rotary dims (evens first, then odds) turns interleaved pairs into
+    # rotate-half pairs: the two layouts are one rotation seen through a permutation
+    rng = np.random.default_rng(21)
+    rot, D = 64, 128
+    perm = np.concatenate([np.arange(0, rot, 2), np.arange(1, rot, 2), np.arange(rot, D)])
+    x = rand_unit(rng, (25, 3, D))
+    pos = rng.integers(0, 3000, 25)
+    cos_t, sin_t = R.neox_tables(5e5, rot, 3000)
+    a = R.rope_gptj(x, pos, cos_t, sin_t, rot)[..., perm]
+    b = R.rope_neox(x[..., perm], pos, cos_t, sin_t, rot)
+    assert np.array_equal(a, b)
+
+
+def test_rope_gptj_relative_position():
+    rng = np.random.default_rng(22)
+    rot = 128
+    cos_t, sin_t = R.neox_tables(1e4, rot, 4000)
+    q = rand_unit(rng, (1, 1, rot)); k = rand_unit(rng, (1, 1, rot))
+    for (m, n, c) in [(10, 3, 100), (0, 500, 7), (1500, 1499, 2000)]:
+        a = np.sum(R.rope_gptj(q, np.array([m]), cos_t, sin_t, rot) * R.rope_gptj(k, np.array([n]), cos_t, sin_t, rot))
+        b = np.sum(R.rope_gptj(q, np.array([m + c]), cos_t, sin_t, rot) * R.rope_gptj(k, np.array([n + c]), cos_t, sin_t, rot))
+        assert abs(a - b) < 1e-9
+
+
 # ------------------------------------------------------------------ softmax / attention
 def test_softmax_printed_temperature_example():
     rows = [l.split() for l in open(os.path.join(HERE, "golden", "softmax_temperature.txt"))

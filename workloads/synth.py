@@ -51,6 +51,7 @@ class Shape:
     kv_dtype: str
     rope_theta: float
     rotary_dim: int = 0          # 0 means head_dim
+    rope_style: str = "neox"     # "neox": pairs (j, j + R/2); "gptj": pairs (2j, 2j + 1)
     k_scale: float = 1.0         # fp8 cache only: real value = scale * stored value
     v_scale: float = 1.0
     max_num_tokens: int = 8192
@@ -201,11 +202,12 @@ def workload(k: int) -> Batch:
     raise KeyError(k)
 
 
-def small_workload(k: int) -> Batch:
+def small_workload(k: int, shape: Shape | None = None) -> Batch:
     """Workload k at a size the oracle finishes in seconds: same heads,
-    head_dim, block size and dtypes; several blocks and a ragged tail."""
+    head_dim, block size and dtypes; several blocks and a ragged tail.  ``shape``
+    replaces workload k's shape (same lengths and seeds)."""
     seed = 2000 + k
-    sh = SHAPES[k]
+    sh = SHAPES[k] if shape is None else shape
     if k == 1:
         return make_batch(sh, ctx=[(37, 0)], gen_past=[50], seed=seed, pool_blocks_min=16, label="s1")
     if k == 2:
