@@ -41,7 +41,7 @@ def algorithmic(batch) -> dict:
     S = batch.sequence_lengths.astype(np.int64)
     n = batch.context_lengths.astype(np.int64)
     p = S - n
-    decode_bytes = int(np.sum(S[gen] * Hkv * D * 2 * bkv + H * D * 2 * bio + 4 * ((S[gen] + T - 1) // T)))
+    decode_bytes = int(np.sum(S[gen] * Hkv * D * 2 * bkv + n[gen] * H * D * 2 * bio + 4 * ((S[gen] + T - 1) // T)))
     ctx = ~gen
     ctx_flops = int(4 * D * H * np.sum(n[ctx] * p[ctx] + n[ctx] * (n[ctx] + 1) // 2))
     N = int(n.sum())
@@ -79,10 +79,14 @@ def variant_batch(name: str):
     if name == "gptj3-half":     # interleaved pairs on the first half of each head (R = D/2)
         sh = dataclasses.replace(W.SHAPES[3], rope_style="gptj", rotary_dim=64)
         return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-gptj-half")
+    if name == "spec4-gqa8":     # workload 4's 128 generation requests, each with 1 + 3 draft tokens
+        sh = dataclasses.replace(W.SHAPES[4])
+        past = W._uniform_pasts(1004, 128, 256, 4096)
+        return W.make_batch(sh, gen_past=past, gen_new=[4] * 128, seed=1004, label="w4-spec4")
     raise KeyError(name)
 
 
-VARIANTS = ("gptj3", "gptj3-half")
+VARIANTS = ("gptj3", "gptj3-half", "spec4-gqa8")
 
 
 def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:

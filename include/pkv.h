@@ -2,12 +2,12 @@
  * pkv.h -- C ABI of the paged-KV GQA + RoPE attention library for AMD MI355X (gfx950).
  *
  * One step of one attention layer over an in-flight batch:
- *   1. pkv_append_rope: rotate the new tokens' q and k (GPT-NeoX RoPE), write the
+ *   1. pkv_append_rope: rotate the new tokens' q and k (RoPE), write the
  *      rotated q to q_out and scatter the rotated k and the raw v into the paged
  *      KV pool through the per-request block table;
- *   2. pkv_attention_forward: causal attention for context-phase rows and
- *      one-token attention for generation-phase rows, reading K/V through the
- *      block table.
+ *   2. pkv_attention_forward: causal attention for context-phase rows and for
+ *      generation-phase rows (one token, or a token and its draft tokens), reading
+ *      K/V through the block table.
  *
  * Sources (secondary descriptions of TensorRT-LLM; cited by page title and section):
  *   [REPORT]   "TensorRT-LLM source analysis report" (adg.csdn.net):
@@ -121,8 +121,12 @@ typedef struct pkv_attn_desc {
  *   max_context_length      : >= every context request's host_context_lengths entry.
  *   host_request_types      : host [B], PKV_REQ_CONTEXT or PKV_REQ_GENERATION.
  *   host_context_lengths    : host [B], n_r = tokens request r brings to this step
- *                             (a prompt or chunk length for a context request, exactly 1
- *                             for a generation request).
+ *                             (a prompt or chunk length for a context request; for a
+ *                             generation request 1, or 1 + k draft tokens to verify, at
+ *                             most 64 -- the generation lengths of [REPORT] 1.4; token i
+ *                             of the request sits at position S_r - n_r + i, i.e. the
+ *                             position offsets are 0 .. n_r - 1 and the drafts form one
+ *                             chain, causal among themselves).
  *   host_sequence_lengths   : host [B], S_r = cached tokens before the step + n_r.  The
  *                             new tokens occupy cache positions S_r - n_r .. S_r - 1.
  *   context_lengths,
@@ -204,8 +208,9 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch,
  * Attention over the paged cache ([NOTES] 六.6.1-6.3; [TEARDOWN] AttentionBackend.forward).
  * For request r, new row i at position m = S_r - n_r + i and query head h, with
  * g = h / (H/Hkv):  out[row][h] = sum_{t <= m} softmax_t(scale * <q[row][h], K_g[t]>) V_g[t].
- * Context rows are therefore causal over the cached prefix plus the chunk; a generation
- * row attends to all S_r cached positions, its own appended token included.
+ * Context rows are therefore causal over the cached prefix plus the chunk; a one-token
+ * generation row attends to all S_r cached positions, its own appended token included,
+ * and the draft tokens of a generation request are causal among themselves.
  *   q        : device, N rows of H*D io elements (normally q_out of the append), row
  *              stride q_row_stride elements, 16-byte aligned rows.
  *   kv_pool  : device pool as above, already holding positions 0 .. S_r-1 of every request.

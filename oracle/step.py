@@ -2,11 +2,14 @@
 
 The step (from the pages' description of the problem):
 
-1. lengths -- request r brings n_r new tokens (1 for a generation request) on
-   top of p_r cached ones, S_r = p_r + n_r ("TensorRT-LLM source analysis
-   report", section 1.1 sequence_length / context_lengths; the teardown's
-   AttentionMetadata section); packed rows carry no padding and context
-   requests come before generation requests (report, section 1.3);
+1. lengths -- request r brings n_r new tokens on top of p_r cached ones,
+   S_r = p_r + n_r ("TensorRT-LLM source analysis report", section 1.1
+   sequence_length / context_lengths; the teardown's AttentionMetadata
+   section); packed rows carry no padding and context requests come before
+   generation requests (report, section 1.3).  A generation request brings 1
+   token, or 1 + k draft tokens to verify (report, section 1.4: generation
+   lengths and position offsets); read as one chain, token i at position
+   p_r + i, so the drafts are causal among themselves like a chunk;
 2. append -- rotate the new q and k at their absolute positions p_r + i
    (RoPE, see ``rope``), round q to the io format (q_out), store the rotated k
    and the raw v in the cache format (see ``codecs``) at cache positions

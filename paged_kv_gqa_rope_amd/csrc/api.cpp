@@ -248,7 +248,8 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
     a.req_begin = plan.num_ctx;
     a.req_end = plan.B;
     a.row_begin = plan.ctx_tokens;
-    a.max_n = 1;
+    a.max_n = plan.max_gen_n;
+    a.col_blocks = plan.col_blocks;
     if (plan.fast_decode) {
       a.chunk = plan.chunk;
       a.max_splits = plan.max_splits;

@@ -83,17 +83,25 @@ template <int KV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
   // KV head fastest: the workgroups of every head of one (request, chunk) run side by
   // side, so together they read each block's K and V rows as contiguous memory.
-  const int g = blockIdx.x, split = blockIdx.y, rg = blockIdx.z;
+  const int g = blockIdx.x % a.Hkv, cb = blockIdx.x / a.Hkv, split = blockIdx.y, rg = blockIdx.z;
   const int r = a.req_begin + rg;
   const int S = a.seq_len[r];
+  const int n = a.ctx_len[r];                                  // 1, or 1 + draft tokens
+  const int G = a.H / a.Hkv;
   const int k0 = split * a.chunk;
-  if (k0 >= S || split >= a.max_splits) return;               // uniform over the block
+  if (k0 >= S || split >= a.max_splits || cb * 16 >= G * n) return;   // uniform over the block
   const int kend = min(k0 + a.chunk, S);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
-  const int G = a.H / a.Hkv;
-  const int64_t row = static_cast<int64_t>(a.row_begin) + rg;
+  // Columns of the score tile: (token, query head) pairs, 16 per column block.  Lane
+  // column li is token tok = gc / G of the request (position S - n + tok; it sees keys up
+  // to that position: causal among a request's draft tokens) and head g*G + gc % G.
+  const int gc = cb * 16 + li, tok = gc / G;
+  const bool col_ok = tok < n;
+  const int key_lim = col_ok ? S - n + tok : -1;               // keys 0 .. key_lim
+  const int64_t row0 = a.max_n == 1 ? static_cast<int64_t>(a.row_begin) + rg : wave_prefix(a.ctx_len, r);
+  const int64_t row = row0 + min(tok, n - 1);
   const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
   // The block table is read-only here: reading it through the constant address space
   // keeps its (wave-uniform) reads on the scalar unit, out of the vector-load queue.
@@ -103,22 +111,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
 
-  // B operand Q^T: head n = li, dims ks*32 + lg*8 + j (the dim order inside a
+  // B operand Q^T: column li, dims ks*32 + lg*8 + j (the dim order inside a
   // contraction is free as long as K uses the same one).
   bf16x8 qf[4];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
-                         static_cast<int64_t>(g * G + min(li, G - 1)) * kD + lg * 8;
+                         static_cast<int64_t>(g * G + gc % G) * kD + lg * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 32);
-      if (li >= G) u = make_uint4(0, 0, 0, 0);
+      if (!col_ok) u = make_uint4(0, 0, 0, 0);
       qf[ks] = as_bf16x8(u);
     }
   }
   const float xscale = a.scale_log2 * a.k_scale;
-  float m_run = -INFINITY, l_run = 0.f;                         // for head li
-  f32x4 o[8];                                                   // O[head lg*4+i][dim nb*16+li]
+  float m_run = -INFINITY, l_run = 0.f;                         // for column li
+  f32x4 o[8];                                                   // O[column lg*4+i][dim nb*16+li]
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -227,31 +235,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = tb + kb * 16 + lg * 4 + i;
-        x[kb * 4 + i] = key < kend ? sacc[kb][i] * xscale : -INFINITY;
+        x[kb * 4 + i] = key < kend && key <= key_lim ? sacc[kb][i] * xscale : -INFINITY;
         tmax = fmaxf(tmax, x[kb * 4 + i]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);                    // finite: key tb is always valid
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, tmax);
+    // -inf while a draft column has seen no key of its causal range yet: exponents then
+    // take offset 0 (every term is exp2(-inf) = 0), never -inf - -inf
+    const float m_off = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_off);
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+      x[e] = __builtin_amdgcn_exp2f(x[e] - m_off);
       lsum += x[e];
     }
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
-    // rescale O rows: lane's O rows are heads lg*4+i; their alpha lives in lane lg*4+i
+    // rescale O rows: lane's O rows are columns lg*4+i; their alpha lives in lane lg*4+i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float ah = __shfl(alpha, lg * 4 + i, kWave);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ah;
     }
-    // P as the A operand: row = head li, k-slot j <-> key (j/4)*16 + lg*4 + j%4
+    // P as the A operand: row = column li, k-slot j <-> key (j/4)*16 + lg*4 + j%4
     uint4 pu;
     pu.x = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
     pu.y = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
@@ -304,19 +315,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     ml[wave][li][1] = l_run;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * kD; e += kThreads) {
-    const int h = e / kD, d = e % kD;
+  const int ncol = min(16, G * n - cb * 16);                     // valid columns of the block
+  for (int e = threadIdx.x; e < ncol * kD; e += kThreads) {
+    const int c = e / kD, d = e % kD;
+    const int cc = cb * 16 + c;                                 // (token cc / G, head g*G + cc % G)
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w][h][0]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w][c][0]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float s = ml[w][h][0] == -INFINITY ? 0.f : exp2f(ml[w][h][0] - M);
-      L += s * ml[w][h][1];
-      O += s * red[(w * 16 + h) * kD + d];
+      const float s = ml[w][c][0] == -INFINITY ? 0.f : exp2f(ml[w][c][0] - M);
+      L += s * ml[w][c][1];
+      O += s * red[(w * 16 + c) * kD + d];
     }
-    const int64_t part = (static_cast<int64_t>(rg) * a.H + g * G + h) * a.max_splits + split;
+    const int64_t tok_row = row0 - a.row_begin + cc / G;        // generation row of the token
+    const int64_t part = (tok_row * a.H + g * G + cc % G) * a.max_splits + split;
     a.ws_o[part * kD + d] = O;
     if (d == 0) {
       a.ws_ml[part * 2] = M;
@@ -325,27 +339,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-// One workgroup of kD threads per (generation request, query head).  Thread s < ns
+// One workgroup of kD threads per (generation token, query head).  Thread s < ns
 // first loads split s's (m, l); a fixed-shape tree gives M = max m and L = sum 2^(m-M) l;
 // then thread d sums 2^(m_s-M) o_s[d] over the splits in order, eight loads in flight.
+// Splits past a draft token's position hold m = -inf and weigh nothing; split 0 always
+// holds key 0, so M is finite.
 __global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
   static_assert(kD >= 128, "one thread per split needs kD >= kMaxSplits");
-  const int h = blockIdx.x, rg = blockIdx.y, t = threadIdx.x;
+  const int h = blockIdx.x, rg = blockIdx.y, tok = blockIdx.z, t = threadIdx.x;
   const int r = a.req_begin + rg;
+  if (tok >= a.ctx_len[r]) return;                                  // uniform
   const int S = a.seq_len[r];
   const int ns = min((S + a.chunk - 1) / a.chunk, a.max_splits);
-  const int64_t base = (static_cast<int64_t>(rg) * a.H + h) * a.max_splits;
+  const int64_t row = (a.max_n == 1 ? static_cast<int64_t>(a.row_begin) + rg : wave_prefix(a.ctx_len, r)) + tok;
+  const int64_t base = ((row - a.row_begin) * a.H + h) * a.max_splits;
   __shared__ float s_w[kD];
   __shared__ float s_red[kD / kWave];
   const float m_t = t < ns ? a.ws_ml[(base + t) * 2] : -INFINITY;
-  const float l_t = t < ns ? a.ws_ml[(base + t) * 2 + 1] : 0.f;
+  const float l_t = t < ns ? a.ws_ml[(base + t) * 2 + 1] : 0.f;   // 0 wherever m_t = -inf
   float M = wave_max(m_t);
   if (t % kWave == 0) s_red[t / kWave] = M;
   __syncthreads();
   M = s_red[0];
 #pragma unroll
   for (int w = 1; w < kD / kWave; ++w) M = fmaxf(M, s_red[w]);
-  const float w_t = t < ns ? exp2f(m_t - M) : 0.f;
+  const float w_t = t < ns && m_t != -INFINITY ? exp2f(m_t - M) : 0.f;
   s_w[t] = w_t;
   float L = wave_sum(w_t * l_t);
   __syncthreads();
@@ -365,15 +383,14 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
     for (int u = 0; u < 8; ++u) o += s_w[s + u] * v[u];
   }
   for (; s < ns; ++s) o += s_w[s] * op[static_cast<int64_t>(s) * kD];
-  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(a.row_begin) + rg) * a.H * kD +
-                  static_cast<int64_t>(h) * kD;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + row * a.H * kD + static_cast<int64_t>(h) * kD;
   out[t] = static_cast<uint16_t>(f32_to_bf16(o * (a.v_scale / L)));
 }
 
 }  // namespace
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.Hkv, a.max_splits, a.req_end - a.req_begin);
+  const dim3 grid(a.Hkv * a.col_blocks, a.max_splits, a.req_end - a.req_begin);
   if (a.kv_fmt == F_FP8)
     hipLaunchKernelGGL(decode_split_kernel<F_FP8>, grid, dim3(kThreads), 0, s, a);
   else
@@ -382,7 +399,7 @@ hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.H, a.req_end - a.req_begin);
+  const dim3 grid(a.H, a.req_end - a.req_begin, a.max_n);
   hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kD), 0, s, a);
   return hipGetLastError();
 }

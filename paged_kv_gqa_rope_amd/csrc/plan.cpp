@@ -102,8 +102,9 @@ int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* p
     if (ty == PKV_REQ_CONTEXT && seen_gen)
       return fail(err, PKV_ERR_ORDER, "request %lld: context request after a generation request", r);
     if (n < 1) return fail(err, PKV_ERR_INVALID_ARG, "request %lld: context length %lld < 1", r, n);
-    if (ty == PKV_REQ_GENERATION && n != 1)
-      return fail(err, PKV_ERR_UNSUPPORTED, "request %lld: generation request with %lld new tokens (only 1)", r, n);
+    if (ty == PKV_REQ_GENERATION && n > kMaxGenTokens)
+      return fail(err, PKV_ERR_UNSUPPORTED, "request %lld: generation request with %lld new tokens (at most %lld)", r, n,
+                  static_cast<int64_t>(kMaxGenTokens));
     if (S < n) return fail(err, PKV_ERR_INVALID_ARG, "request %lld: sequence length %lld < context length %lld", r, S, n);
     if (ty == PKV_REQ_CONTEXT && (S - n) % T)
       return fail(err, PKV_ERR_CHUNK_ALIGN, "request %lld: cached length %lld is not a multiple of tokens_per_block %lld",
@@ -129,6 +130,8 @@ int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* p
       p.num_gen++;
       p.max_S_gen = std::max(p.max_S_gen, S);
       p.gen_keys += S;
+      p.gen_tokens += n;
+      p.max_gen_n = std::max(p.max_gen_n, n);
     }
     p.max_n = std::max(p.max_n, n);
     p.max_S = std::max(p.max_S, S);
@@ -147,7 +150,9 @@ int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* p
 }
 
 void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) {
-  p->fast_decode = p->num_gen > 0 && desc_fast_decode(d);
+  const int32_t G = d.num_heads / d.num_kv_heads;
+  p->fast_decode = p->num_gen > 0 && desc_fast_decode(d) && G * p->max_gen_n <= kMaxDecodeCols;
+  p->col_blocks = (G * p->max_gen_n + 15) / 16;
   p->fast_prefill = p->num_ctx > 0 && desc_fast_prefill(d);
   p->chunk = 0;
   p->max_splits = 0;
@@ -182,7 +187,7 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   p->chunk = static_cast<int32_t>(c);
   p->max_splits = static_cast<int32_t>(mx);
   p->decode_items = items;
-  const int64_t rows = static_cast<int64_t>(p->num_gen) * d.num_heads * mx;
+  const int64_t rows = static_cast<int64_t>(p->gen_tokens) * d.num_heads * mx;
   const size_t ml = static_cast<size_t>(rows) * 2 * sizeof(float);
   p->ws_ml_off = 0;
   p->ws_o_off = ((ml + 255) / 256) * 256;
@@ -194,7 +199,10 @@ size_t workspace_upper_bound(const pkv_attn_desc& d, int32_t max_num_requests, i
   if (!desc_fast_decode(d)) return 0;
   const int64_t min_chunk = std::max<int64_t>(64, d.tokens_per_block);
   const int64_t splits = std::min<int64_t>(kMaxSplits, (max_seq_len + min_chunk - 1) / min_chunk);
-  const int64_t rows = static_cast<int64_t>(max_num_requests) * d.num_heads * splits;
+  // generation rows: at most kMaxGenTokens per request and at most the token budget
+  const int64_t gen_rows = std::min<int64_t>(static_cast<int64_t>(max_num_requests) * kMaxGenTokens,
+                                             std::max<int64_t>(d.max_num_tokens, max_num_requests));
+  const int64_t rows = gen_rows * d.num_heads * splits;
   const size_t ml = static_cast<size_t>(rows) * 2 * sizeof(float);
   const size_t o = static_cast<size_t>(rows) * d.head_dim * sizeof(float);
   return ((ml + 255) / 256) * 256 + o;

@@ -21,12 +21,15 @@ struct BatchPlan {
   int32_t max_S_gen = 0;      // largest S_r over generation requests
   int64_t ctx_pairs = 0;      // causal (query, key) pairs of context rows
   int64_t gen_keys = 0;       // sum of S_r over generation requests
+  int32_t gen_tokens = 0;     // packed rows owned by generation requests
+  int32_t max_gen_n = 0;      // most new tokens of one generation request (1 + draft tokens)
   // split-KV decode policy (generation rows on the MFMA decode path)
   bool fast_decode = false;
   bool fast_prefill = false;
   int32_t chunk = 0;          // keys per split, a multiple of tokens_per_block
   int32_t max_splits = 0;     // max over generation requests of ceil(S_r / chunk)
   int64_t decode_items = 0;   // (request, kv head, split) work items
+  int32_t col_blocks = 0;     // blocks of 16 (token, query head) columns per (request, kv head)
   // workspace layout (bytes)
   size_t ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
 };
@@ -36,6 +39,11 @@ constexpr int32_t kMaxSplits = 128;       // splits per generation request
 constexpr int32_t kDefaultChunk = 1024;    // keys per split before balancing
 constexpr int64_t kTargetDecodeItems = 4096; // (request, kv head, split) items to aim for
 constexpr int64_t kMinChunkBytes = 256 << 10;  // one KV head's K and V per split, at least
+// Generation requests carry 1 .. kMaxGenTokens new tokens (a token and its draft tokens).
+constexpr int32_t kMaxGenTokens = 64;
+// The split pass takes (token, query head) columns of one KV head in blocks of 16; with
+// more than kMaxDecodeCols columns per request the generic kernel takes the batch.
+constexpr int32_t kMaxDecodeCols = 64;
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
 constexpr bool kHaveFastDecode = true;
 constexpr bool kHaveFastPrefill = true;

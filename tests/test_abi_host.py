@@ -150,7 +150,8 @@ def test_unsupported_configurations():
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(io_dtype=L.PKV_FP8_E4M3), hb))
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(rope_style=7), hb))
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(rotary_dim=40), hb))
-    expect(L.PKV_ERR_UNSUPPORTED, forward(desc_for(), HostBatch([1], [2], [5], [[0]], 1)))  # 2-token generation
+    # generation requests carry at most 64 new tokens (a token and its draft tokens)
+    expect(L.PKV_ERR_UNSUPPORTED, forward(desc_for(), HostBatch([1], [65], [70], [[0, 1]], 2)))
 
 
 def test_empty_batch_is_a_no_op():
@@ -165,10 +166,12 @@ def test_workspace_bounds_cover_every_batch():
         d = desc_for(W.SHAPES[k])
         for _ in range(30):
             B = int(rng.integers(1, 40))
-            seq = rng.integers(1, 40000, B).astype(np.int32)
+            seq = rng.integers(65, 40000, B).astype(np.int32)
+            gen_n = rng.integers(1, 65, B) if rng.random() < 0.5 else np.ones(B, np.int64)  # with draft tokens
             T = d.tokens_per_block
             width = int((seq.max() + T - 1) // T)
-            hb = HostBatch([1] * B, [1] * B, seq, np.zeros((B, width)), 1, with_host_table=False)
+            hb = HostBatch([1] * B, gen_n.tolist(), seq, np.zeros((B, width)), 1, with_host_table=False)
+            d.max_num_tokens = 1 << 20
             need = L.pkv_workspace_size_for_batch(d, hb.desc)
             bound = L.pkv_workspace_size(d, B, int(seq.max()))
             assert need <= bound, (k, B, need, bound)

@@ -91,6 +91,35 @@ def test_interleaved_rope_append_and_attention(H, k, rot):
     print(b.label, "gptj", rot, stats)
 
 
+SPEC_CASES = [
+    # (shape, cached lengths, new tokens per generation request, context requests)
+    (2, [70, 300, 5], [2, 4, 7], []),                         # MHA: up to 7 x 1 columns
+    (5, [1500, 700, 64], [4, 1, 3], []),                      # fp8 cache, G = 4
+    (4, [300, 90, 1000, 63], [8, 2, 5, 1], []),               # G = 8: 64 columns, 4 blocks
+    (4, [200, 1200], [9, 3], []),                             # 72 columns: generic kernel
+    (1, [40, 9], [3, 6], [(20, 16)]),                         # fp32: generic kernel
+    (4, [500, 250], [4, 6], [(100, 0), (64, 128)]),           # context chunks, then drafts
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(SPEC_CASES)))
+def test_generation_requests_with_draft_tokens(H, case_i):
+    """Generation requests with 1 + k new tokens: token i at position p + i sees keys
+    0 .. p + i (causal among the drafts)."""
+    k, past, new, ctx = SPEC_CASES[case_i]
+    sh = dataclasses.replace(W.SHAPES[k], max_num_tokens=1 << 16)
+    b = W.make_batch(sh, ctx=ctx, gen_past=past, gen_new=new, seed=3100 + case_i, pool_blocks_min=8,
+                     label=f"spec{case_i}")
+    case("draft tokens", b.label, sh.name, "new", new, "past", past, "ctx", ctx)
+    st = run_step(H, b)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(sh.kv_dtype)), "pool")
+    stats = compare_attention(st.out_host(), O.run(b)["out"], sh, b.label)
+    print(b.label, stats)
+
+
 def test_full_tiny_workload(H):
     b = W.workload(1)
     case("full", b.label)

@@ -149,6 +149,31 @@ def test_rope_gptj_relative_position():
         assert abs(a - b) < 1e-9
 
 
+def test_draft_tokens_equal_single_token_steps_with_the_earlier_drafts_cached():
+    """A generation request with 1 + k new tokens (speculative-decoding verification:
+    generation length and position offsets, source analysis report 1.4): token i sits
+    at position p + i and sees the cache and tokens 0..i.  So its output equals that of
+    a one-token generation request at position p + i whose cache already holds tokens
+    0..i-1 (rotated, stored) -- built here as a separate batch."""
+    from batch_util import Crafted
+    sh = W.SHAPES[1]                                   # fp32 io and cache: storing is exact
+    p, n = 29, 5
+    A = W.make_batch(sh, gen_past=[p], gen_new=[n], seed=77)
+    tabs = S.tables(A)
+    outA = S.attention_request(A, 0, tabs)
+    q_out, k_new, v_new = S.append_request(A, 0, tabs)
+    hk, hv = A.hist_k(0), A.hist_v(0)
+    for i in range(n):
+        Bi = W.make_batch(sh, gen_past=[p + i], seed=78)
+        Ci = Crafted(sh, Bi.seed, Bi.request_types, Bi.context_lengths, Bi.sequence_lengths,
+                     Bi.block_table, Bi.num_pool_blocks, "draft-step")
+        Ci.set_values([A.new_q(0)[i:i + 1]], [A.new_k(0)[i:i + 1]], [A.new_v(0)[i:i + 1]],
+                      [np.concatenate([hk, k_new[:i].view(np.float32)])],
+                      [np.concatenate([hv, v_new[:i].view(np.float32)])])
+        outB = S.attention_request(Ci, 0, S.tables(Ci))
+        assert np.allclose(outA[i], outB[0], rtol=0, atol=1e-12), i
+
+
 # ------------------------------------------------------------------ softmax / attention
 def test_softmax_printed_temperature_example():
     rows = [l.split() for l in open(os.path.join(HERE, "golden", "softmax_temperature.txt"))

@@ -139,19 +139,21 @@ class Batch:
 
 
 def make_batch(shape: Shape, ctx=(), gen_past=(), seed: int = 0, pool_blocks_min: int = 0,
-               label: str = "") -> Batch:
+               label: str = "", gen_new=None) -> Batch:
     """Build a batch from explicit lengths.
 
     ``ctx`` is a sequence of (n_r, past_r) for context requests (their chunk
     and the tokens already cached before it); ``gen_past`` lists the cached
-    length of each generation request (each brings one new token).
+    length of each generation request.  A generation request brings one new
+    token, or ``gen_new[j]`` tokens (the token plus draft tokens to verify).
     """
     T = shape.tokens_per_block
     types, n, s = [], [], []
     for (nr, pr) in ctx:
         types.append(CONTEXT); n.append(int(nr)); s.append(int(pr) + int(nr))
-    for pr in gen_past:
-        types.append(GENERATION); n.append(1); s.append(int(pr) + 1)
+    for j, pr in enumerate(gen_past):
+        nr = 1 if gen_new is None else int(gen_new[j])
+        types.append(GENERATION); n.append(nr); s.append(int(pr) + nr)
     types = np.asarray(types, np.int32)
     n = np.asarray(n, np.int32)
     s = np.asarray(s, np.int32)
