@@ -27,7 +27,7 @@ if ROOT not in sys.path:
 METRIC = "decode attn GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak; tok/s"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-BYTES = {"fp32": 4, "bf16": 2, "fp8_e4m3": 1}
+BYTES = {"fp32": 4, "bf16": 2, "fp8_e4m3": 1, "int8": 1}
 HEADLINE = 2
 
 
@@ -83,10 +83,15 @@ def variant_batch(name: str):
         sh = dataclasses.replace(W.SHAPES[4])
         past = W._uniform_pasts(1004, 128, 256, 4096)
         return W.make_batch(sh, gen_past=past, gen_new=[4] * 128, seed=1004, label="w4-spec4")
+    if name == "int8kv5":        # workload 5 with an int8 KV cache (scale 2^-5 for K and V)
+        sh = dataclasses.replace(W.SHAPES[5], name="longdecode-gqa4-int8kv", kv_dtype=W.INT8,
+                                 k_scale=2.0 ** -5, v_scale=2.0 ** -5)
+        b = W.workload(5)
+        return dataclasses.replace(b, shape=sh, label="w5-int8kv")
     raise KeyError(name)
 
 
-VARIANTS = ("gptj3", "gptj3-half", "spec4-gqa8")
+VARIANTS = ("gptj3", "gptj3-half", "spec4-gqa8", "int8kv5")
 
 
 def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:

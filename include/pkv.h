@@ -65,7 +65,8 @@ typedef enum pkv_status {
 } pkv_status;
 
 /* element formats */
-enum { PKV_FP32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* OCP E4M3: bias 7, max 448, no inf */ };
+enum { PKV_FP32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* OCP E4M3: bias 7, max 448, no inf */,
+       PKV_INT8 = 3 /* two's-complement int8 codes, -128 .. 127 */ };
 /* host_request_types values ([REPORT] 1.1: context vs generation phase) */
 enum { PKV_REQ_CONTEXT = 0, PKV_REQ_GENERATION = 1 };
 /* rotary embedding styles ([REPORT] 1.1 names GPT-NeoX among the RoPE variants) */
@@ -79,7 +80,7 @@ enum { PKV_ROPE_NONE = 0, PKV_ROPE_NEOX = 1, PKV_ROPE_GPTJ = 2 };
  *   head_dim                : D, 64 or 128.
  *   tokens_per_block        : T, tokens per KV block: 16, 32, 64, 128 or 256.
  *   io_dtype                : q, k, v, q_out and out: PKV_FP32 or PKV_BF16.
- *   kv_dtype                : KV pool: PKV_FP32, PKV_BF16 or PKV_FP8_E4M3.
+ *   kv_dtype                : KV pool: PKV_FP32, PKV_BF16, PKV_FP8_E4M3 or PKV_INT8.
  *   rope_style, rotary_dim  : PKV_ROPE_NEOX rotates pairs (j, j + R/2), j < R/2, of
  *                             each q and new k head by angle pos * theta_j, where R =
  *                             rotary_dim (0 means head_dim; otherwise a multiple of 16,
@@ -91,10 +92,13 @@ enum { PKV_ROPE_NONE = 0, PKV_ROPE_NEOX = 1, PKV_ROPE_GPTJ = 2 };
  *                             and in R.  PKV_ROPE_NONE stores k as given.
  *   softmax_scale           : <= 0 means 1/sqrt(head_dim).
  *   k_scale_quant_orig,
- *   v_scale_quant_orig      : fp8 cache only: real value = scale * stored e4m3 value.
- *                             The append quantises with 1/scale (computed in fp64) and
- *                             rounds to nearest-even, saturating to +-448 ([NOTES] 6.4:
- *                             kv_scale_orig_quant on write, kv_scale_quant_orig on read).
+ *   v_scale_quant_orig      : fp8 and int8 caches only: real value = scale * stored
+ *                             value (the e4m3 value, or the integer code).  The append
+ *                             quantises with 1/scale (computed in fp64) and rounds to
+ *                             nearest-even, saturating to +-448 (fp8) or to -128 .. 127
+ *                             (int8; NaN stores 0) ([NOTES] 6.4: kv_scale_orig_quant on
+ *                             write, kv_scale_quant_orig on read, the INT8 KV cache
+ *                             compressing only the stored format).
  *   max_num_tokens          : token budget of one batch (8192 by default, [REPORT] 1.3).
  */
 typedef struct pkv_attn_desc {

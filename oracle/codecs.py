@@ -6,22 +6,28 @@
   4 exponent bits (bias 7), 3 fraction bits, subnormals, no infinities,
   NaN only at S.1111.111, largest finite magnitude 1.75 * 2^8 = 448.
 * fp32: IEEE-754 binary32; the fp64 -> fp32 step uses numpy's IEEE cast.
+* int8: two's-complement 8-bit integer codes, -128 .. 127; the code's value is the
+  integer itself.
 
 Every encoder rounds an fp64 value DIRECTLY to the target format, round to
 nearest, ties to even, in one step (never via an intermediate format).  The
-fp8 encoder saturates finite overflow and infinities to +-448 ("satfinite").
+fp8 encoder saturates finite overflow and infinities to +-448 ("satfinite"); the
+int8 encoder rounds to the nearest integer (ties to even) and saturates to
+-128 .. 127, storing NaN as 0.
 
 The KV-cache quantisation follows the INT8/FP8 KV cache passage of
 "TensorRT-LLM 1.0 study notes", section 6.4: values are quantised on write with
 the scale kv_scale_orig_quant and dequantised on read with kv_scale_quant_orig.
 Reading taken: one fp32 per-tensor scale s = kv_scale_quant_orig per K and V;
-the write multiplies by 1/s computed in fp64, the read multiplies by s.
+the write multiplies by 1/s computed in fp64, the read multiplies by s.  The
+passage names the INT8 KV cache as the one that only compresses the stored
+format (dequantised on read); the same pair of scales serves fp8 and int8.
 """
 from __future__ import annotations
 
 import numpy as np
 
-FP32, BF16, FP8_E4M3 = "fp32", "bf16", "fp8_e4m3"
+FP32, BF16, FP8_E4M3, INT8 = "fp32", "bf16", "fp8_e4m3", "int8"
 
 
 # ---------------------------------------------------------------- bf16
@@ -104,16 +110,33 @@ def f64_to_e4m3(x) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+# ---------------------------------------------------------------- int8
+INT8_MIN, INT8_MAX = -128, 127
+
+
+def int8_to_f64(codes) -> np.ndarray:
+    """Decode int8 codes (int8, or their uint8 bit patterns) to their integer value."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
+def f64_to_int8(x) -> np.ndarray:
+    """Round fp64 to the nearest integer (ties to even), saturate to -128 .. 127; NaN -> 0."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.rint(np.where(np.isnan(x), 0.0, x))
+    return np.clip(r, INT8_MIN, INT8_MAX).astype(np.int8)
+
+
 # ---------------------------------------------------------------- dispatch
 def storage_dtype(fmt: str):
-    return {FP32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8}[fmt]
+    return {FP32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, INT8: np.int8}[fmt]
 
 
 def encode(values, fmt: str, scale: float = 1.0) -> np.ndarray:
     """fp64 values -> stored representation of ``fmt``.
 
-    For fp8 the value is first multiplied by 1/scale (fp64), i.e. quantised with
-    kv_scale_orig_quant = 1/kv_scale_quant_orig.
+    For fp8 and int8 the value is first multiplied by 1/scale (fp64), i.e. quantised
+    with kv_scale_orig_quant = 1/kv_scale_quant_orig.
     """
     v = np.asarray(values, dtype=np.float64)
     if fmt == FP32:
@@ -123,15 +146,20 @@ def encode(values, fmt: str, scale: float = 1.0) -> np.ndarray:
     if fmt == FP8_E4M3:
         inv = 1.0 / np.float64(np.float32(scale))
         return f64_to_e4m3(v * inv)
+    if fmt == INT8:
+        inv = 1.0 / np.float64(np.float32(scale))
+        return f64_to_int8(v * inv)
     raise ValueError(fmt)
 
 
 def decode(stored, fmt: str, scale: float = 1.0) -> np.ndarray:
-    """Stored representation -> fp64 value (fp8: scale * code value)."""
+    """Stored representation -> fp64 value (fp8, int8: scale * code value)."""
     if fmt == FP32:
         return np.asarray(stored, dtype=np.float32).astype(np.float64)
     if fmt == BF16:
         return bf16_to_f64(stored)
     if fmt == FP8_E4M3:
         return np.float64(np.float32(scale)) * e4m3_to_f64(stored)
+    if fmt == INT8:
+        return np.float64(np.float32(scale)) * int8_to_f64(stored)
     raise ValueError(fmt)

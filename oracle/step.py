@@ -122,12 +122,12 @@ def run(batch):
     }
 
 
-BITS = {codecs.FP32: np.uint32, codecs.BF16: np.uint16, codecs.FP8_E4M3: np.uint8}
+BITS = {codecs.FP32: np.uint32, codecs.BF16: np.uint16, codecs.FP8_E4M3: np.uint8, codecs.INT8: np.uint8}
 
 
 def expected_pool(batch, sentinel, include_new: bool = True, include_history: bool = True):
     """The whole paged pool [nb, 2, T, Hkv, D] as stored bit patterns (uint32 / uint16 /
-    uint8 for fp32 / bf16 / fp8) after the history fill and the step's append; slots
+    uint8 for fp32 / bf16 / fp8 and int8) after the history fill and the step's append; slots
     nobody writes hold the bit pattern ``sentinel``."""
     sh = batch.shape
     T = sh.tokens_per_block

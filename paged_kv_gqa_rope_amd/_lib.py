@@ -23,7 +23,7 @@ PKV_ERR_BLOCK_RANGE = -6
 PKV_ERR_WORKSPACE = -7
 PKV_ERR_HIP = -8
 
-PKV_FP32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_FP32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
 PKV_REQ_CONTEXT, PKV_REQ_GENERATION = 0, 1
 PKV_ROPE_NONE, PKV_ROPE_NEOX, PKV_ROPE_GPTJ = 0, 1, 2
 

@@ -72,7 +72,10 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int fmt_of(int32_t dt) { return dt == PKV_FP32 ? pkv::F_FP32 : dt == PKV_BF16 ? pkv::F_BF16 : pkv::F_FP8; }
+int fmt_of(int32_t dt) {
+  return dt == PKV_FP32 ? pkv::F_FP32 : dt == PKV_BF16 ? pkv::F_BF16 : dt == PKV_INT8 ? pkv::F_INT8 : pkv::F_FP8;
+}
+bool scaled_cache(int32_t dt) { return dt == PKV_FP8_E4M3 || dt == PKV_INT8; }
 
 int check_rows(const void* p, int64_t stride, int64_t min_elems, int32_t dtype, const char* name) {
   if (stride < min_elems)
@@ -171,9 +174,9 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, 
   a.R = pkv::rot_dim(*desc);
   a.mbps = batch->max_blocks_per_seq;
   a.num_blocks = batch->num_pool_blocks;
-  const bool fp8 = desc->kv_dtype == PKV_FP8_E4M3;
-  a.inv_k_scale = fp8 ? 1.0 / static_cast<double>(desc->k_scale_quant_orig) : 1.0;
-  a.inv_v_scale = fp8 ? 1.0 / static_cast<double>(desc->v_scale_quant_orig) : 1.0;
+  const bool quant = scaled_cache(desc->kv_dtype);
+  a.inv_k_scale = quant ? 1.0 / static_cast<double>(desc->k_scale_quant_orig) : 1.0;
+  a.inv_v_scale = quant ? 1.0 / static_cast<double>(desc->v_scale_quant_orig) : 1.0;
   a.io_fmt = fmt_of(desc->io_dtype);
   a.kv_fmt = fmt_of(desc->kv_dtype);
   a.rope = desc->rope_style == PKV_ROPE_NEOX ? pkv::kRopeNeox
@@ -226,9 +229,9 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
   a.num_blocks = batch->num_pool_blocks;
   const double scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0 / std::sqrt(static_cast<double>(D));
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
-  const bool fp8 = desc->kv_dtype == PKV_FP8_E4M3;
-  a.k_scale = fp8 ? desc->k_scale_quant_orig : 1.f;
-  a.v_scale = fp8 ? desc->v_scale_quant_orig : 1.f;
+  const bool quant = scaled_cache(desc->kv_dtype);
+  a.k_scale = quant ? desc->k_scale_quant_orig : 1.f;
+  a.v_scale = quant ? desc->v_scale_quant_orig : 1.f;
   a.io_fmt = fmt_of(desc->io_dtype);
   a.kv_fmt = fmt_of(desc->kv_dtype);
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -77,7 +77,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, double (&x)
   }
 }
 
-// Round y (times `mul` for fp8) once to format F and store 8 elements at base+off.
+// Round y (times `mul` for fp8 and int8) once to format F and store 8 elements at base+off.
 template <int F>
 __device__ __forceinline__ void store8(void* base, int64_t off, const double (&y)[8], double mul) {
   if constexpr (F == F_FP32) {
@@ -94,7 +94,8 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const double (&y
   } else {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i / 4] |= f64_to_e4m3(y[i] * mul) << (8 * (i % 4));
+    for (int i = 0; i < 8; ++i)
+      w[i / 4] |= (F == F_INT8 ? f64_to_int8(y[i] * mul) : f64_to_e4m3(y[i] * mul)) << (8 * (i % 4));
     *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + off) = make_uint2(w[0], w[1]);
   }
 }
@@ -373,10 +374,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.io_fmt == F_BF16) {
     if (a.kv_fmt == F_BF16) return launch_append_t<F_BF16, F_BF16>(a, s);
     if (a.kv_fmt == F_FP8) return launch_append_t<F_BF16, F_FP8>(a, s);
+    if (a.kv_fmt == F_INT8) return launch_append_t<F_BF16, F_INT8>(a, s);
     return launch_append_t<F_BF16, F_FP32>(a, s);
   }
   if (a.kv_fmt == F_BF16) return launch_append_t<F_FP32, F_BF16>(a, s);
   if (a.kv_fmt == F_FP8) return launch_append_t<F_FP32, F_FP8>(a, s);
+  if (a.kv_fmt == F_INT8) return launch_append_t<F_FP32, F_INT8>(a, s);
   return launch_append_t<F_FP32, F_FP32>(a, s);
 }
 

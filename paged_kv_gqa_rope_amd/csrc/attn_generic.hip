@@ -21,6 +21,7 @@ template <int F>
 __device__ __forceinline__ float load_elem(const void* base, int64_t off) {
   if constexpr (F == F_FP32) return static_cast<const float*>(base)[off];
   else if constexpr (F == F_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
+  else if constexpr (F == F_INT8) return static_cast<float>(static_cast<const int8_t*>(base)[off]);
   else return e4m3x2_to_f32(static_cast<const uint8_t*>(base)[off]).x;
 }
 
@@ -156,10 +157,12 @@ hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s) {
   if (a.io_fmt == F_BF16) {
     if (a.kv_fmt == F_BF16) return launch_t<F_BF16, F_BF16>(a, s);
     if (a.kv_fmt == F_FP8) return launch_t<F_BF16, F_FP8>(a, s);
+    if (a.kv_fmt == F_INT8) return launch_t<F_BF16, F_INT8>(a, s);
     return launch_t<F_BF16, F_FP32>(a, s);
   }
   if (a.kv_fmt == F_BF16) return launch_t<F_FP32, F_BF16>(a, s);
   if (a.kv_fmt == F_FP8) return launch_t<F_FP32, F_FP8>(a, s);
+  if (a.kv_fmt == F_INT8) return launch_t<F_FP32, F_INT8>(a, s);
   return launch_t<F_FP32, F_FP32>(a, s);
 }
 

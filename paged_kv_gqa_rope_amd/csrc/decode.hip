@@ -17,9 +17,9 @@
 //     same head), exp2 with the log2(e) factor folded into the scale.
 //   * O += P V on MFMA: A = P (heads x 32 keys) straight from the score registers,
 //     B = V read transposed from an LDS copy of the tile with ds_read_b64_tr_b16.
-//   * an fp8 cache is dequantised to bf16 on load (exact: every e4m3 value is a
-//     bf16 value); k_scale folds into the softmax scale and v_scale into the
-//     combine, so the pass works on raw codes times one.
+//   * an fp8 or int8 cache is dequantised to bf16 on load (exact: every e4m3 value
+//     and every integer -128 .. 127 is a bf16 value); k_scale folds into the softmax
+//     scale and v_scale into the combine, so the pass works on raw codes times one.
 // Pass 2, one workgroup per (request, query head): M = max m_s, L = sum 2^(m_s-M) l_s,
 // O = sum 2^(m_s-M) o_s / L in a fixed order (no atomics: bitwise reproducible).
 #include <math.h>
@@ -65,6 +65,23 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
   return make_uint4(lo(c.x), hi(c.x), lo(c.y), hi(c.y));
 }
 
+// 8 int8 codes (two dwords) -> 8 bf16 values, exactly: each byte is sign-extended and
+// converted to fp32 (one SDWA v_cvt_f32_i32 per code); an integer of magnitude <= 128
+// has at most 8 significant bits, so the upper half of its fp32 pattern is its bf16
+// pattern, and v_perm_b32 packs two of them per dword.
+__device__ __forceinline__ uint4 int8x8_to_bf16x8(uint2 c) {
+  auto cv = [](uint32_t w, int byte) { return __float_as_uint(static_cast<float>(static_cast<int8_t>(w >> (8 * byte)))); };
+  auto pk = [](uint32_t lo, uint32_t hi) { return __builtin_amdgcn_perm(hi, lo, 0x07060302u); };
+  return make_uint4(pk(cv(c.x, 0), cv(c.x, 1)), pk(cv(c.x, 2), cv(c.x, 3)), pk(cv(c.y, 0), cv(c.y, 1)),
+                    pk(cv(c.y, 2), cv(c.y, 3)));
+}
+// One-byte cache codes -> bf16 for the cache format KV.
+template <int KV>
+__device__ __forceinline__ uint4 codes8_to_bf16x8(uint2 c) {
+  if constexpr (KV == F_INT8) return int8x8_to_bf16x8(c);
+  else return e4m3x8_to_bf16x8(c);
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -72,7 +89,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 // Registers of one 32-key tile in flight: K and V rows as loaded (16 lanes per bf16
-// row, 8 lanes per fp8 row), copied to LDS at compute time.
+// row, 8 lanes per fp8 / int8 row), copied to LDS at compute time.
 template <int KV>
 struct TileRegs {
   uint4 k[KV == F_BF16 ? 8 : 4];
@@ -163,7 +180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int key = min(tb + it * 4 + lg, kend - 1);        // clamp: never read unwritten slots
         R.k[it] = load_kv(static_cast<const uint16_t*>(a.pool) + base_of(key) + li * 8);
       }
-    } else {                                                   // 8 lanes per 128-byte row
+    } else {                                                   // 8 lanes per 128-byte row (fp8, int8)
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int key = min(tb + it * 8 + lane / 8, kend - 1);
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Online-softmax update and O += P V for tile `tile` held in `R`.
   auto compute = [&](int tile, const TileRegs<KV>& R) {
     const int tb = k0 + tile * kTile;
-    // K and V rows into this wave's LDS tiles (bf16; an fp8 cache is dequantised here)
+    // K and V rows into this wave's LDS tiles (bf16; an fp8 / int8 cache is dequantised here)
     wave_lds_fence();
     if constexpr (KV == F_BF16) {
 #pragma unroll
@@ -201,12 +218,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int row = it * 8 + lane / 8, c0 = (lane % 8) * 2;
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) = e4m3x8_to_bf16x8(make_uint2(R.k[it].x, R.k[it].y));
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) =
+            codes8_to_bf16x8<KV>(make_uint2(R.k[it].x, R.k[it].y));
         *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) =
-            e4m3x8_to_bf16x8(make_uint2(R.k[it].z, R.k[it].w));
+            codes8_to_bf16x8<KV>(make_uint2(R.k[it].z, R.k[it].w));
         uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
-        *reinterpret_cast<uint4*>(d) = e4m3x8_to_bf16x8(make_uint2(R.v[it].x, R.v[it].y));
-        *reinterpret_cast<uint4*>(d + 8) = e4m3x8_to_bf16x8(make_uint2(R.v[it].z, R.v[it].w));
+        *reinterpret_cast<uint4*>(d) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].x, R.v[it].y));
+        *reinterpret_cast<uint4*>(d + 8) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].z, R.v[it].w));
       }
     }
     wave_lds_fence();
@@ -393,6 +411,8 @@ hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.Hkv * a.col_blocks, a.max_splits, a.req_end - a.req_begin);
   if (a.kv_fmt == F_FP8)
     hipLaunchKernelGGL(decode_split_kernel<F_FP8>, grid, dim3(kThreads), 0, s, a);
+  else if (a.kv_fmt == F_INT8)
+    hipLaunchKernelGGL(decode_split_kernel<F_INT8>, grid, dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(decode_split_kernel<F_BF16>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -87,6 +87,14 @@ __device__ __forceinline__ uint32_t f64_to_e4m3(double x) {
   return sign | static_cast<uint32_t>(q);
 }
 
+// fp64 -> int8 code: round to the nearest integer (ties to even, v_rndne_f64), saturate
+// to -128 .. 127 (infinities included); NaN stores 0.  Returns the code's low byte.
+__device__ __forceinline__ uint32_t f64_to_int8(double x) {
+  if (x != x) return 0u;
+  const double r = fmin(fmax(__builtin_rint(x), -128.0), 127.0);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+}
+
 // OCP E4M3 -> fp32 for two codes (bytes 0 and 1 of `packed`), hardware conversion.
 __device__ __forceinline__ float2 e4m3x2_to_f32(uint32_t packed) {
   auto v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(packed), false);

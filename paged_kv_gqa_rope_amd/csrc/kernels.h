@@ -7,7 +7,7 @@
 namespace pkv {
 
 // element formats of io tensors and the KV pool
-enum : int { F_FP32 = 0, F_BF16 = 1, F_FP8 = 2 };
+enum : int { F_FP32 = 0, F_BF16 = 1, F_FP8 = 2, F_INT8 = 3 };
 // rotary pairing of the append: none, (j, j + R/2), (2j, 2j + 1)
 enum : int { kRopeNone = 0, kRopeNeox = 1, kRopeGptj = 2 };
 
@@ -25,7 +25,7 @@ struct AppendArgs {
   const int32_t* table;     // device [B][mbps]
   int32_t B, N, H, Hkv, D, T, R, mbps;
   int64_t num_blocks;
-  double inv_k_scale, inv_v_scale;   // fp8 cache: 1/scale; otherwise 1
+  double inv_k_scale, inv_v_scale;   // fp8 / int8 cache: 1/scale; otherwise 1
   int32_t io_fmt, kv_fmt, rope;   // rope: kRopeNone / kRopeNeox / kRopeGptj
   int32_t max_n;            // largest n_r (grid extent)
 };
@@ -42,7 +42,7 @@ struct AttnArgs {
   int32_t tshift;                // log2(T)
   int64_t num_blocks;
   float scale_log2;         // softmax scale * log2(e)
-  float k_scale, v_scale;   // dequantisation scales (1 unless fp8)
+  float k_scale, v_scale;   // dequantisation scales (1 unless fp8 / int8)
   int32_t io_fmt, kv_fmt;
   int32_t req_begin, req_end;    // requests [begin, end) handled by this launch
   int32_t row_begin;             // packed row of request req_begin

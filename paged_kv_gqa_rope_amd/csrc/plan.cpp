@@ -38,8 +38,8 @@ int validate_desc(const pkv_attn_desc* d, std::string& err) {
     return fail(err, PKV_ERR_UNSUPPORTED, "tokens_per_block=%lld (supported: 16, 32, 64, 128, 256)", d->tokens_per_block);
   if (d->io_dtype != PKV_FP32 && d->io_dtype != PKV_BF16)
     return fail(err, PKV_ERR_UNSUPPORTED, "io_dtype=%lld (supported: FP32, BF16)", d->io_dtype);
-  if (d->kv_dtype != PKV_FP32 && d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3)
-    return fail(err, PKV_ERR_UNSUPPORTED, "kv_dtype=%lld (supported: FP32, BF16, FP8_E4M3)", d->kv_dtype);
+  if (d->kv_dtype != PKV_FP32 && d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3 && d->kv_dtype != PKV_INT8)
+    return fail(err, PKV_ERR_UNSUPPORTED, "kv_dtype=%lld (supported: FP32, BF16, FP8_E4M3, INT8)", d->kv_dtype);
   if (d->rope_style != PKV_ROPE_NONE && d->rope_style != PKV_ROPE_NEOX && d->rope_style != PKV_ROPE_GPTJ)
     return fail(err, PKV_ERR_UNSUPPORTED, "rope_style=%lld (supported: NONE, NEOX, GPTJ)", d->rope_style);
   if (d->rotary_dim < 0 || d->rotary_dim > d->head_dim)
@@ -48,10 +48,10 @@ int validate_desc(const pkv_attn_desc* d, std::string& err) {
     return fail(err, PKV_ERR_UNSUPPORTED, "rotary_dim=%lld is not a multiple of 16", d->rotary_dim);
   if (!std::isfinite(d->softmax_scale))
     return fail(err, PKV_ERR_INVALID_ARG, "softmax_scale is not finite");
-  if (d->kv_dtype == PKV_FP8_E4M3) {
+  if (d->kv_dtype == PKV_FP8_E4M3 || d->kv_dtype == PKV_INT8) {
     if (!(std::isfinite(d->k_scale_quant_orig) && d->k_scale_quant_orig > 0.f &&
           std::isfinite(d->v_scale_quant_orig) && d->v_scale_quant_orig > 0.f))
-      return fail(err, PKV_ERR_INVALID_ARG, "fp8 cache needs finite positive k/v scales");
+      return fail(err, PKV_ERR_INVALID_ARG, "fp8 / int8 cache needs finite positive k/v scales");
   }
   if (d->max_num_tokens < 0) return fail(err, PKV_ERR_INVALID_ARG, "max_num_tokens=%lld < 0", d->max_num_tokens);
   return PKV_OK;
@@ -60,7 +60,8 @@ int validate_desc(const pkv_attn_desc* d, std::string& err) {
 bool desc_fast_decode(const pkv_attn_desc& d) {
   if (!kHaveFastDecode) return false;
   const int32_t G = d.num_heads / d.num_kv_heads;
-  return d.io_dtype == PKV_BF16 && (d.kv_dtype == PKV_BF16 || d.kv_dtype == PKV_FP8_E4M3) && G <= 16 &&
+  return d.io_dtype == PKV_BF16 && (d.kv_dtype == PKV_BF16 || d.kv_dtype == PKV_FP8_E4M3 || d.kv_dtype == PKV_INT8) &&
+         G <= 16 &&
          d.head_dim == 128;
 }
 
@@ -175,7 +176,7 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
     *max_s = mx;
     return tot * d.num_kv_heads;
   };
-  const int64_t key_bytes = 2 * static_cast<int64_t>(d.head_dim) * (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+  const int64_t key_bytes = 2 * static_cast<int64_t>(d.head_dim) * (d.kv_dtype == PKV_BF16 ? 2 : d.kv_dtype == PKV_FP32 ? 4 : 1);
   const int64_t lo = std::max<int64_t>(std::max<int64_t>(64, T), kMinChunkBytes / key_bytes);
   int64_t c = std::max<int64_t>(kDefaultChunk, T), mx = 0;
   while (count(c, &mx) < kTargetDecodeItems && c > lo) c /= 2;

@@ -20,11 +20,11 @@ import torch
 
 from . import _lib as L
 
-DTYPE_CODE = {"fp32": L.PKV_FP32, "bf16": L.PKV_BF16, "fp8_e4m3": L.PKV_FP8_E4M3}
-TORCH_STORE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}
-NUMPY_STORE = {"fp32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+DTYPE_CODE = {"fp32": L.PKV_FP32, "bf16": L.PKV_BF16, "fp8_e4m3": L.PKV_FP8_E4M3, "int8": L.PKV_INT8}
+TORCH_STORE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8, "int8": torch.uint8}
+NUMPY_STORE = {"fp32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8, "int8": np.uint8}
 # views of the stored bits with a same-width integer type (for downloads and sentinels)
-TORCH_BITS = {"fp32": torch.int32, "bf16": torch.int16, "fp8_e4m3": torch.uint8}
+TORCH_BITS = {"fp32": torch.int32, "bf16": torch.int16, "fp8_e4m3": torch.uint8, "int8": torch.uint8}
 
 
 def make_desc(shape, rope: bool = True, max_num_tokens: int | None = None) -> L.pkv_attn_desc:

@@ -140,6 +140,9 @@ def test_invalid_arguments():
     expect(L.PKV_ERR_INVALID_ARG, append(desc_for(), HostBatch([0], [0], [0], [[0]], 1)))   # empty context
     fp8 = desc_for(W.SHAPES[5], k_scale_quant_orig=0.0)
     expect(L.PKV_ERR_INVALID_ARG, append(fp8, ok_batch()))
+    int8 = desc_for(W.SHAPES[5], kv_dtype=L.PKV_INT8, v_scale_quant_orig=float("inf"))
+    expect(L.PKV_ERR_INVALID_ARG, forward(int8, ok_batch()))
+    expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(kv_dtype=4), ok_batch()))
 
 
 def test_unsupported_configurations():
@@ -148,6 +151,7 @@ def test_unsupported_configurations():
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(tokens_per_block=8), hb))
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(tokens_per_block=48), hb))
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(io_dtype=L.PKV_FP8_E4M3), hb))
+    expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(io_dtype=L.PKV_INT8), hb))
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(rope_style=7), hb))
     expect(L.PKV_ERR_UNSUPPORTED, append(desc_for(rotary_dim=40), hb))
     # generation requests carry at most 64 new tokens (a token and its draft tokens)

@@ -1,4 +1,4 @@
-"""Pins of the oracle's storage codecs (bf16, OCP fp8 e4m3, fp32)."""
+"""Pins of the oracle's storage codecs (bf16, OCP fp8 e4m3, int8, fp32)."""
 import numpy as np
 import pytest
 import torch
@@ -149,6 +149,47 @@ def test_fp8_scaled_codec_is_quantise_on_write_dequantise_on_read():
     back = C.decode(codes, C.FP8_E4M3, s)
     assert back[1] == 1.0 and back[2] == -3.25 and back[3] == 7.0
     assert back[4] == 448.0 * s                                    # saturated
+
+
+# ------------------------------------------------------------------ int8
+def test_int8_decode_matches_torch_int8_view():
+    # every byte pattern read as a two's-complement int8 by torch's own dtype view
+    ref = torch.from_numpy(ALL8.copy()).view(torch.int8).to(torch.float64).numpy()
+    assert np.array_equal(C.int8_to_f64(ALL8), ref)
+    assert np.array_equal(C.int8_to_f64(ALL8.view(np.int8)), ref)
+    assert C.int8_to_f64(np.uint8(0x80)) == -128 and C.int8_to_f64(np.uint8(0x7F)) == 127
+
+
+def test_int8_encode_roundtrip_ties_and_saturation():
+    codes = ALL8.view(np.int8)
+    assert np.array_equal(C.f64_to_int8(C.int8_to_f64(codes)), codes)
+    enc = lambda v: int(C.f64_to_int8(np.array([v]))[0])
+    # ties go to the even neighbour, on both signs
+    assert [enc(v) for v in (0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5)] == [0, 2, 2, 0, -2, -2, 126]
+    assert enc(np.nextafter(0.5, 1.0)) == 1 and enc(np.nextafter(2.5, 0.0)) == 2
+    # saturation at the ends of the int8 range; NaN stores 0
+    assert [enc(v) for v in (127.49, 127.5, 128.0, 1e30, np.inf)] == [127, 127, 127, 127, 127]
+    assert [enc(v) for v in (-128.5, -129.0, -1e30, -np.inf)] == [-128, -128, -128, -128]
+    assert enc(np.nan) == 0
+
+
+def test_int8_encode_matches_torch_round_half_even_in_range():
+    # torch.round rounds half to even; inside the range no saturation applies
+    x = np.random.default_rng(11).uniform(-127.9, 127.4, 20000)
+    x[:200] = np.round(x[:200]) + 0.5                              # exact ties
+    x = x[(x > -128.5) & (x < 127.5)]
+    ref = torch.round(torch.from_numpy(x)).to(torch.int8).numpy()
+    assert np.array_equal(C.f64_to_int8(x), ref)
+
+
+def test_int8_scaled_codec_is_quantise_on_write_dequantise_on_read():
+    s = 2.0 ** -5
+    x = np.array([0.0, 1.0, -3.25, 3.96875, 100.0, -100.0, 0.015625, 0.046875])
+    codes = C.encode(x, C.INT8, s)
+    assert codes.dtype == np.int8
+    assert list(codes) == [0, 32, -104, 127, 127, -128, 0, 2]     # 0.5 and 1.5 quanta tie to even
+    back = C.decode(codes, C.INT8, s)
+    assert list(back) == [0.0, 1.0, -3.25, 3.96875, 3.96875, -4.0, 0.0, 0.0625]
 
 
 def test_fp32_codec():

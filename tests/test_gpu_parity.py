@@ -151,7 +151,7 @@ def test_outputs_are_bitwise_invariant_to_block_placement_and_reruns(H, k):
         assert np.array_equal(bits_of(o), bits_of(outs[0])), "block placement changes the output"
 
 
-@pytest.mark.parametrize("kv", [W.BF16, W.FP8_E4M3])
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8_E4M3, W.INT8])
 def test_gqa_equals_mha_with_replicated_kv_heads(H, kv):
     G = 4
     gqa = W.Shape("gqa", 16, 4, 128, 64, W.BF16, kv, 5e5, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
@@ -246,7 +246,8 @@ def test_empty_batch_launches_nothing(H):
 
 # ------------------------------------------------------------------ decode kernel edges
 @pytest.mark.parametrize("T,G,kv", [(16, 1, W.BF16), (32, 2, W.BF16), (64, 4, W.FP8_E4M3), (128, 8, W.BF16),
-                                    (256, 16, W.BF16), (16, 8, W.FP8_E4M3), (64, 3, W.BF16)])
+                                    (256, 16, W.BF16), (16, 8, W.FP8_E4M3), (64, 3, W.BF16),
+                                    (32, 4, W.INT8), (256, 16, W.INT8), (16, 1, W.INT8)])
 def test_decode_lengths_blocks_and_groups(H, T, G, kv):
     Hkv = 2
     sh = W.Shape(f"dec-T{T}-G{G}", Hkv * G, Hkv, 128, T, W.BF16, kv, 1e4, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
@@ -269,6 +270,52 @@ def test_decode_fp8_saturating_values(H):
     assert np.any((want & 0x7F) == 0x7E), "expected some saturated codes"
     assert_bits_equal(bits_of(st.pool_host()), want, "pool")
     compare_attention(st.out_host(), O.run(b)["out"], sh, "fp8-sat")
+
+
+def test_decode_int8_saturating_values(H):
+    # values beyond 127.5 * scale (or below -128.5 * scale) saturate on write
+    sh = W.Shape("int8-sat", 8, 2, 128, 64, W.BF16, W.INT8, 1e4, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    b = W.make_batch(sh, gen_past=[200, 70], seed=3)
+    case("int8-saturation")
+    st = run_step(H, b)
+    want = O.expected_pool(b, sentinel(W.INT8))
+    assert np.any(want == 0x7F) and np.any(want == 0x80), "expected saturated codes of both signs"
+    assert_bits_equal(bits_of(st.pool_host()), want, "pool")
+    compare_attention(st.out_host(), O.run(b)["out"], sh, "int8-sat")
+
+
+def _int8_shape(k, scale=2.0 ** -5, **kw):
+    return dataclasses.replace(W.SHAPES[k], name=W.SHAPES[k].name + "-int8kv", kv_dtype=W.INT8,
+                               k_scale=scale, v_scale=scale, **kw)
+
+
+INT8_CASES = [
+    # (label, batch builder): the int8 cache on every attention path
+    ("decode-gqa4", lambda: W.small_workload(5, shape=_int8_shape(5))),
+    ("decode-mha", lambda: W.small_workload(2, shape=_int8_shape(2))),
+    ("mixed-gqa8", lambda: W.small_workload(4, shape=_int8_shape(4))),
+    ("prefill-gqa4", lambda: W.small_workload(3, shape=_int8_shape(3))),
+    ("fp32-io", lambda: W.small_workload(1, shape=_int8_shape(1, scale=2.0 ** -4))),
+    ("drafts-gqa8", lambda: W.make_batch(_int8_shape(4, max_num_tokens=1 << 16), ctx=[(64, 128)],
+                                         gen_past=[300, 1000, 63], gen_new=[4, 8, 2], seed=77, pool_blocks_min=4)),
+    ("gptj-half", lambda: W.small_workload(4, shape=_int8_shape(4, rope_style="gptj", rotary_dim=64))),
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(INT8_CASES)))
+def test_int8_cache_step(H, case_i):
+    """INT8 KV cache ("TensorRT-LLM 1.0 study notes", 6.4): the append quantises with
+    1/scale and stores codes bit-exactly as the oracle does; attention dequantises on read."""
+    label, make = INT8_CASES[case_i]
+    b = make()
+    case("int8", label, b.shape.name)
+    st = run_step(H, b)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(W.INT8)), "pool")
+    stats = compare_attention(st.out_host(), O.run(b)["out"], b.shape, label)
+    print("int8", label, stats)
 
 
 # ------------------------------------------------------------------ context kernel edges

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 # ------------------------------------------------------------------ helpers
-from batch_util import Crafted, crafted  # noqa: E402
+from batch_util import Crafted, as_crafted, crafted  # noqa: E402
 
 
 def rand_unit(rng, shape):
@@ -387,6 +387,59 @@ def test_fp8_cache_dequantises_what_was_quantised():
     assert np.array_equal(C.e4m3_to_f64(codes) * s, K)            # K holds exactly representable values
     hk = C.bf16_to_f64(b.hist_k(0))
     assert np.max(np.abs(K[: hk.shape[0]] - hk)) <= 2.0 ** -4 * np.max(np.abs(hk)) + 1e-12
+
+
+def _int8_grid_batch(kv, ks, vs):
+    """Generation + context batch whose cached K/V are integers times their scale (bf16
+    io); new k rows are zero, so RoPE keeps them on the grid."""
+    sh = W.Shape("int8-grid", 8, 2, 128, 16, W.BF16, kv, 1.0e4, k_scale=ks, v_scale=vs)
+
+    def fill(tag, r, rows, heads):
+        rng = np.random.default_rng([77, r, len(tag)])
+        if tag == "q":
+            x = rng.standard_normal((rows, heads, 128)).astype(np.float32)
+        elif tag == "k":
+            x = np.zeros((rows, heads, 128), np.float32)
+        else:
+            sc = ks if tag == "hk" else vs
+            x = (rng.integers(-128, 128, (rows, heads, 128)) * sc).astype(np.float32)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    return crafted(sh, ctx=[(21, 40)], gen_past=[70, 33], seed=5, fill=fill)
+
+
+def test_int8_cache_is_exact_on_its_grid_and_matches_bf16_cache():
+    # "TensorRT-LLM 1.0 study notes", 6.4: the INT8 KV cache changes only the stored
+    # format.  Values that are integers (-128 .. 127) times the scale survive the round
+    # trip exactly, so the step must give the bf16 cache's results bit for bit.
+    ks, vs = 2.0 ** -4, 2.0 ** -6
+    b8 = _int8_grid_batch(W.INT8, ks, vs)
+    b16 = as_crafted(b8, shape=W.with_shape(b8, kv_dtype=W.BF16).shape).set_values(**b8._vals)
+    r8, r16 = S.run(b8), S.run(b16)
+    assert np.array_equal(r8["out"], r16["out"])
+    tabs = S.tables(b8)
+    for r in range(b8.num_requests):
+        _, K8, V8 = S.cache_request(b8, r, tabs)
+        _, K16, V16 = S.cache_request(b16, r, tabs)
+        assert np.array_equal(K8, K16) and np.array_equal(V8, V16)
+        assert np.all(np.abs(K8) <= 128 * ks) and np.all(np.abs(V8) <= 128 * vs)
+    pool = S.expected_pool(b8, 0)
+    assert pool.dtype == np.uint8
+
+
+def test_int8_cache_rounds_and_saturates_history():
+    b = W.small_workload(5, shape=W.Shape("s5-int8", 32, 8, 128, 64, W.BF16, W.INT8, 5.0e5,
+                                          k_scale=2.0 ** -5, v_scale=2.0 ** -5))
+    tabs = S.tables(b)
+    _, K, V = S.cache_request(b, 0, tabs)
+    s = 2.0 ** -5
+    c = K / s
+    assert np.array_equal(c, np.round(c)) and c.min() >= -128 and c.max() <= 127
+    hk = C.bf16_to_f64(b.hist_k(0))
+    inside = (hk > -128.5 * s) & (hk < 127.5 * s)
+    assert np.all(np.abs(K[: hk.shape[0]][inside] - hk[inside]) <= s / 2)
+    assert np.all(K[: hk.shape[0]][hk >= 127.5 * s] == 127 * s)
+    assert np.all(K[: hk.shape[0]][hk <= -128.5 * s] == -128 * s)
+    assert np.any(~inside)                                         # the draw does reach saturation
 
 
 def test_small_workload_runs_and_rows_are_convex_combinations():

@@ -7,6 +7,6 @@ RoPE, the storage codecs, the paged scatter and attention all live on the
 two sides that are compared.
 """
 from .synth import (  # noqa: F401
-    FP32, BF16, FP8_E4M3, CONTEXT, GENERATION,
+    FP32, BF16, FP8_E4M3, INT8, CONTEXT, GENERATION,
     Shape, Batch, make_batch, SHAPES, workload, small_workload, WORKLOADS, SMALL_WORKLOADS,
 )

@@ -17,8 +17,8 @@ Recipe (the same for every workload):
 Values are returned in the io dtype's own representation: ``float32`` arrays
 for fp32, ``uint16`` bit patterns for bf16.  History ("already cached") values
 are returned the same way; they count as already rotated, and each side writes
-them into its own cache representation (for an fp8 cache that means its own
-quantiser).
+them into its own cache representation (for an fp8 or int8 cache that means its
+own quantiser).
 
 Nothing here rotates, rounds to a storage format, scatters into pages or
 attends: those are the method, and each compared side implements them itself.
@@ -29,7 +29,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-FP32, BF16, FP8_E4M3 = "fp32", "bf16", "fp8_e4m3"
+FP32, BF16, FP8_E4M3, INT8 = "fp32", "bf16", "fp8_e4m3", "int8"
 CONTEXT, GENERATION = 0, 1
 
 _TAGS = {"lengths": 1, "blocks": 2, "q": 3, "k": 4, "v": 5, "hist_k": 6, "hist_v": 7}
@@ -52,7 +52,7 @@ class Shape:
     rope_theta: float
     rotary_dim: int = 0          # 0 means head_dim
     rope_style: str = "neox"     # "neox": pairs (j, j + R/2); "gptj": pairs (2j, 2j + 1)
-    k_scale: float = 1.0         # fp8 cache only: real value = scale * stored value
+    k_scale: float = 1.0         # fp8 / int8 cache only: real value = scale * stored value
     v_scale: float = 1.0
     max_num_tokens: int = 8192
 
