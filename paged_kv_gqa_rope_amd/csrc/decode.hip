@@ -57,6 +57,11 @@ __device__ __forceinline__ uint4 load_kv(const void* p) {
 __device__ __forceinline__ int kpos(int r, int c) { return c ^ (r & 15); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16, round to nearest-even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 // 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly (every e4m3 value is a bf16 value):
 // v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes per instruction.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
@@ -150,9 +155,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int ntiles = (kend - k0 + kTile - 1) / kTile;
   const int tshift = a.tshift, tmask = a.T - 1;
   const int last_blk = (kend - 1) >> tshift;
-  const int64_t blk_elems = 2 * static_cast<int64_t>(a.T) * kv_row;   // one block: K and V of T slots
+  const int64_t blk_bytes = 2 * static_cast<int64_t>(a.T) * kv_row * (KV == F_BF16 ? 2 : 1);   // K and V of T slots
   uint16_t* vt = vtile[wave];
   uint16_t* kt = ktile[wave];
+  // Load `it` of a tile covers rows it*kRows + lane/kLanes at byte column (lane%kLanes)*16
+  // (16 lanes per 256-byte bf16 row, 8 per 128-byte fp8 / int8 row).
+  constexpr int kEB = KV == F_BF16 ? 2 : 1;                    // cache element bytes
+  constexpr int kLoads = KV == F_BF16 ? 8 : 4;
+  constexpr int kRows = kWave * 16 / (kD * kEB);               // rows per load instruction
+  constexpr int kLanes = kWave / kRows;                        // lanes per row
+  const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * kEB;
+  uint32_t lane_off[kLoads];                                   // byte offset inside a tile
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it)
+    lane_off[it] = static_cast<uint32_t>(it * kRows + lane / kLanes) * row_bytes + (lane % kLanes) * 16u;
+  // A tile needs no masking when it lies inside the chunk and inside the causal range of
+  // every valid column of the block (the lowest of them is token cb*16 / G).
+  const int lim_all = S - n + (cb * 16) / G;
 
   // Block IDs of a tile: tiles are 32-aligned and T is a power of two >= 16, so a tile
   // lies in one block (T >= 32) or covers two (T = 16).  Read two tiles ahead.
@@ -161,46 +180,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     raw[0] = __builtin_amdgcn_readfirstlane(table[min(kb0, last_blk)]);
     raw[1] = __builtin_amdgcn_readfirstlane(table[min(kb0 + 1, last_blk)]);
   };
-  // Issue every load of tile `tile` (ids already resolved) into `R`.
+  // Issue every load of tile `tile` (ids already resolved) into `R`.  Loads it < kLoads/2
+  // cover tile rows 0..15, the others rows 16..31, so every load has one scalar base: B0
+  // (the tile's block at the tile's first slot) or B1 (the block of rows 16..31; the
+  // same block unless T = 16).  Rows past the chunk end are still slots of an allocated
+  // block (in bounds); their scores are masked and their V rows zeroed in compute.
   auto issue = [&](int tile, const int32_t (&rawid)[2], TileRegs<KV>& R) {
     const int tb = k0 + tile * kTile;
-    const int kb0 = tb >> tshift;
     int32_t id0 = __builtin_amdgcn_readfirstlane(rawid[0]);
     int32_t id1 = __builtin_amdgcn_readfirstlane(rawid[1]);
     id0 = (id0 >= 0 && id0 < a.num_blocks) ? id0 : 0;
     id1 = (id1 >= 0 && id1 < a.num_blocks) ? id1 : 0;
-    auto base_of = [&](int key) -> int64_t {                  // element offset of (block, K, slot)
-      const int32_t id = ((key >> tshift) == kb0) ? id0 : id1;
-      return static_cast<int64_t>(id) * blk_elems + static_cast<int64_t>(key & tmask) * kv_row +
-             static_cast<int64_t>(g) * kD;
-    };
-    if constexpr (KV == F_BF16) {                              // 16 lanes per 256-byte row
+    const char* head = static_cast<const char*>(a.pool) + g * (kD * kEB);
+    const char* b0 = head + static_cast<int64_t>(id0) * blk_bytes + static_cast<int64_t>(tb & tmask) * row_bytes;
+    const char* b1 = a.T >= kTile ? b0 : head + static_cast<int64_t>(id1) * blk_bytes - 16 * static_cast<int64_t>(row_bytes);
+    const int64_t vofs = static_cast<int64_t>(a.T) * row_bytes;
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int key = min(tb + it * 4 + lg, kend - 1);        // clamp: never read unwritten slots
-        R.k[it] = load_kv(static_cast<const uint16_t*>(a.pool) + base_of(key) + li * 8);
-      }
-    } else {                                                   // 8 lanes per 128-byte row (fp8, int8)
+    for (int it = 0; it < kLoads; ++it) R.k[it] = load_kv((it < kLoads / 2 ? b0 : b1) + lane_off[it]);
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int key = min(tb + it * 8 + lane / 8, kend - 1);
-        R.k[it] = load_kv(static_cast<const uint8_t*>(a.pool) + base_of(key) + (lane % 8) * 16);
-      }
-    }
-    const int64_t vofs = static_cast<int64_t>(a.T) * kv_row;
-    if constexpr (KV == F_BF16) {                              // 16 lanes per 256-byte row
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int key = min(tb + it * 4 + lg, kend - 1);
-        R.v[it] = load_kv(static_cast<const uint16_t*>(a.pool) + base_of(key) + vofs + li * 8);
-      }
-    } else {                                                   // 8 lanes per 128-byte row
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int key = min(tb + it * 8 + lane / 8, kend - 1);
-        R.v[it] = load_kv(static_cast<const uint8_t*>(a.pool) + base_of(key) + vofs + (lane % 8) * 16);
-      }
-    }
+    for (int it = 0; it < kLoads; ++it) R.v[it] = load_kv((it < kLoads / 2 ? b0 : b1) + vofs + lane_off[it]);
   };
   // Online-softmax update and O += P V for tile `tile` held in `R`.
   auto compute = [&](int tile, const TileRegs<KV>& R) {
@@ -227,6 +225,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         *reinterpret_cast<uint4*>(d + 8) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].z, R.v[it].w));
       }
     }
+    if (tb + kTile > kend) {
+      // wave-uniform, last tile of a chunk only: rows at or past the chunk end were read
+      // from unwritten slots; zero their V so that P = 0 times them stays 0
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it) {
+        const int row = it * kRows + lane / kLanes;
+        if (tb + row >= kend) {
+          uint16_t* d = vt + row * kVStride + (lane % kLanes) * (kD / kLanes);
+#pragma unroll
+          for (int j = 0; j < kD / kLanes; j += 8) *reinterpret_cast<uint4*>(d + j) = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
     wave_lds_fence();
     // A operand K: lane (li, lg) of step ks holds key kb*16 + li, dims ks*32 + lg*8 .. +7
     bf16x8 kf[2][4];
@@ -248,21 +259,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     float x[8];
     float tmax = -INFINITY;
+    if (tb + kTile <= kend && tb + kTile - 1 <= lim_all) {      // wave-uniform: no masking
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = tb + kb * 16 + lg * 4 + i;
-        x[kb * 4 + i] = key < kend && key <= key_lim ? sacc[kb][i] * xscale : -INFINITY;
-        tmax = fmaxf(tmax, x[kb * 4 + i]);
+      for (int e = 0; e < 8; ++e) {
+        x[e] = sacc[e / 4][e % 4] * xscale;
+        tmax = fmaxf(tmax, x[e]);
       }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = tb + kb * 16 + lg * 4 + i;
+          x[kb * 4 + i] = key < kend && key <= key_lim ? sacc[kb][i] * xscale : -INFINITY;
+          tmax = fmaxf(tmax, x[kb * 4 + i]);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    // -inf while a draft column has seen no key of its causal range yet: exponents then
-    // take offset 0 (every term is exp2(-inf) = 0), never -inf - -inf
-    const float m_off = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_off);
+    // Lazy rescale: the reference m_run moves only when some column's tile max exceeds it
+    // by more than 8 (log2 units); otherwise the tile's terms are taken against the old
+    // reference (each at most 2^8) and O needs no rescaling.  (m, l, o) stay consistent
+    // for the combine, whatever the reference.
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, tmax);
+      // -inf while a draft column has seen no key of its causal range yet: offset 0 then
+      // (every term is exp2(-inf) = 0), never -inf - -inf
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+      m_run = m_new;
+      // rescale O rows: lane's O rows are columns lg*4+i; their alpha lives in lane lg*4+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ah = __shfl(alpha, lg * 4 + i, kWave);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ah;
+      }
+    }
+    const float m_off = m_run == -INFINITY ? 0.f : m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -271,21 +305,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    // rescale O rows: lane's O rows are columns lg*4+i; their alpha lives in lane lg*4+i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ah = __shfl(alpha, lg * 4 + i, kWave);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ah;
-    }
+    l_run += lsum;
     // P as the A operand: row = column li, k-slot j <-> key (j/4)*16 + lg*4 + j%4
     uint4 pu;
-    pu.x = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
-    pu.y = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
-    pu.z = f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16);
-    pu.w = f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16);
+    pu.x = pack_bf16(x[0], x[1]);
+    pu.y = pack_bf16(x[2], x[3]);
+    pu.z = pack_bf16(x[4], x[5]);
+    pu.w = pack_bf16(x[6], x[7]);
     const bf16x8 pa = as_bf16x8(pu);
     // O += P V: B operand = V[keys][dims nb*16 .. +15] read transposed
     const int krow = lg * 4 + li / 4;
