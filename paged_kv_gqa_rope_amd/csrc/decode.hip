@@ -275,8 +275,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           tmax = fmaxf(tmax, x[kb * 4 + i]);
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    tmax = xor_max<32>(xor_max<16>(tmax));
     // Lazy rescale: the reference m_run moves only when some column's tile max exceeds it
     // by more than 8 (log2 units); otherwise the tile's terms are taken against the old
     // reference (each at most 2^8) and O needs no rescaling.  (m, l, o) stay consistent
@@ -303,8 +302,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       x[e] = __builtin_amdgcn_exp2f(x[e] - m_off);
       lsum += x[e];
     }
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
+    lsum = xor_sum<32>(xor_sum<16>(lsum));
     l_run += lsum;
     // P as the A operand: row = column li, k-slot j <-> key (j/4)*16 + lg*4 + j%4
     uint4 pu;

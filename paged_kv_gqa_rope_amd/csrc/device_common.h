@@ -123,6 +123,35 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
   return v;
 }
 
+// Combine each lane with lane l ^ 16 (ROWS = 16) or l ^ 32 (ROWS = 32) through the VALU
+// lane swaps of gfx950 (no LDS round trip); both lanes of a pair get op(x_l, x_partner).
+template <int ROWS>
+__device__ __forceinline__ void lane_swap(float v, float& a, float& b) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (ROWS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    static_assert(ROWS == 32, "row pairs of 16 or 32 lanes");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+template <int ROWS>
+__device__ __forceinline__ float xor_max(float v) {
+  float a, b;
+  lane_swap<ROWS>(v, a, b);
+  return fmaxf(a, b);
+}
+template <int ROWS>
+__device__ __forceinline__ float xor_sum(float v) {
+  float a, b;
+  lane_swap<ROWS>(v, a, b);
+  return a + b;
+}
+
 // Sum of len[0 .. r-1] over one wave (every lane gets the result).
 __device__ __forceinline__ int64_t wave_prefix(const int32_t* __restrict__ len, int r) {
   int64_t s = 0;

@@ -36,9 +36,8 @@ struct BatchPlan {
 
 // Numeric limits of the split policy.
 constexpr int32_t kMaxSplits = 128;       // splits per generation request
-constexpr int32_t kDefaultChunk = 1024;    // keys per split before balancing
-constexpr int64_t kTargetDecodeItems = 4096; // (request, kv head, split) items to aim for
-constexpr int64_t kMinChunkBytes = 256 << 10;  // one KV head's K and V per split, at least
+constexpr int32_t kMaxChunk = 4096;        // keys per split, at most
+constexpr int64_t kMinDecodeItems = 1408;  // (request, kv head, split) items, at least: 5.5 per CU
 // Generation requests carry 1 .. kMaxGenTokens new tokens (a token and its draft tokens).
 constexpr int32_t kMaxGenTokens = 64;
 // The split pass takes (token, query head) columns of one KV head in blocks of 16; with

@@ -69,24 +69,41 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-__device__ __forceinline__ const lds_u32x4* lds_at(uint32_t byte) {
-  return reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(byte));
-}
-
 // ds_read_b64_tr_b16 issued as inline asm: the compiler would otherwise wait for every
 // outstanding global-to-LDS tile load before it (it cannot tell the stages apart).  The
-// results are only valid after lds_wait() has been passed them.
+// results are only valid after an lgkm wait has been passed them.
 template <int OFF>
 __device__ __forceinline__ s16x4 tr_read(uint32_t addr) {
   s16x4 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
-// wait for all LDS reads of this wave; the operands tie the values read to the wait
-__device__ __forceinline__ void lds_wait(s16x4& a0, s16x4& a1, s16x4& a2, s16x4& a3, s16x4& a4, s16x4& a5,
-                                         s16x4& a6, s16x4& a7) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
+template <int N>
+__device__ __forceinline__ void lgkm_wait2(s16x4& v0, s16x4& v1) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v0), "+v"(v1) : "i"(N));
+}
+// ds_read_b128 issued as inline asm (same reason as tr_read)
+template <int OFF>
+__device__ __forceinline__ u32x4 k_read(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// wait until at most N LDS operations of this wave are outstanding; the operands tie the
+// values of the reads that must have completed to the wait
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& k0, u32x4& k1) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0), "+v"(k1) : "i"(N));
+}
+template <int I>
+using ic = std::integral_constant<int, I>;
+// f(ic<I>()) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>());
+    static_for<B + 1, E>(f);
+  }
 }
 
 // BT: a cache block holds a whole number of 64-key tiles (tokens_per_block >= 64), so a
@@ -266,22 +283,22 @@ void prefill_kernel(AttnArgs a) {
     f32x16 s[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
-    auto kread = [&](int kb, int ks) __attribute__((always_inline)) {
-      return as_bf16x8(*lds_at(ka_[ks] + kb * 32 * kRowBytes));
+    constexpr int RA = 3;                    // steps of K operands in flight ahead of the MFMAs
+    u32x4 kr[RA + 1][2];
+    auto kread = [&](auto KSc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KSc)::value;
+      kr[ks % (RA + 1)][0] = k_read<0>(ka_[ks]);
+      kr[ks % (RA + 1)][1] = k_read<32 * kRowBytes>(ka_[ks]);
     };
-    bf16x8 ka = kread(0, 0), kc = kread(1, 0);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 na = ka, nc = kc;
-      if (ks < 7) {
-        na = kread(0, ks + 1);
-        nc = kread(1, ks + 1);
-      }
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s[1], 0, 0, 0);
-      ka = na;
-      kc = nc;
-    }
+    static_for<0, RA>([&](auto KSc) __attribute__((always_inline)) { kread(KSc); });
+    static_for<0, 8>([&](auto KSc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KSc)::value;
+      if constexpr (ks + RA < 8) kread(ic<ks + RA>());
+      auto& x = kr[ks % (RA + 1)];
+      lgkm_wait<2 * (ks + RA < 8 ? RA : 7 - ks)>(x[0], x[1]);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[0]), qf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[1]), qf[ks], s[1], 0, 0, 0);
+    });
     // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
     if (kb0 + kTileK - 1 > past + q0) {
       const int lim = my_pos - kb0 - lh * 4;                 // key offset kb*32+(i/4)*8+i%4 <= lim
@@ -291,12 +308,20 @@ void prefill_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) s[kb][i] = (kb * 32 + (i / 4) * 8 + (i % 4) <= lim) ? s[kb][i] : -INFINITY;
     }
     // ---- online softmax (raw-score domain; exp2 of (s - m) * c)
-    float tmax = -INFINITY;
+    // row max: four independent chains over the lane's 32 scores, then across the lane
+    // halves (lanes l and l^32 hold the same query) with a VALU lane swap
+    float m4[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int k = 0; k < 4; ++k) {
+      m4[k] = s[k / 2][(k % 2) * 8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      for (int j = 1; j < 8; ++j) m4[k] = fmaxf(m4[k], s[k / 2][(k % 2) * 8 + j]);
+    }
+    float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     // Lazy rescaling: the running maximum used as the exponent offset only moves when a
     // score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough in
     // fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first tile
@@ -314,6 +339,7 @@ void prefill_kernel(AttnArgs a) {
     const float mc = m_run * c;
     // P^T as four B operands (16 keys each): slot j of step ks2 is s[ks2/2][(ks2%2)*8 + j]
     bf16x8 pb[4];
+    float l4[4];                             // partial row sums, one per B operand
 #pragma unroll
     for (int ks2 = 0; ks2 < 4; ++ks2) {
       const int kb = ks2 / 2, i0 = (ks2 % 2) * 8;
@@ -325,46 +351,36 @@ void prefill_kernel(AttnArgs a) {
       // The row sum takes the same bf16-rounded P that enters the product, two keys per
       // dot2.  Its operands are the scalar words: fed lanes of the packed vector, hipcc
       // emitted v_dot2c_f32_bf16 on the vector's first register four times.
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, l_run, false);
+      float l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, 0.f, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, l, false);
+      l4[ks2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, l, false);
       pb[ks2] = as_bf16x8(u32x4{w0, w1, w2, w3});
     }
-    // ---- O^T += V^T P^T over four 16-key steps; the V^T operands of step ks2+1 are read
-    //      while the MFMAs of step ks2 run
+    l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    // ---- O^T += V^T P^T: 16 MFMAs (step ks2 = R/4 of 16 keys, dim block b = R%4), the
+    //      V^T operands of each read RV MFMAs ahead
     uint32_t va_[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) va_[b] = sbase + vrd[b];
-    s16x4 vr[2][8];
-    auto vread = [&](auto KS2, s16x4* d) __attribute__((always_inline)) {
-      constexpr int base = decltype(KS2)::value * 16 * kRowBytes;
-      d[0] = tr_read<base>(va_[0]);
-      d[1] = tr_read<base + 8 * kRowBytes>(va_[0]);
-      d[2] = tr_read<base>(va_[1]);
-      d[3] = tr_read<base + 8 * kRowBytes>(va_[1]);
-      d[4] = tr_read<base>(va_[2]);
-      d[5] = tr_read<base + 8 * kRowBytes>(va_[2]);
-      d[6] = tr_read<base>(va_[3]);
-      d[7] = tr_read<base + 8 * kRowBytes>(va_[3]);
-      lds_wait(d[0], d[1], d[2], d[3], d[4], d[5], d[6], d[7]);
+    constexpr int RV = 4;
+    s16x4 vr[RV + 1][2];
+    auto vread = [&](auto Rc) __attribute__((always_inline)) {
+      constexpr int R = decltype(Rc)::value;
+      constexpr int base = (R / 4) * 16 * kRowBytes;
+      vr[R % (RV + 1)][0] = tr_read<base>(va_[R % 4]);
+      vr[R % (RV + 1)][1] = tr_read<base + 8 * kRowBytes>(va_[R % 4]);
     };
-    auto pv = [&](int ks2, const s16x4* d) __attribute__((always_inline)) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const u32x4 u = {__builtin_bit_cast(uint2, d[2 * b]).x, __builtin_bit_cast(uint2, d[2 * b]).y,
-                         __builtin_bit_cast(uint2, d[2 * b + 1]).x, __builtin_bit_cast(uint2, d[2 * b + 1]).y};
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[ks2], o[b], 0, 0, 0);
-      }
-    };
-    vread(std::integral_constant<int, 0>(), vr[0]);
-    vread(std::integral_constant<int, 1>(), vr[1]);
-    pv(0, vr[0]);
-    vread(std::integral_constant<int, 2>(), vr[0]);
-    pv(1, vr[1]);
-    vread(std::integral_constant<int, 3>(), vr[1]);
-    pv(2, vr[0]);
-    pv(3, vr[1]);
+    static_for<0, RV>([&](auto Rc) __attribute__((always_inline)) { vread(Rc); });
+    static_for<0, 16>([&](auto Rc) __attribute__((always_inline)) {
+      constexpr int R = decltype(Rc)::value;
+      if constexpr (R + RV < 16) vread(ic<R + RV>());
+      auto& d = vr[R % (RV + 1)];
+      lgkm_wait2<2 * (R + RV < 16 ? RV : 15 - R)>(d[0], d[1]);
+      const u32x4 u = {__builtin_bit_cast(uint2, d[0]).x, __builtin_bit_cast(uint2, d[0]).y,
+                       __builtin_bit_cast(uint2, d[1]).x, __builtin_bit_cast(uint2, d[1]).y};
+      o[R % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[R / 4], o[R % 4], 0, 0, 0);
+    });
   };
 
   // ---- the ring: tile t lives in stage t % NS.  Iteration t waits for this wave's loads of
