@@ -4,7 +4,8 @@
  * One step of one attention layer over an in-flight batch:
  *   1. pkv_append_rope: rotate the new tokens' q and k (RoPE), write the
  *      rotated q to q_out and scatter the rotated k and the raw v into the paged
- *      KV pool through the per-request block table;
+ *      KV pool through the per-request block table (pkv_append_qknorm_rope: the
+ *      same with each q and k head normalised first);
  *   2. pkv_attention_forward: causal attention for context-phase rows and for
  *      generation-phase rows (one token, or a token and its draft tokens), reading
  *      K/V through the block table.
@@ -207,6 +208,50 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch,
                         const void* k, const void* v, int64_t kv_row_stride,
                         const double* rope_cos_sin, int32_t rope_max_pos,
                         void* q_out, void* kv_pool, void* stream);
+
+/* kinds of per-head q/k normalisation (see pkv_append_qknorm_rope) */
+enum { PKV_NORM_NONE = 0, PKV_NORM_RMS = 1, PKV_NORM_LAYER = 2 };
+
+/*
+ * Per-head normalisation of queries and keys before the rotation.  [REPORT] 1.1 lists
+ * "QK LayerNorm" (layer normalisation of the queries and keys) among the attention
+ * features; [TEARDOWN]'s listing of the kernel directory names a fused QK-norm + RoPE
+ * kernel next to grouped RMSNorm kernels.  Over the D elements x_j of one q head or one
+ * new k head, in fp64, in this order, sums in index order j = 0 .. D-1, no fused
+ * multiply-add:
+ *   PKV_NORM_RMS  : mu = 0;                 PKV_NORM_LAYER: mu = (sum_j x_j) / D;
+ *   d_j = x_j - mu,  var = (sum_j d_j * d_j) / D,  inv = 1 / sqrt(var + eps),
+ *   y_j = (d_j * inv) * w_j          (RMS)      y_j = (d_j * inv) * w_j + b_j   (LAYER).
+ *   kind             : PKV_NORM_RMS or PKV_NORM_LAYER (PKV_NORM_NONE: no normalisation).
+ *   eps              : finite, >= 0.
+ *   q_weight, k_weight : device fp32 [head_dim], 16-byte aligned, one vector for all query
+ *                      heads and one for all key heads; q_weight may be NULL when q is.
+ *   q_bias, k_bias   : device fp32 [head_dim], 16-byte aligned; PKV_NORM_LAYER only
+ *                      (NULL means zero).
+ */
+typedef struct pkv_qk_norm {
+  int32_t kind;
+  float eps;
+  const float* q_weight;
+  const float* k_weight;
+  const float* q_bias;
+  const float* k_bias;
+} pkv_qk_norm;
+
+/*
+ * pkv_append_rope with each q head and each new k head normalised first: y as defined
+ * for pkv_qk_norm replaces x in the rotation (and in the dimensions past rotary_dim), and
+ * the stored value is y rotated and rounded once.  v is stored as given.  norm == NULL or
+ * kind PKV_NORM_NONE is exactly pkv_append_rope.  Arguments and errors as for
+ * pkv_append_rope; additionally PKV_ERR_INVALID_ARG for an unknown kind, a negative or
+ * non-finite eps or a missing or misaligned weight, and PKV_ERR_UNSUPPORTED when
+ * num_heads + num_kv_heads > 256.
+ */
+int32_t pkv_append_qknorm_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_qk_norm* norm,
+                               const void* q, int64_t q_row_stride,
+                               const void* k, const void* v, int64_t kv_row_stride,
+                               const double* rope_cos_sin, int32_t rope_max_pos,
+                               void* q_out, void* kv_pool, void* stream);
 
 /*
  * Attention over the paged cache ([NOTES] 六.6.1-6.3; [TEARDOWN] AttentionBackend.forward).

@@ -26,7 +26,8 @@ Sources, by page (all pages are secondary descriptions of TensorRT-LLM):
   layout [num_blocks, 2, tokens_per_block, num_kv_heads, head_dim] and the
   per-request block ID table), the AttentionMetadata fields and the
   AttentionBackend.forward signature (packed q [num_tokens, num_heads*head_dim]
-  and k, v [num_tokens, num_kv_heads*head_dim]).
+  and k, v [num_tokens, num_kv_heads*head_dim]), and the kernel directory
+  listing (a fused QK-norm + RoPE kernel).
 
 No page writes down the formula of attention, RoPE, the GQA mapping or the
 fp8 encoding; the readings taken here are listed in each function.
@@ -36,4 +37,4 @@ Parity status per function: every public function is pinned by tests in
 invariants, library special cases, exhaustive codec enumeration and a
 pure-Python brute force); none is "parity unpinned".
 """
-from . import codecs, rope, attention, step  # noqa: F401
+from . import codecs, rope, qknorm, attention, step  # noqa: F401

@@ -10,7 +10,8 @@ The step (from the pages' description of the problem):
    token, or 1 + k draft tokens to verify (report, section 1.4: generation
    lengths and position offsets); read as one chain, token i at position
    p_r + i, so the drafts are causal among themselves like a chunk;
-2. append -- rotate the new q and k at their absolute positions p_r + i
+2. append -- optionally normalise each head of the new q and k (see
+   ``qknorm``), rotate them at their absolute positions p_r + i
    (RoPE, see ``rope``), round q to the io format (q_out), store the rotated k
    and the raw v in the cache format (see ``codecs``) at cache positions
    p_r .. S_r - 1 (study notes, section "KVCacheManager": the attention op
@@ -35,6 +36,7 @@ import numpy as np
 
 from . import codecs
 from .attention import attend
+from .qknorm import qk_norm
 from .rope import neox_tables, rope_apply
 
 
@@ -65,6 +67,11 @@ def append_request(batch, r: int, tabs, rope: bool = True):
     if rope:
         cos_t, sin_t = tabs
         q = io_decode(batch, batch.new_q(r))
+        if sh.qk_norm != "none":
+            prm = batch.norm_params()
+            eps = float(np.float32(sh.norm_eps))
+            q = qk_norm(q, sh.qk_norm, prm["q_weight"], prm["q_bias"], eps)
+            k = qk_norm(k, sh.qk_norm, prm["k_weight"], prm["k_bias"], eps)
         q_out = codecs.encode(rope_apply(sh.rope_style, q, pos, cos_t, sin_t, sh.rot_dim), sh.io_dtype)
         k = rope_apply(sh.rope_style, k, pos, cos_t, sin_t, sh.rot_dim)
     k_store = codecs.encode(k, sh.kv_dtype, sh.k_scale)

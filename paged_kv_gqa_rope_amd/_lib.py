@@ -26,6 +26,7 @@ PKV_ERR_HIP = -8
 PKV_FP32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
 PKV_REQ_CONTEXT, PKV_REQ_GENERATION = 0, 1
 PKV_ROPE_NONE, PKV_ROPE_NEOX, PKV_ROPE_GPTJ = 0, 1, 2
+PKV_NORM_NONE, PKV_NORM_RMS, PKV_NORM_LAYER = 0, 1, 2
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -64,6 +65,17 @@ class pkv_batch_desc(ctypes.Structure):
     ]
 
 
+class pkv_qk_norm(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("q_weight", ctypes.c_void_p),
+        ("k_weight", ctypes.c_void_p),
+        ("q_bias", ctypes.c_void_p),
+        ("k_bias", ctypes.c_void_p),
+    ]
+
+
 class PkvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"pkv status {status}: {message}")
@@ -92,6 +104,9 @@ def lib() -> ctypes.CDLL:
         L.pkv_rope_cos_sin.restype = i32
         L.pkv_append_rope.argtypes = [D, Bt, vp, i64, vp, vp, i64, vp, i32, vp, vp, vp]
         L.pkv_append_rope.restype = i32
+        L.pkv_append_qknorm_rope.argtypes = [D, Bt, ctypes.POINTER(pkv_qk_norm), vp, i64, vp, vp, i64, vp, i32,
+                                             vp, vp, vp]
+        L.pkv_append_qknorm_rope.restype = i32
         L.pkv_attention_forward.argtypes = [D, Bt, vp, i64, vp, vp, vp, sz, vp]
         L.pkv_attention_forward.restype = i32
         L.pkv_kernel_timing_enable.argtypes = [i32]
@@ -132,6 +147,13 @@ def pkv_append_rope(desc, batch, q, q_row_stride, k, v, kv_row_stride, rope_cos_
                     q_out, kv_pool, stream) -> int:
     return lib().pkv_append_rope(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, k, v, kv_row_stride,
                                  rope_cos_sin, rope_max_pos, q_out, kv_pool, stream)
+
+
+def pkv_append_qknorm_rope(desc, batch, norm, q, q_row_stride, k, v, kv_row_stride, rope_cos_sin, rope_max_pos,
+                           q_out, kv_pool, stream) -> int:
+    return lib().pkv_append_qknorm_rope(ctypes.byref(desc), ctypes.byref(batch),
+                                        ctypes.byref(norm) if norm is not None else None, q, q_row_stride, k, v,
+                                        kv_row_stride, rope_cos_sin, rope_max_pos, q_out, kv_pool, stream)
 
 
 def pkv_attention_forward(desc, batch, q, q_row_stride, kv_pool, out, workspace, workspace_bytes, stream) -> int:

@@ -125,9 +125,10 @@ int32_t pkv_rope_cos_sin(double base, int32_t rotary_dim, int32_t max_pos, doubl
   return PKV_OK;
 }
 
-int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q, int64_t q_row_stride,
-                        const void* k, const void* v, int64_t kv_row_stride, const double* rope_cos_sin,
-                        int32_t rope_max_pos, void* q_out, void* kv_pool, void* stream) {
+static int32_t append_impl(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_qk_norm* norm,
+                           const void* q, int64_t q_row_stride, const void* k, const void* v, int64_t kv_row_stride,
+                           const double* rope_cos_sin, int32_t rope_max_pos, void* q_out, void* kv_pool,
+                           void* stream) {
   std::string err;
   int rc = pkv::validate_desc(desc, err);
   if (rc != PKV_OK) return set_err(rc, err);
@@ -151,6 +152,20 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, 
     if (rope_max_pos < plan.max_S)
       return set_err(PKV_ERR_INVALID_ARG, "rope_max_pos=" + std::to_string(rope_max_pos) +
                                               " does not cover position " + std::to_string(plan.max_S - 1));
+  }
+  const int32_t nkind = norm ? norm->kind : PKV_NORM_NONE;
+  if (nkind != PKV_NORM_NONE) {
+    if (nkind != PKV_NORM_RMS && nkind != PKV_NORM_LAYER)
+      return set_err(PKV_ERR_INVALID_ARG, "unknown qk norm kind " + std::to_string(nkind));
+    if (!(norm->eps >= 0.f) || !std::isfinite(norm->eps))
+      return set_err(PKV_ERR_INVALID_ARG, "qk norm eps must be finite and >= 0");
+    if (!norm->k_weight || !aligned16(norm->k_weight) || (q && (!norm->q_weight || !aligned16(norm->q_weight))))
+      return set_err(PKV_ERR_INVALID_ARG, "qk norm weights missing or not 16-byte aligned");
+    if (nkind == PKV_NORM_LAYER && ((norm->q_bias && !aligned16(norm->q_bias)) || (norm->k_bias && !aligned16(norm->k_bias))))
+      return set_err(PKV_ERR_INVALID_ARG, "qk norm biases must be 16-byte aligned");
+    if ((q ? H : 0) + Hkv > pkv::kMaxNormHeads)
+      return set_err(PKV_ERR_UNSUPPORTED, "qk norm supports at most " + std::to_string(pkv::kMaxNormHeads) +
+                                              " q + k heads per token");
   }
   pkv::AppendArgs a{};
   a.q = q;
@@ -182,10 +197,33 @@ int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, 
   a.rope = desc->rope_style == PKV_ROPE_NEOX ? pkv::kRopeNeox
            : desc->rope_style == PKV_ROPE_GPTJ ? pkv::kRopeGptj : pkv::kRopeNone;
   a.max_n = plan.max_n;
+  a.norm = nkind == PKV_NORM_RMS ? pkv::kNormRms : nkind == PKV_NORM_LAYER ? pkv::kNormLayer : pkv::kNormNone;
+  if (a.norm != pkv::kNormNone) {
+    a.norm_eps = static_cast<double>(norm->eps);
+    a.qn_w = norm->q_weight;
+    a.kn_w = norm->k_weight;
+    a.qn_b = a.norm == pkv::kNormLayer ? norm->q_bias : nullptr;
+    a.kn_b = a.norm == pkv::kNormLayer ? norm->k_bias : nullptr;
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = timed("append_rope", s, [&] { return pkv::launch_append(a, s); });
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return PKV_OK;
+}
+
+int32_t pkv_append_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q, int64_t q_row_stride,
+                        const void* k, const void* v, int64_t kv_row_stride, const double* rope_cos_sin,
+                        int32_t rope_max_pos, void* q_out, void* kv_pool, void* stream) {
+  return append_impl(desc, batch, nullptr, q, q_row_stride, k, v, kv_row_stride, rope_cos_sin, rope_max_pos, q_out,
+                     kv_pool, stream);
+}
+
+int32_t pkv_append_qknorm_rope(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_qk_norm* norm,
+                               const void* q, int64_t q_row_stride, const void* k, const void* v,
+                               int64_t kv_row_stride, const double* rope_cos_sin, int32_t rope_max_pos,
+                               void* q_out, void* kv_pool, void* stream) {
+  return append_impl(desc, batch, norm, q, q_row_stride, k, v, kv_row_stride, rope_cos_sin, rope_max_pos, q_out,
+                     kv_pool, stream);
 }
 
 int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,

@@ -11,7 +11,10 @@
 // the (head, 8-element group) tasks of those tokens over its 256 threads, so every
 // load and store is a 16-byte access and neighbouring lanes touch neighbouring bytes.
 // Arithmetic is fp64 with contraction off and one rounding per stored element, so the
-// stored bits depend only on the inputs and the table.
+// stored bits depend only on the inputs and the table.  With a per-head q/k norm
+// ("TensorRT-LLM source analysis report", 1.1, QK LayerNorm; the teardown's kernel
+// directory lists a fused QK-norm + RoPE kernel), a pre-pass computes each head's mean
+// and inverse deviation into LDS and the tasks normalise their elements before rotating.
 #include <type_traits>
 
 #include "device_common.h"
@@ -116,6 +119,27 @@ __device__ __forceinline__ void rotate8(const double (&x1)[8], const double (&x2
   }
 }
 
+// Per-head normalisation of 8 elements at dims dim0 .. dim0+7 of one q or k head:
+// y = ((x - mean) * inv) * w (+ b), fp64, with (mean, inv) of the head from the pre-pass.
+__device__ __forceinline__ void norm8(double (&x)[8], int dim0, double2 st, const float* __restrict__ w,
+                                      const float* __restrict__ b) {
+#pragma clang fp contract(off)
+  const float4 w0 = *reinterpret_cast<const float4*>(w + dim0), w1 = *reinterpret_cast<const float4*>(w + dim0 + 4);
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (b) {
+    const float4 b0 = *reinterpret_cast<const float4*>(b + dim0), b1 = *reinterpret_cast<const float4*>(b + dim0 + 4);
+    bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
+    bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double d = x[i] - st.x;
+    const double y = (d * st.y) * static_cast<double>(wv[i]);
+    x[i] = b ? y + static_cast<double>(bv[i]) : y;
+  }
+}
+
 // Where one token goes: its packed row, request, absolute position and pool slot.
 struct TokenSlot {
   int64_t row;
@@ -131,11 +155,12 @@ constexpr int kHeadsPerRotTask = 4;
 // group of 8 pairs for up to kHeadsPerRotTask q/k heads, so the table slice is read
 // once for all of them), pass-through groups of 8 dims past the rotary part, and
 // groups of 8 v dims.  A task's loads are all issued before its arithmetic.
-template <int IO, int KV, int RS>
+template <int IO, int KV, int RS, bool NORM>
 __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot& tk, int t, int Hq,
                                             const void* __restrict__ q, const void* __restrict__ k,
                                             const void* __restrict__ v, const double* __restrict__ cs_base,
-                                            void* __restrict__ q_out, void* __restrict__ pool) {
+                                            void* __restrict__ q_out, void* __restrict__ pool,
+                                            const double2* __restrict__ stat) {
   const int R = RS != kRopeNone ? a.R : 0;
   const int half = R / 2;
   const int rg = R / 16, pg = (a.D - R) / 8, vg = a.D / 8;
@@ -148,6 +173,13 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
   auto pool_off = [&](int which, int g) {
     return ((static_cast<int64_t>(tk.blk) * 2 + which) * a.T + tk.slot) * static_cast<int64_t>(a.Hkv) * a.D +
            static_cast<int64_t>(g) * a.D;
+  };
+  // normalise a widened group of head `head` (NORM only); (mean, inv) come from stat[head]
+  auto normalise = [&](double (&x)[8], int head, int dim0) {
+    if constexpr (NORM) {
+      const bool isq = head < Hq;
+      norm8(x, dim0, stat[head], isq ? a.qn_w : a.kn_w, isq ? a.qn_b : a.kn_b);
+    }
   };
   auto head_src = [&](int head, const void*& src, int64_t& off) {
     const bool isq = head < Hq;
@@ -184,6 +216,8 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
         double e0[8], e1[8];
         widen8<IO>(r1[u], e0);
         widen8<IO>(r2[u], e1);
+        normalise(e0, head, off_a(j0));
+        normalise(e1, head, off_b(j0));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x1[i] = e0[2 * i];
@@ -194,6 +228,8 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
       } else {
         widen8<IO>(r1[u], x1);
         widen8<IO>(r2[u], x2);
+        normalise(x1, head, off_a(j0));
+        normalise(x2, head, off_b(j0));
       }
       rotate8(x1, x2, c, y1, y2);
       double s1[8], s2[8];                                // the two stored groups of 8
@@ -230,6 +266,7 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
     head_src(head, src, off);
     double x[8];
     load8<IO>(src, off + j, x);
+    normalise(x, head, j);
     if (head < Hq)
       store8<IO>(q_out, tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D + j, x, 1.0);
     else if (tk.blk >= 0)
@@ -259,7 +296,7 @@ __device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row,
 // and each workgroup finds the rows' requests through an LDS prefix scan of the
 // context lengths (batches of at most kFlatMaxRequests requests).  Otherwise the grid
 // is (row tile, request), for any batch size.
-template <int IO, int KV, int RS, bool FLAT>
+template <int IO, int KV, int RS, bool FLAT, bool NORM>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, int tokens_per_wg) {
   __shared__ int32_t s_cu[kFlatMaxRequests + 1];
   __shared__ TokenSlot s_tok[kMaxTokensPerWg];
@@ -314,6 +351,49 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
       s_tok[threadIdx.x] = make_slot(a, rowr + tok0 + threadIdx.x, r, tok0 + threadIdx.x);
   }
   __syncthreads();
+  // NORM: (mean, 1/sqrt(var + eps)) of every q and k head of the workgroup's tokens, one
+  // thread per (token, head), fp64 sums in index order (as the oracle and pkv.h state)
+  const double2* stat = nullptr;
+  if constexpr (NORM) {
+    __shared__ double2 s_stat[kMaxTokensPerWg * kMaxNormHeads];
+    const int nh = Hq + a.Hkv;
+    const bool layer = a.norm == kNormLayer;
+    for (int u = threadIdx.x; u < ntok * nh; u += kAppendThreads) {
+      const int it = u / nh, head = u - it * nh;
+      const TokenSlot tk = s_tok[it];
+      double mean = 0.0, inv = 0.0;
+      if (tk.row < a.N && tk.m >= 0) {
+        const bool isq = head < Hq;
+        const void* src = isq ? a.q : a.k;
+        const int64_t off = isq ? tk.row * a.q_stride + static_cast<int64_t>(head) * a.D
+                                : tk.row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
+        if (layer) {
+          double s = 0.0;
+          for (int j = 0; j < a.D; j += 8) {
+            double x[8];
+            load8<IO>(src, off + j, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s += x[i];
+          }
+          mean = s / static_cast<double>(a.D);
+        }
+        double ss = 0.0;
+        for (int j = 0; j < a.D; j += 8) {
+          double x[8];
+          load8<IO>(src, off + j, x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const double d = x[i] - mean;
+            ss += d * d;
+          }
+        }
+        inv = 1.0 / __builtin_sqrt(ss / static_cast<double>(a.D) + a.norm_eps);
+      }
+      s_stat[u] = make_double2(mean, inv);
+    }
+    __syncthreads();
+    stat = s_stat;
+  }
   const int R = RS != kRopeNone ? a.R : 0;
   const int per_tok = ((Hq + a.Hkv + kHeadsPerRotTask - 1) / kHeadsPerRotTask) * (R / 16) +
                       (Hq + a.Hkv) * ((a.D - R) / 8) + a.Hkv * (a.D / 8);
@@ -328,7 +408,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
     const int it = task / per_tok;
     const TokenSlot tk = s_tok[it];
     if (tk.row >= a.N || tk.m < 0) continue;
-    append_task<IO, KV, RS>(a, tk, task - it * per_tok, Hq, q, k, v, cs, q_out, pool);
+    append_task<IO, KV, RS, NORM>(a, tk, task - it * per_tok, Hq, q, k, v, cs, q_out, pool,
+                                  NORM ? stat + it * (Hq + a.Hkv) : nullptr);
   }
 }
 
@@ -352,15 +433,20 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
   // enough workgroups to fill the chip: about N / 512 tokens each, at most 8
   int64_t want = a.N / 512;
   const int tpw = static_cast<int>(want < 1 ? 1 : want > kMaxTokensPerWg ? kMaxTokensPerWg : want);
-  auto go = [&](auto rs) {
+  auto go2 = [&](auto rs, auto nrm) {
     constexpr int RS = decltype(rs)::value;
+    constexpr bool NORM = decltype(nrm)::value;
     if (a.B <= kFlatMaxRequests) {
       const dim3 grid(static_cast<unsigned>((a.N + tpw - 1) / tpw));
-      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true, NORM>), grid, dim3(kAppendThreads), 0, s, a, tpw);
     } else {
       const dim3 grid((a.max_n + tpw - 1) / tpw, a.B);
-      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false, NORM>), grid, dim3(kAppendThreads), 0, s, a, tpw);
     }
+  };
+  auto go = [&](auto rs) {
+    if (a.norm != kNormNone) go2(rs, std::true_type());
+    else go2(rs, std::false_type());
   };
   if (a.rope == kRopeNeox) go(std::integral_constant<int, kRopeNeox>());
   else if (a.rope == kRopeGptj) go(std::integral_constant<int, kRopeGptj>());

@@ -10,6 +10,9 @@ namespace pkv {
 enum : int { F_FP32 = 0, F_BF16 = 1, F_FP8 = 2, F_INT8 = 3 };
 // rotary pairing of the append: none, (j, j + R/2), (2j, 2j + 1)
 enum : int { kRopeNone = 0, kRopeNeox = 1, kRopeGptj = 2 };
+// per-head normalisation of q and k in the append
+enum : int { kNormNone = 0, kNormRms = 1, kNormLayer = 2 };
+constexpr int kMaxNormHeads = 256;   // q heads + k heads per token with a norm
 
 struct AppendArgs {
   const void* q;            // may be null (then q_out is null)
@@ -28,6 +31,13 @@ struct AppendArgs {
   double inv_k_scale, inv_v_scale;   // fp8 / int8 cache: 1/scale; otherwise 1
   int32_t io_fmt, kv_fmt, rope;   // rope: kRopeNone / kRopeNeox / kRopeGptj
   int32_t max_n;            // largest n_r (grid extent)
+  // per-head q/k normalisation before the rotation
+  int32_t norm;             // kNormNone / kNormRms / kNormLayer
+  double norm_eps;
+  const float* qn_w;        // [D] weights for query heads (may be null without q)
+  const float* kn_w;        // [D] weights for key heads
+  const float* qn_b;        // [D] biases (layer form; may be null: zero)
+  const float* kn_b;
 };
 
 struct AttnArgs {

@@ -120,6 +120,19 @@ class PagedStep:
         self.rot = sh.rot_dim
         self.rope = torch.empty((self.max_pos, self.rot // 2, 2), dtype=torch.float64, device=self.device)
         L.check(L.pkv_rope_cos_sin(float(sh.rope_theta), self.rot, self.max_pos, self.rope.data_ptr(), self.stream))
+        self.norm = None
+        if getattr(sh, "qk_norm", "none") != "none":
+            prm = batch.norm_params()
+            self.norm_tensors = {n: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(self.device)
+                                 for n, a in prm.items()}
+            nrm = L.pkv_qk_norm()
+            nrm.kind = {"rms": L.PKV_NORM_RMS, "layer": L.PKV_NORM_LAYER}[sh.qk_norm]
+            nrm.eps = sh.norm_eps
+            nrm.q_weight = self.norm_tensors["q_weight"].data_ptr()
+            nrm.k_weight = self.norm_tensors["k_weight"].data_ptr()
+            nrm.q_bias = self.norm_tensors["q_bias"].data_ptr()
+            nrm.k_bias = self.norm_tensors["k_bias"].data_ptr()
+            self.norm = nrm
         self.ws_bytes = L.pkv_workspace_size_for_batch(self.desc, self.bdesc)
         self.ws = torch.empty((max(self.ws_bytes, 256),), dtype=torch.uint8, device=self.device)
         if fill_history:
@@ -151,7 +164,11 @@ class PagedStep:
             del k, v, lens
 
     def append(self) -> int:
-        sh = self.shape
+        if self.norm is not None:
+            return L.pkv_append_qknorm_rope(self.desc, self.bdesc, self.norm, self.q.data_ptr(), self.q.shape[1],
+                                            self.k.data_ptr(), self.v.data_ptr(), self.k.shape[1],
+                                            self.rope.data_ptr(), self.max_pos, self.q_out.data_ptr(),
+                                            self.pool.data_ptr(), self.stream)
         return L.pkv_append_rope(self.desc, self.bdesc, self.q.data_ptr(), self.q.shape[1], self.k.data_ptr(),
                                  self.v.data_ptr(), self.k.shape[1], self.rope.data_ptr(), self.max_pos,
                                  self.q_out.data_ptr(), self.pool.data_ptr(), self.stream)

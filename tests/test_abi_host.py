@@ -158,6 +158,29 @@ def test_unsupported_configurations():
     expect(L.PKV_ERR_UNSUPPORTED, forward(desc_for(), HostBatch([1], [65], [70], [[0, 1]], 2)))
 
 
+def test_qk_norm_arguments():
+    hb = ok_batch()
+    d = desc_for()
+
+    def call(kind=L.PKV_NORM_RMS, eps=1e-6, qw=P, kw=P, qb=None, kb=None, q=P, q_out=P, desc=d):
+        n = L.pkv_qk_norm()
+        n.kind, n.eps, n.q_weight, n.k_weight, n.q_bias, n.k_bias = kind, eps, qw, kw, qb, kb
+        qs, kvs = desc.num_heads * desc.head_dim, desc.num_kv_heads * desc.head_dim
+        return L.pkv_append_qknorm_rope(desc, hb.desc, n, q, qs, P, P, kvs, P, 10 ** 6, q_out, P, None)
+
+    expect(L.PKV_ERR_INVALID_ARG, call(kind=3))
+    expect(L.PKV_ERR_INVALID_ARG, call(eps=-1.0))
+    expect(L.PKV_ERR_INVALID_ARG, call(eps=float("inf")))
+    expect(L.PKV_ERR_INVALID_ARG, call(kw=None))
+    expect(L.PKV_ERR_INVALID_ARG, call(qw=None))                       # q given without its weights
+    expect(L.PKV_ERR_INVALID_ARG, call(qw=P + 4))                      # misaligned
+    expect(L.PKV_ERR_INVALID_ARG, call(kind=L.PKV_NORM_LAYER, qb=P + 8))
+    # 256 + 32 heads exceed the per-token limit of the norm pre-pass
+    expect(L.PKV_ERR_UNSUPPORTED, call(desc=desc_for(num_heads=256, num_kv_heads=32)))
+    # the same arguments are rejected by the shared validation first
+    expect(L.PKV_ERR_INVALID_ARG, call(q_out=None))
+
+
 def test_empty_batch_is_a_no_op():
     hb = HostBatch([], [], [], np.zeros((0, 1)), 1)
     assert append(desc_for(), hb, q=None, q_out=None, k=None, v=None, pool=None) == L.PKV_OK

@@ -91,6 +91,37 @@ def test_interleaved_rope_append_and_attention(H, k, rot):
     print(b.label, "gptj", rot, stats)
 
 
+QKNORM_CASES = [
+    # (workload shape, norm, rope style, rotary_dim, kv dtype)
+    (1, "rms", "neox", 0, None),            # fp32 io and cache
+    (1, "layer", "gptj", 32, None),         # interleaved pairs on half the head
+    (3, "rms", "neox", 0, None),            # bf16, GQA-4
+    (3, "layer", "neox", 64, None),         # partial rotary: normalised pass-through dims
+    (4, "layer", "gptj", 0, None),          # GQA-8, chunks on cached prefixes, generation rows
+    (5, "rms", "neox", 0, None),            # fp8 cache
+    (5, "layer", "neox", 0, "int8"),        # int8 cache
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(QKNORM_CASES)))
+def test_qk_norm_append_and_attention(H, case_i):
+    """Per-head q/k normalisation before RoPE: q_out and the whole pool bit-exact,
+    attention within the bars."""
+    k, kind, style, rot, kv = QKNORM_CASES[case_i]
+    sh = dataclasses.replace(W.SHAPES[k], qk_norm=kind, rope_style=style, rotary_dim=rot, norm_eps=1e-5)
+    if kv == "int8":
+        sh = dataclasses.replace(sh, kv_dtype=W.INT8, k_scale=2.0 ** -5, v_scale=2.0 ** -5)
+    b = W.small_workload(k, shape=sh)
+    case("qk norm", b.label, sh.name, kind, style, rot, sh.kv_dtype)
+    st = run_step(H, b)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(sh.kv_dtype)), "pool")
+    stats = compare_attention(st.out_host(), O.run(b)["out"], sh, b.label)
+    print(b.label, kind, style, rot, stats)
+
+
 SPEC_CASES = [
     # (shape, cached lengths, new tokens per generation request, context requests)
     (2, [70, 300, 5], [2, 4, 7], []),                         # MHA: up to 7 x 1 columns

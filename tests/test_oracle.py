@@ -458,3 +458,103 @@ def test_small_workload_runs_and_rows_are_convex_combinations():
                 g = h // G
                 assert np.all(o[:, h] <= V[:, g].max(axis=0) + 1e-12)
                 assert np.all(o[:, h] >= V[:, g].min(axis=0) - 1e-12)
+
+
+# ------------------------------------------------------------------ QK norm
+from oracle import qknorm as QN  # noqa: E402
+
+
+@pytest.mark.parametrize("D", [8, 64, 128])
+def test_qk_norm_closed_forms(D):
+    rng = np.random.default_rng(20 + D)
+    x = rng.standard_normal((5, 3, D)) * rng.uniform(0.1, 10.0, (5, 3, 1))
+    ones, zeros = np.ones(D), np.zeros(D)
+    y = QN.qk_norm(x, "rms", ones, None, 0.0)              # unit root mean square
+    assert np.max(np.abs(np.mean(y * y, axis=-1) - 1.0)) < 1e-14
+    y = QN.qk_norm(x, "layer", ones, zeros, 0.0)           # zero mean, unit variance
+    assert np.max(np.abs(np.mean(y, axis=-1))) < 1e-14
+    assert np.max(np.abs(np.mean(y * y, axis=-1) - 1.0)) < 1e-14
+    c = np.full((1, 1, D), 3.25)                           # a constant head: d = 0, y = bias
+    b = rng.standard_normal(D)
+    assert np.array_equal(QN.qk_norm(c, "layer", rng.standard_normal(D), b, 1e-6)[0, 0], b)
+    assert np.array_equal(QN.qk_norm(x, "none", ones, None, 0.0), x)
+
+
+def test_qk_norm_invariances():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((4, 2, 128))
+    w, b = rng.standard_normal(128), rng.standard_normal(128)
+    for kind in ("rms", "layer"):
+        ref = QN.qk_norm(x, kind, w, b, 0.0)
+        # a power-of-two scale changes every intermediate exactly: bitwise the same
+        assert np.array_equal(QN.qk_norm(x * 8.0, kind, w, b, 0.0), ref)
+        assert np.allclose(QN.qk_norm(x * 0.37, kind, w, b, 0.0), ref, rtol=0, atol=1e-12)
+    # layer form: shifting a head by a constant changes nothing
+    ref = QN.qk_norm(x, "layer", w, b, 0.0)
+    assert np.allclose(QN.qk_norm(x + 5.5, "layer", w, b, 0.0), ref, rtol=0, atol=1e-11)
+    # the rms form of a zero-mean head is the layer form without bias
+    xz = x - x.mean(axis=-1, keepdims=True)
+    assert np.allclose(QN.qk_norm(xz, "rms", w, None, 0.0), QN.qk_norm(xz, "layer", w, np.zeros(128), 0.0),
+                       rtol=0, atol=1e-13)
+
+
+def test_qk_norm_matches_torch_layer_norm_and_rms_norm():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((6, 4, 128))
+    w, b = rng.standard_normal(128), rng.standard_normal(128)
+    eps = 1e-5
+    tx, tw, tb = (torch.from_numpy(a) for a in (x, w, b))
+    ln = torch.nn.functional.layer_norm(tx, (128,), tw, tb, eps).numpy()
+    assert np.allclose(QN.qk_norm(x, "layer", w, b, eps), ln, rtol=0, atol=1e-12)
+    rms = torch.nn.functional.rms_norm(tx, (128,), tw, eps).numpy()
+    assert np.allclose(QN.qk_norm(x, "rms", w, None, eps), rms, rtol=0, atol=1e-12)
+
+
+def test_qk_norm_matches_pure_python_loops_bitwise():
+    rng = np.random.default_rng(51)
+    D = 16
+    x = rng.standard_normal((3, D))
+    w, b = rng.standard_normal(D), rng.standard_normal(D)
+    for kind in ("rms", "layer"):
+        got = QN.qk_norm(x, kind, w, b, 1e-3)
+        for row in range(3):
+            xs = [float(v) for v in x[row]]
+            mu = 0.0
+            if kind == "layer":
+                s = 0.0
+                for v in xs:
+                    s += v
+                mu = s / D
+            ss = 0.0
+            for v in xs:
+                ss += (v - mu) * (v - mu)
+            inv = 1.0 / math.sqrt(ss / D + 1e-3)
+            want = [(v - mu) * inv * float(w[j]) + (float(b[j]) if kind == "layer" else 0.0)
+                    for j, v in enumerate(xs)]
+            assert got[row].tolist() == want
+
+
+def test_step_normalises_q_and_k_before_rotating():
+    """A context request's first token sits at position 0 (the rotation is the identity),
+    so its stored q and k are the normalised inputs rounded once; at later positions they
+    are the rotation of the normalised inputs."""
+    torch = pytest.importorskip("torch")
+    sh = W.Shape("qkn", 4, 2, 64, 16, W.FP32, W.FP32, 1e4, qk_norm="layer", norm_eps=1e-5)
+    b = W.make_batch(sh, ctx=[(20, 0)], seed=77)
+    prm = b.norm_params()
+    eps = float(np.float32(sh.norm_eps))
+    q = b.new_q(0).astype(np.float64)
+    k = b.new_k(0).astype(np.float64)
+
+    def tnorm(x, w, bias):
+        return torch.nn.functional.layer_norm(torch.from_numpy(x), (64,), torch.from_numpy(w.astype(np.float64)),
+                                              torch.from_numpy(bias.astype(np.float64)), eps).numpy()
+    qn, kn = tnorm(q, prm["q_weight"], prm["q_bias"]), tnorm(k, prm["k_weight"], prm["k_bias"])
+    q_out, k_store, _ = S.append_request(b, 0, S.tables(b))
+    assert np.allclose(q_out[0].astype(np.float64), qn[0], rtol=2 ** -23, atol=1e-12)
+    assert np.allclose(k_store[0].astype(np.float64), kn[0], rtol=2 ** -23, atol=1e-12)
+    cos_t, sin_t = S.tables(b)
+    pos = np.arange(20)
+    assert np.allclose(q_out.astype(np.float64), R.rope_neox(qn, pos, cos_t, sin_t, 64), rtol=1e-6, atol=1e-6)
+    assert np.allclose(k_store.astype(np.float64), R.rope_neox(kn, pos, cos_t, sin_t, 64), rtol=1e-6, atol=1e-6)

@@ -32,7 +32,7 @@ import numpy as np
 FP32, BF16, FP8_E4M3, INT8 = "fp32", "bf16", "fp8_e4m3", "int8"
 CONTEXT, GENERATION = 0, 1
 
-_TAGS = {"lengths": 1, "blocks": 2, "q": 3, "k": 4, "v": 5, "hist_k": 6, "hist_v": 7}
+_TAGS = {"lengths": 1, "blocks": 2, "q": 3, "k": 4, "v": 5, "hist_k": 6, "hist_v": 7, "norm": 8}
 
 
 def _rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
@@ -55,6 +55,8 @@ class Shape:
     k_scale: float = 1.0         # fp8 / int8 cache only: real value = scale * stored value
     v_scale: float = 1.0
     max_num_tokens: int = 8192
+    qk_norm: str = "none"        # per-head norm of q and new k before RoPE: "none", "rms", "layer"
+    norm_eps: float = 1e-6       # float32 value handed to both sides
 
     @property
     def group(self) -> int:
@@ -131,6 +133,16 @@ class Batch:
 
     def hist_v(self, r: int) -> np.ndarray:
         return self._draw("hist_v", r, int(self.past_lengths[r]), self.shape.num_kv_heads)
+
+    def norm_params(self) -> dict:
+        """Synthetic per-dimension norm parameters, float32 [head_dim] each: weights
+        1 + N(0, 1)/4 and biases N(0, 1)/4 for q and for k (the biases apply to the
+        "layer" form only)."""
+        g = _rng(self.seed, "norm").standard_normal((4, self.shape.head_dim), dtype=np.float32)
+        one = np.float32(1.0)
+        quarter = np.float32(0.25)
+        return {"q_weight": one + quarter * g[0], "k_weight": one + quarter * g[1],
+                "q_bias": quarter * g[2], "k_bias": quarter * g[3]}
 
     def packed(self, which: str) -> np.ndarray:
         """Concatenate new_q / new_k / new_v over requests in packed row order."""
