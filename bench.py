@@ -66,7 +66,8 @@ def describe(batch) -> str:
             f"T={sh.tokens_per_block} io={sh.io_dtype} kv={sh.kv_dtype} rope_base={sh.rope_theta:g}"
             + (f" rope={sh.rope_style} rotary_dim={sh.rot_dim}" if sh.rope_style != "neox" or sh.rot_dim != sh.head_dim
                else "")
-            + (f" qk_norm={sh.qk_norm}" if sh.qk_norm != "none" else ""))
+            + (f" qk_norm={sh.qk_norm}" if sh.qk_norm != "none" else "")
+            + (f" out=fp8(scale {sh.out_fp8_scale:g})" if sh.out_fp8_scale > 0 else ""))
 
 
 def variant_batch(name: str):
@@ -87,6 +88,9 @@ def variant_batch(name: str):
     if name == "qknorm3":        # workload 3 with a per-head RMS norm of q and k before RoPE
         sh = dataclasses.replace(W.SHAPES[3], qk_norm="rms")
         return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-qknorm")
+    if name == "fp8out3":        # workload 3 with the attention output written as fp8 (scale 2^-6)
+        sh = dataclasses.replace(W.SHAPES[3], out_fp8_scale=2.0 ** -6)
+        return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-fp8out")
     if name == "int8kv5":        # workload 5 with an int8 KV cache (scale 2^-5 for K and V)
         sh = dataclasses.replace(W.SHAPES[5], name="longdecode-gqa4-int8kv", kv_dtype=W.INT8,
                                  k_scale=2.0 ** -5, v_scale=2.0 ** -5)
@@ -95,7 +99,7 @@ def variant_batch(name: str):
     raise KeyError(name)
 
 
-VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "spec4-gqa8", "int8kv5")
+VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "fp8out3", "spec4-gqa8", "int8kv5")
 
 
 def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:

@@ -274,6 +274,23 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
                               void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_attention_forward with the result written as fp8 by the attention kernels themselves
+ * ([TEARDOWN], attention backends: the default backend's FP8 output, which fuses the
+ * quantisation into the attention computation instead of a separate quantisation kernel
+ * between attention and the next GEMM).
+ *   out_scale_quant_orig : real value = scale * stored value (the convention of the KV
+ *              scales); finite, > 0, with a finite reciprocal.
+ *   out      : device [N, H*D] bytes, dense, OCP E4M3 codes: the fp32 attention result
+ *              times 1/out_scale_quant_orig (the reciprocal computed in fp64, rounded to
+ *              fp32), rounded once to nearest-even, saturating to +-448; NaN stays NaN.
+ * Everything else as for pkv_attention_forward.
+ */
+int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch_desc* batch,
+                                      const void* q, int64_t q_row_stride, const void* kv_pool,
+                                      float out_scale_quant_orig, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Opt-in per-kernel timing for measurement tools.  While enabled, every kernel launch of
  * the library is bracketed by HIP events recorded on its stream (this adds no
  * synchronisation).  pkv_kernel_timings() synchronises on those events, writes up to

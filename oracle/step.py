@@ -129,6 +129,14 @@ def run(batch):
     }
 
 
+def output_codes(batch, out: np.ndarray) -> np.ndarray:
+    """The attention output in fp8 when the batch asks for it: OCP e4m3 codes of
+    out / scale, one nearest-even rounding with saturation, the convention of the KV
+    scales ("TensorRT-LLM source teardown part 1", attention backends: FP8 output fused
+    into the attention computation; the rounding is the reading of the fp8 cache codec)."""
+    return codecs.encode(out, codecs.FP8_E4M3, batch.shape.out_fp8_scale)
+
+
 BITS = {codecs.FP32: np.uint32, codecs.BF16: np.uint16, codecs.FP8_E4M3: np.uint8, codecs.INT8: np.uint8}
 
 

@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
                                              vp, vp, vp]
         L.pkv_append_qknorm_rope.restype = i32
         L.pkv_attention_forward.argtypes = [D, Bt, vp, i64, vp, vp, vp, sz, vp]
+        L.pkv_attention_forward_fp8_out.argtypes = [D, Bt, vp, i64, vp, ctypes.c_float, vp, vp, sz, vp]
+        L.pkv_attention_forward_fp8_out.restype = i32
         L.pkv_attention_forward.restype = i32
         L.pkv_kernel_timing_enable.argtypes = [i32]
         L.pkv_kernel_timing_enable.restype = i32
@@ -159,6 +161,12 @@ def pkv_append_qknorm_rope(desc, batch, norm, q, q_row_stride, k, v, kv_row_stri
 def pkv_attention_forward(desc, batch, q, q_row_stride, kv_pool, out, workspace, workspace_bytes, stream) -> int:
     return lib().pkv_attention_forward(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, kv_pool, out,
                                        workspace, workspace_bytes, stream)
+
+
+def pkv_attention_forward_fp8_out(desc, batch, q, q_row_stride, kv_pool, out_scale_quant_orig, out, workspace,
+                                  workspace_bytes, stream) -> int:
+    return lib().pkv_attention_forward_fp8_out(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, kv_pool,
+                                               out_scale_quant_orig, out, workspace, workspace_bytes, stream)
 
 
 def pkv_kernel_timing_enable(on: bool) -> int:

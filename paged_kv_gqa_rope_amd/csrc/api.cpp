@@ -226,9 +226,9 @@ int32_t pkv_append_qknorm_rope(const pkv_attn_desc* desc, const pkv_batch_desc* 
                      kv_pool, stream);
 }
 
-int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
-                              int64_t q_row_stride, const void* kv_pool, void* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
+                              int64_t q_row_stride, const void* kv_pool, void* out, bool fp8_out, float out_scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   std::string err;
   int rc = pkv::validate_desc(desc, err);
   if (rc != PKV_OK) return set_err(rc, err);
@@ -240,6 +240,8 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
   if (!q || !kv_pool || !out) return set_err(PKV_ERR_INVALID_ARG, "q, kv_pool and out must not be NULL");
   if ((rc = check_rows(q, q_row_stride, static_cast<int64_t>(H) * D, desc->io_dtype, "q")) != PKV_OK) return rc;
   if (!aligned16(out) || !aligned16(kv_pool)) return set_err(PKV_ERR_INVALID_ARG, "out and kv_pool must be 16-byte aligned");
+  if (fp8_out && !(std::isfinite(out_scale) && out_scale > 0.f && std::isfinite(1.0f / out_scale)))
+    return set_err(PKV_ERR_INVALID_ARG, "out_scale_quant_orig must be finite and > 0 (with a finite reciprocal)");
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return set_err(PKV_ERR_WORKSPACE, "workspace of " + std::to_string(plan.ws_bytes) + " bytes required, " +
@@ -272,6 +274,8 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
   a.v_scale = quant ? desc->v_scale_quant_orig : 1.f;
   a.io_fmt = fmt_of(desc->io_dtype);
   a.kv_fmt = fmt_of(desc->kv_dtype);
+  a.out_fmt = fp8_out ? pkv::F_FP8 : a.io_fmt;
+  a.out_mul = fp8_out ? static_cast<float>(1.0 / static_cast<double>(out_scale)) : 1.f;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (plan.num_ctx > 0) {
@@ -306,6 +310,19 @@ int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* b
     }
   }
   return PKV_OK;
+}
+
+int32_t pkv_attention_forward(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
+                              int64_t q_row_stride, const void* kv_pool, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, false, 1.f, workspace, workspace_bytes, stream);
+}
+
+int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
+                                      int64_t q_row_stride, const void* kv_pool, float out_scale_quant_orig,
+                                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, true, out_scale_quant_orig, workspace,
+                        workspace_bytes, stream);
 }
 
 int32_t pkv_kernel_timing_enable(int32_t on) {

@@ -128,7 +128,11 @@ __global__ __launch_bounds__(kWave) void attn_generic_kernel(AttnArgs a, int hc)
     for (int j = 0; j < 2; ++j) {
       const int d = lane + kWave * j;
       if (d >= a.D) break;
-      store_elem<IO>(a.out, row * a.H * a.D + static_cast<int64_t>(h0 + hh) * a.D + d, acc[hh][j] * inv);
+      const int64_t o = row * a.H * a.D + static_cast<int64_t>(h0 + hh) * a.D + d;
+      if (a.out_fmt == F_FP8)
+        static_cast<uint8_t*>(a.out)[o] = static_cast<uint8_t>(f32_to_e4m3((acc[hh][j] * inv) * a.out_mul));
+      else
+        store_elem<IO>(a.out, o, acc[hh][j] * inv);
     }
   }
 }

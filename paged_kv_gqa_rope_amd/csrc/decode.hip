@@ -425,8 +425,12 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
     for (int u = 0; u < 8; ++u) o += s_w[s + u] * v[u];
   }
   for (; s < ns; ++s) o += s_w[s] * op[static_cast<int64_t>(s) * kD];
-  uint16_t* out = static_cast<uint16_t*>(a.out) + row * a.H * kD + static_cast<int64_t>(h) * kD;
-  out[t] = static_cast<uint16_t>(f32_to_bf16(o * (a.v_scale / L)));
+  const float val = o * (a.v_scale / L);
+  const int64_t oi = row * a.H * kD + static_cast<int64_t>(h) * kD + t;
+  if (a.out_fmt == F_FP8)
+    static_cast<uint8_t*>(a.out)[oi] = static_cast<uint8_t>(f32_to_e4m3(val * a.out_mul));
+  else
+    static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16(val));
 }
 
 }  // namespace

@@ -87,6 +87,23 @@ __device__ __forceinline__ uint32_t f64_to_e4m3(double x) {
   return sign | static_cast<uint32_t>(q);
 }
 
+// fp32 -> OCP E4M3 code in one rounding (nearest-even), saturating finite overflow and
+// infinities to +-448; NaN -> 0x7F with the sign.  Normal results keep the exponent and the
+// top 3 fraction bits (20 bits dropped); results below 2^-6 are multiples of 2^-9, so they
+// are |f| * 2^9 (exact) rounded to an integer with ties to even.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;                          // NaN
+  if (a >= (121u << 23)) {                                           // |f| >= 2^-6
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;      // exponent:fraction3, rounded
+    const uint32_t code = r - (120u << 3);                            // rebias 127 -> 7
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+  }
+  return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+}
+
 // fp64 -> int8 code: round to the nearest integer (ties to even, v_rndne_f64), saturate
 // to -128 .. 127 (infinities included); NaN stores 0.  Returns the code's low byte.
 __device__ __forceinline__ uint32_t f64_to_int8(double x) {

@@ -54,6 +54,8 @@ struct AttnArgs {
   float scale_log2;         // softmax scale * log2(e)
   float k_scale, v_scale;   // dequantisation scales (1 unless fp8 / int8)
   int32_t io_fmt, kv_fmt;
+  int32_t out_fmt;               // io_fmt, or F_FP8: out = e4m3(O * out_mul)
+  float out_mul;                 // 1 / out_scale_quant_orig for an fp8 output
   int32_t req_begin, req_end;    // requests [begin, end) handled by this launch
   int32_t row_begin;             // packed row of request req_begin
   int32_t max_n;                 // largest n_r among the handled requests

@@ -417,17 +417,32 @@ void prefill_kernel(AttnArgs a) {
   const float inv = 1.f / l_tot;
   const int qi = q0 + l32;
   if (qi >= n) return;
-  uint16_t* op = static_cast<uint16_t*>(a.out) + (row0 + qi) * static_cast<int64_t>(a.H) * kD +
-                 static_cast<int64_t>(h) * kD;
+  const int64_t oe = (row0 + qi) * static_cast<int64_t>(a.H) * kD + static_cast<int64_t>(h) * kD;
+  if (a.out_fmt == F_FP8) {                                  // four e4m3 codes per store
+    uint8_t* op = static_cast<uint8_t*>(a.out) + oe;
+    const float m = a.out_mul;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = b * 32 + i4 * 8 + lh * 4;
-      const uint32_t w0 = pack_bf16(o[b][i4 * 4 + 0] * inv, o[b][i4 * 4 + 1] * inv);
-      const uint32_t w1 = pack_bf16(o[b][i4 * 4 + 2] * inv, o[b][i4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
-    }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = b * 32 + i4 * 8 + lh * 4;
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= f32_to_e4m3((o[b][i4 * 4 + e] * inv) * m) << (8 * e);
+        *reinterpret_cast<uint32_t*>(op + d) = w;
+      }
+  } else {
+    uint16_t* op = static_cast<uint16_t*>(a.out) + oe;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = b * 32 + i4 * 8 + lh * 4;
+        const uint32_t w0 = pack_bf16(o[b][i4 * 4 + 0] * inv, o[b][i4 * 4 + 1] * inv);
+        const uint32_t w1 = pack_bf16(o[b][i4 * 4 + 2] * inv, o[b][i4 * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+      }
+  }
 }
 
 template <int NW, int G, int NS>

@@ -111,7 +111,9 @@ class PagedStep:
         self.v = io_to_device(batch.packed("new_v"), sh.io_dtype, self.device) if N else \
             torch.empty((0, Hkv * D), dtype=TORCH_STORE[sh.io_dtype], device=self.device)
         self.q_out = torch.empty((max(N, 1), H * D), dtype=TORCH_STORE[sh.io_dtype], device=self.device)
-        self.out = torch.empty((max(N, 1), H * D), dtype=TORCH_STORE[sh.io_dtype], device=self.device)
+        self.out_fp8_scale = float(getattr(sh, "out_fp8_scale", 0.0))
+        out_dtype = torch.uint8 if self.out_fp8_scale > 0 else TORCH_STORE[sh.io_dtype]
+        self.out = torch.empty((max(N, 1), H * D), dtype=out_dtype, device=self.device)
         self.pool = torch.empty((batch.num_pool_blocks, 2, T, Hkv, D), dtype=TORCH_STORE[sh.kv_dtype],
                                 device=self.device)
         if sentinel:
@@ -174,6 +176,10 @@ class PagedStep:
                                  self.q_out.data_ptr(), self.pool.data_ptr(), self.stream)
 
     def forward(self) -> int:
+        if self.out_fp8_scale > 0:
+            return L.pkv_attention_forward_fp8_out(self.desc, self.bdesc, self.q_out.data_ptr(), self.q_out.shape[1],
+                                                   self.pool.data_ptr(), self.out_fp8_scale, self.out.data_ptr(),
+                                                   self.ws.data_ptr(), self.ws_bytes, self.stream)
         return L.pkv_attention_forward(self.desc, self.bdesc, self.q_out.data_ptr(), self.q_out.shape[1],
                                        self.pool.data_ptr(), self.out.data_ptr(), self.ws.data_ptr(),
                                        self.ws_bytes, self.stream)
@@ -189,7 +195,8 @@ class PagedStep:
 
     def out_host(self) -> np.ndarray:
         sh = self.shape
-        return stored_to_host(self.out[:self.N], sh.io_dtype).reshape(self.N, sh.num_heads, sh.head_dim)
+        fmt = "fp8_e4m3" if self.out_fp8_scale > 0 else sh.io_dtype
+        return stored_to_host(self.out[:self.N], fmt).reshape(self.N, sh.num_heads, sh.head_dim)
 
     def pool_host(self) -> np.ndarray:
         return stored_to_host(self.pool, self.shape.kv_dtype)

@@ -181,6 +181,16 @@ def test_qk_norm_arguments():
     expect(L.PKV_ERR_INVALID_ARG, call(q_out=None))
 
 
+def test_fp8_output_scale():
+    hb = ok_batch()
+    d = desc_for()
+    qs = d.num_heads * d.head_dim
+    for s in (0.0, -1.0, float("inf"), float("nan"), 1e-45):     # 1e-45: reciprocal overflows
+        expect(L.PKV_ERR_INVALID_ARG,
+               L.pkv_attention_forward_fp8_out(d, hb.desc, P, qs, P, s, P, P, 1 << 40, None))
+    expect(L.PKV_ERR_INVALID_ARG, L.pkv_attention_forward_fp8_out(d, hb.desc, P, qs, P, 1.0, None, P, 1 << 40, None))
+
+
 def test_empty_batch_is_a_no_op():
     hb = HostBatch([], [], [], np.zeros((0, 1)), 1)
     assert append(desc_for(), hb, q=None, q_out=None, k=None, v=None, pool=None) == L.PKV_OK

@@ -122,6 +122,32 @@ def test_qk_norm_append_and_attention(H, case_i):
     print(b.label, kind, style, rot, stats)
 
 
+FP8_OUT_CASES = [
+    # (workload shape, output scale, no saturation): scales that fit the outputs (decode
+    # outputs stay below ~0.2, early prompt rows reach ~4); mostly subnormal codes; a scale
+    # that saturates every output above 448 * 2^-14; fp32 io (generic kernel); an fp8 cache
+    (2, 2.0 ** -9, True), (3, 2.0 ** -6, True), (3, 2.0 ** -2, True), (4, 2.0 ** -14, False),
+    (1, 2.0 ** -5, True), (5, 2.0 ** -10, True),
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(FP8_OUT_CASES)))
+def test_fp8_attention_output(H, case_i):
+    """Attention output quantised to e4m3 inside the attention kernels."""
+    from parity_util import compare_fp8_output
+    k, s, fits = FP8_OUT_CASES[case_i]
+    sh = dataclasses.replace(W.SHAPES[k], out_fp8_scale=s)
+    b = W.small_workload(k, shape=sh)
+    case("fp8 out", b.label, sh.name, "scale", s)
+    st = run_step(H, b)
+    out = O.run(b)["out"]
+    stats = compare_fp8_output(st.out_host(), out, sh, b.label, check_values=fits)
+    print(b.label, "fp8 out", s, stats)
+    if not fits:                                      # large outputs saturate exactly
+        big = np.abs(out) > 1.1 * 448 * s
+        assert big.mean() > 0.1 and np.array_equal(st.out_host()[big], O.output_codes(b, out)[big])
+
+
 SPEC_CASES = [
     # (shape, cached lengths, new tokens per generation request, context requests)
     (2, [70, 300, 5], [2, 4, 7], []),                         # MHA: up to 7 x 1 columns

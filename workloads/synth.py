@@ -57,6 +57,7 @@ class Shape:
     max_num_tokens: int = 8192
     qk_norm: str = "none"        # per-head norm of q and new k before RoPE: "none", "rms", "layer"
     norm_eps: float = 1e-6       # float32 value handed to both sides
+    out_fp8_scale: float = 0.0   # > 0: attention output as fp8 e4m3 codes, real = scale * code value
 
     @property
     def group(self) -> int:
