@@ -164,11 +164,10 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   // still give at least kMinDecodeItems (request, kv head, split) items, then doubled
   // until no request needs more than kMaxSplits splits.  Every split pays a start-up
   // (its first tiles' memory latency) and a merge, so fewer, longer splits stream better,
-  // while 5.5 items per CU keep the last round of workgroups short.  Measured on MI355X:
-  // 64 MHA requests of 512..4096 keys run equally fast at 1024..4096-key splits; 128 GQA-8
-  // requests of 256..4096 keys take 244 us at 512, 220 us at 2048; 16 fp8 requests of
-  // 16K..32K keys 166 us at 1024, 162 us at 2048, 186 us at 512.  Deterministic in the
-  // lengths.
+  // while 5.5 items per CU keep the last round of workgroups short.  Measured on MI355X
+  // (split pass, us, at 1024 / 2048 / 4096-key splits): 64 MHA requests of 512..4096 keys
+  // 373 / 372 / 380; 128 GQA-8 requests of 256..4096 keys 249 / 220 / 219; 16 fp8 requests
+  // of 16K..32K keys 165 / 161 / 162 (512: 186).  Deterministic in the lengths.
   const int64_t T = d.tokens_per_block;
   auto count = [&](int64_t c, int64_t* max_s) {
     int64_t tot = 0, mx = 0;

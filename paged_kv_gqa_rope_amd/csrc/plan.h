@@ -36,7 +36,7 @@ struct BatchPlan {
 
 // Numeric limits of the split policy.
 constexpr int32_t kMaxSplits = 128;       // splits per generation request
-constexpr int32_t kMaxChunk = 4096;        // keys per split, at most
+constexpr int32_t kMaxChunk = 2048;        // keys per split, at most
 constexpr int64_t kMinDecodeItems = 1408;  // (request, kv head, split) items, at least: 5.5 per CU
 // Generation requests carry 1 .. kMaxGenTokens new tokens (a token and its draft tokens).
 constexpr int32_t kMaxGenTokens = 64;
