@@ -284,7 +284,7 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
     a.row_begin = 0;
     a.max_n = plan.max_ctx_n;
     if (plan.fast_prefill)
-      e = timed("prefill_mfma", s, [&] { return pkv::launch_prefill(a, s); });
+      e = timed("prefill_mfma", s, [&] { return pkv::launch_prefill(a, batch->host_context_lengths, batch->host_sequence_lengths, s); });
     else
       e = timed("attn_generic_ctx", s, [&] { return pkv::launch_attn_generic(a, s); });
     if (e != hipSuccess) return hip_fail(e, "context attention launch");

@@ -95,13 +95,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
   const uint32_t u = __float_as_uint(f);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;                          // NaN
-  if (a >= (121u << 23)) {                                           // |f| >= 2^-6
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;      // exponent:fraction3, rounded
-    const uint32_t code = r - (120u << 3);                            // rebias 127 -> 7
-    return sign | (code > 0x7Eu ? 0x7Eu : code);
-  }
-  return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  // all three candidates, then a select (no divergent branches)
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;          // exponent:fraction3, rounded
+  const uint32_t nrm = min(r - (120u << 3), 0x7Eu);                     // rebias 127 -> 7, saturate
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(min(a, 121u << 23)) * 512.0f));
+  const uint32_t code = a > 0x7F800000u ? 0x7Fu : a >= (121u << 23) ? nrm : sub;   // NaN / |f| >= 2^-6 / below
+  return sign | code;
 }
 
 // fp64 -> int8 code: round to the nearest integer (ties to even, v_rndne_f64), saturate

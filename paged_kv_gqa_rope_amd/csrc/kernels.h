@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace pkv {
 
 // element formats of io tensors and the KV pool
@@ -71,6 +73,15 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s);
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
+// Persistent context kernel: one launch per kPrefillMaxReqs context requests.
+struct PrefillSched {
+  int32_t nreq;        // requests of this launch
+  int32_t groups;      // 8: KV head g runs in the group of XCD g % 8; 1: one group
+  int32_t hpg;         // KV heads per group
+  uint16_t rank[kPrefillMaxReqs];   // place of request req_begin + i in the work order (most tiles first)
+};
+// host_ctx_len, host_seq_len: host copies of n_r and S_r, indexed by request
+hipError_t launch_prefill(const AttnArgs& a, const int32_t* host_ctx_len, const int32_t* host_seq_len,
+                          hipStream_t s);
 
 }  // namespace pkv

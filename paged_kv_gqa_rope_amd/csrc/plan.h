@@ -43,6 +43,9 @@ constexpr int32_t kMaxGenTokens = 64;
 // The split pass takes (token, query head) columns of one KV head in blocks of 16; with
 // more than kMaxDecodeCols columns per request the generic kernel takes the batch.
 constexpr int32_t kMaxDecodeCols = 64;
+// The persistent context kernel orders up to kPrefillMaxReqs requests per launch (larger
+// batches take several launches).
+constexpr int32_t kPrefillMaxReqs = 512;
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
 constexpr bool kHaveFastDecode = true;
 constexpr bool kHaveFastPrefill = true;

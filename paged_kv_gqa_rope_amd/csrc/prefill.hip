@@ -27,6 +27,7 @@
 //    the output rescale is skipped unless some lane's running maximum grew by > 2^8.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -95,6 +96,13 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x4& k0, u32x4& k1) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0), "+v"(k1) : "i"(N));
 }
+// 16-byte global load issued as inline asm into a register the caller keeps in place
+// ("+v"): the compiler would otherwise wait for it, and with it for every tile load in
+// flight, at its first use.  The value is only valid after a vmcnt wait that covers it.
+template <int OFF>
+__device__ __forceinline__ void g_load16(u32x4& r, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "+v"(r) : "v"(p), "i"(OFF));
+}
 template <int I>
 using ic = std::integral_constant<int, I>;
 // f(ic<I>()) for I = B .. E-1, unrolled at compile time
@@ -106,73 +114,128 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Block-wide exclusive prefix sum of one int per thread (blockDim.x = NT, a multiple of
+// 64); part[] holds NT / 64 wave totals.  Every thread calls it (it synchronises).
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* part) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) part[w] = x;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += part[i];
+  __syncthreads();
+  return off + x - v;
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Persistent schedule.  An item is (request, KV head, query tile); its cost is its number
+// of 64-key tiles, largest for the last query tile of a chunk.  A group's items are
+// numbered request by request in the order the host gives (most tiles first), KV head by
+// KV head within a request, and heaviest query tile first within a (request, KV head):
+// s = (items of earlier requests) + (KV head within the group) * ntq + k, with ntq the
+// request's query tiles and k = 0 its last one.  Workgroup w of the W in its group takes
+// the items s = j * W + (j even ? w : W - 1 - w), j = 0, 1, ...: every round of W items is
+// dealt out in alternating direction, so the sums of the costs even out, and the W
+// workgroups of a round mostly share one (request, KV head), whose K/V then stays in L2.
+// Groups: when the KV heads split evenly over the 8 XCDs (workgroups go to the XCDs
+// round-robin by linear ID), group x = ID % 8 holds the KV heads h = x (mod 8) of every
+// request and runs on XCD x; otherwise one group holds everything.
+//
 // BT: a cache block holds a whole number of 64-key tiles (tokens_per_block >= 64), so a
 // tile sits in one block and its address is scalar.  Otherwise a tile spans 64/T <= 4
 // blocks and each lane picks its row's block among the tile's (scalar) block IDs.
 template <int NW, int G, int NS, bool BT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_kernel(AttnArgs a) {
+void prefill_kernel(AttnArgs a, PrefillSched sc) {
   constexpr int RB = NW / G;               // 32-row blocks per workgroup
-  constexpr int ROWS = RB * 32;            // query positions per workgroup
+  constexpr int ROWS = RB * 32;            // query positions per item
+  constexpr int NT = NW * kWave;
   constexpr int LPW = kChunksPerStage / NW;   // 1 KB loads per wave per tile
   static_assert(kChunksPerStage % NW == 0, "whole loads per wave");
   static_assert(NS >= 2, "at least double buffering");
-  // XCD-aware placement: workgroups go to the 8 XCDs round-robin by linear ID, so when
-  // the (request, KV head) pairs split evenly, linear ID L runs on XCD L % 8 and takes
-  // that XCD's (L / 8)-th item; all query tiles of one pair then share one L2.
-  const int nq = a.max_n > 0 ? (a.max_n + ROWS - 1) / ROWS : 1;   // query tiles of the longest chunk
-  const int np = a.Hkv * (a.req_end - a.req_begin);                 // (request, KV head) pairs
-  const int L = blockIdx.x;
-  int pair, qt;
-  if (np % kXcds == 0) {
-    const int j = L / kXcds;
-    pair = (j / nq) * kXcds + L % kXcds;
-    qt = j % nq;
-  } else {
-    pair = L / nq;
-    qt = L % nq;
-  }
-  const int g = pair % a.Hkv;
-  const int r = a.req_begin + pair / a.Hkv;
-  const int n = a.ctx_len[r];
-  const int ntq = (n + ROWS - 1) / ROWS;
-  if (qt >= ntq) return;                                            // uniform
-  const int qtile = ntq - 1 - qt;                                   // heaviest tiles first
-  const int S = a.seq_len[r];
-  const int past = S - n;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int l32 = lane % 32, lh = lane / 32;
-  const int h = g * G + wave % G;
-  const int q0 = qtile * ROWS + (wave / G) * 32;                        // first row of this wave
-  const bool wave_active = q0 < n;
-  const int qlast = min(q0 + 31, n - 1);                                // last valid row
-  const int wave_max_pos = past + qlast;
-  const int tile_rows_end = min(qtile * ROWS + ROWS, n);               // rows of the workgroup
-  const int kv_end = past + tile_rows_end;                              // keys 0 .. kv_end-1
-  const int ntiles = (kv_end + kTileK - 1) / kTileK;
-  const int64_t row0 = wave_prefix(a.ctx_len, r);                       // packed row of request r
-  const int tshift = a.tshift, tmask = a.T - 1;
-  // The block table is read-only here: reading it through the constant address space keeps
-  // its uniform reads on the scalar unit although the tile loads write memory (LDS).
-  const __attribute__((address_space(4))) int32_t* table =
-      (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(r) * a.mbps);
-  const int last_blk = (S - 1) >> tshift;
+  static_assert(NT >= kPrefillMaxReqs, "one request per thread when the table is built");
 
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * kStageBytes];
+  __shared__ int4 s_req[kPrefillMaxReqs];            // {n, S, first packed row, request} in the host's order
+  __shared__ int32_t s_pre[kPrefillMaxReqs + 1];     // a group's items before each request
+  __shared__ int32_t s_part[NW];
+
+  const int tid = threadIdx.x;
+  const int wave = uni(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane % 32, lh = lane / 32;
+  const int nreq = sc.nreq, hpg = sc.hpg;
+
+  // ---- request table: lengths and first packed rows in the host's order, then the
+  //      running count of a group's items over that order
+  {
+    const int64_t base = block_prefix(a.ctx_len, a.req_begin);
+    int n = 0, S = 0;
+    if (tid < nreq) {
+      n = a.ctx_len[a.req_begin + tid];
+      S = a.seq_len[a.req_begin + tid];
+    }
+    const int ex = block_excl_scan<NT>(n, s_part);
+    if (tid < nreq) {
+      const int at = sc.rank[tid];
+      s_req[at] = make_int4(n, S, static_cast<int>(base + ex), a.req_begin + tid);
+      s_pre[at] = hpg * ((n + ROWS - 1) / ROWS);
+    }
+  }
+  __syncthreads();
+  {
+    const int v = tid < nreq ? s_pre[tid] : 0;
+    const int ex = block_excl_scan<NT>(v, s_part);
+    if (tid < nreq) s_pre[tid] = ex;
+    if (tid == nreq - 1) s_pre[nreq] = ex + v;
+  }
+  __syncthreads();
+
+  const int groups = sc.groups;
+  const int x = blockIdx.x % groups;
+  const int w = blockIdx.x / groups;
+  const int W = gridDim.x / groups;
+  const int Mg = uni(s_pre[nreq]);
+  const int full = Mg / W, rem = Mg - full * W;
+  const int J = full + (((full & 1) ? W - 1 - w : w) < rem ? 1 : 0);   // this workgroup's items
+  if (J == 0) return;                                                  // uniform
+
+  struct Item {
+    int r, g, qtile, n, S, row0, ntiles;
+  };
+  auto item = [&](int j) __attribute__((always_inline)) {
+    const int s = j * W + ((j & 1) ? W - 1 - w : w);
+    int lo = 0, hi = nreq - 1;                                         // last request i with s_pre[i] <= s
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uni(s_pre[mid]) <= s) lo = mid;
+      else hi = mid - 1;
+    }
+    const int4 q = s_req[lo];
+    Item it;
+    it.n = uni(q.x);
+    it.S = uni(q.y);
+    it.row0 = uni(q.z);
+    it.r = uni(q.w);
+    const int ntq = (it.n + ROWS - 1) / ROWS;
+    const int off = s - uni(s_pre[lo]);
+    const int gl = off / ntq, k = off - gl * ntq;
+    it.g = gl * groups + x;
+    it.qtile = max(ntq - 1 - k, 0);
+    const int kv_end = (it.S - it.n) + min(it.qtile * ROWS + ROWS, it.n);
+    it.ntiles = (kv_end + kTileK - 1) / kTileK;
+    return it;
+  };
+
   const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) unsigned char*)(ring)));
-
-  // ---- Q^T (B operand): query q0 + l32, dims lh*64 + ks*8 + j for ks = 0..7
-  bf16x8 qf[8];
-  {
-    const int qi = min(q0 + l32, n - 1);
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row0 + qi) * a.q_stride +
-                         static_cast<int64_t>(h) * kD + lh * 64;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + ks * 8));
-  }
-  const int my_pos = past + min(q0 + l32, n - 1);                       // this lane's query position
   const float c = a.scale_log2;
 
   // ---- tile loads: wave w moves the 1 KB chunks q = w*LPW + j of a stage (K tile: q < 16,
@@ -181,7 +244,7 @@ void prefill_kernel(AttnArgs a) {
   const uint32_t kvrb = static_cast<uint32_t>(a.Hkv) * kRowBytes;   // bytes per token row
   const uint32_t vofs = static_cast<uint32_t>(a.T) * kvrb;          // V half of a block
   const int64_t blk_bytes = 2 * static_cast<int64_t>(vofs);
-  const char* pool_g = static_cast<const char*>(a.pool) + static_cast<int64_t>(g) * kRowBytes;
+  const int tshift = a.tshift, tmask = a.T - 1;
   auto ld_row = [&](int j) __attribute__((always_inline)) { return 4 * ((wave * LPW + j) % 16) + lane / 16; };
   auto ld_isv = [&](int j) __attribute__((always_inline)) { return wave * LPW + j >= 16; };   // uniform
   auto ld_col = [&](int j) __attribute__((always_inline)) {                                   // byte column
@@ -200,24 +263,33 @@ void prefill_kernel(AttnArgs a) {
   struct Ids {
     int32_t i0, i1, i2, i3;
   };
-  // block IDs of a tile: BT -> its one block; else its 64/T blocks (clamped to the last)
-  auto fetch = [&](int tile, Ids& x) __attribute__((always_inline)) {
-    const int b0 = __builtin_amdgcn_readfirstlane((tile * kTileK) >> tshift);
-    x.i0 = __builtin_amdgcn_readfirstlane(table[min(b0, last_blk)]);
+  // The block table is read-only here: reading it through the constant address space keeps
+  // its uniform reads on the scalar unit although the tile loads write memory (LDS).
+  auto table_of = [&](int r) __attribute__((always_inline)) {
+    return (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(r) * a.mbps);
+  };
+  // block IDs of tile `tile` of item `it`: BT -> its one block; else its 64/T blocks
+  // (clamped to the request's last block)
+  auto fetch = [&](const Item& it, int tile, Ids& xi) __attribute__((always_inline)) {
+    const auto table = table_of(it.r);
+    const int last_blk = min((it.S - 1) >> tshift, a.mbps - 1);
+    const int b0 = uni((tile * kTileK) >> tshift);
+    xi.i0 = uni(table[min(b0, last_blk)]);
     if constexpr (!BT) {
-      x.i1 = __builtin_amdgcn_readfirstlane(table[min(b0 + 1, last_blk)]);
-      x.i2 = __builtin_amdgcn_readfirstlane(table[min(b0 + 2, last_blk)]);
-      x.i3 = __builtin_amdgcn_readfirstlane(table[min(b0 + 3, last_blk)]);
+      xi.i1 = uni(table[min(b0 + 1, last_blk)]);
+      xi.i2 = uni(table[min(b0 + 2, last_blk)]);
+      xi.i3 = uni(table[min(b0 + 3, last_blk)]);
     }
   };
   auto valid_id = [&](int32_t id) __attribute__((always_inline)) { return (id >= 0 && id < a.num_blocks) ? id : 0; };
   // Keys past S-1 (only in the tile that holds key S-1) are fetched from key S-1 instead:
   // never an unwritten slot, and their scores are masked anyway.
-  auto issue = [&](int tile, int slot, const Ids& x) __attribute__((always_inline)) {
+  auto issue = [&](const Item& it, int tile, int slot, const Ids& xi) __attribute__((always_inline)) {
     unsigned char* st = ring + slot * kStageBytes;
-    const int lim = S - 1 - tile * kTileK;                             // last tile row with a key
+    const char* pool_g = static_cast<const char*>(a.pool) + static_cast<int64_t>(it.g) * kRowBytes;
+    const int lim = it.S - 1 - tile * kTileK;                          // last tile row with a key
     if constexpr (BT) {
-      const char* base = pool_g + static_cast<int64_t>(valid_id(x.i0)) * blk_bytes +
+      const char* base = pool_g + static_cast<int64_t>(valid_id(xi.i0)) * blk_bytes +
                          static_cast<int64_t>((tile * kTileK) & tmask) * kvrb;
       if (lim >= kTileK - 1) {
 #pragma unroll
@@ -237,9 +309,9 @@ void prefill_kernel(AttnArgs a) {
       const int b0 = (tile * kTileK) >> tshift;
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
-        const int key = min(tile * kTileK + ld_row(j), S - 1);
+        const int key = min(tile * kTileK + ld_row(j), it.S - 1);
         const int sb = (key >> tshift) - b0;                          // 0 .. 64/T - 1
-        const int32_t id = valid_id(sb == 0 ? x.i0 : sb == 1 ? x.i1 : sb == 2 ? x.i2 : x.i3);
+        const int32_t id = valid_id(sb == 0 ? xi.i0 : sb == 1 ? xi.i1 : sb == 2 ? xi.i2 : xi.i3);
         const char* p = pool_g + static_cast<int64_t>(id) * blk_bytes + (ld_isv(j) ? vofs : 0u) +
                         static_cast<uint32_t>(key & tmask) * kvrb + ld_col(j);
         __builtin_amdgcn_global_load_lds(p, (lds_void*)(st + ld_dst(j)), 16, 0, 0);
@@ -263,6 +335,46 @@ void prefill_kernel(AttnArgs a) {
     for (int b = 0; b < 4; ++b) vrd[b] = lp + ((b ^ xv) * 4) * 16;
   }
 
+  // ---- Q^T (B operand) of an item: query q0 + l32 of this wave's head, dims lh*64 + ks*8 + j
+  //      for ks = 0..7; rows past the chunk repeat its last row
+  //      (asynchronous: see g_load16)
+  auto load_q = [&](const Item& it, u32x4 (&dst)[8]) __attribute__((always_inline)) {
+    const int hh = it.g * G + wave % G;
+    const int qq0 = it.qtile * ROWS + (wave / G) * 32;
+    const int64_t row = min<int64_t>(it.row0 + min(qq0 + l32, it.n - 1), a.N - 1);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride + static_cast<int64_t>(hh) * kD + lh * 64;
+    static_for<0, 8>([&](auto KSc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KSc)::value;
+      g_load16<ks * 16>(dst[ks], qp);
+    });
+  };
+
+  // ---- the compute side's item: this wave's head, rows and causal limits
+  Item C = item(0);
+  int h, q0, past, wave_max_pos, my_pos;
+  bool wave_active;
+  auto enter = [&](const Item& it) __attribute__((always_inline)) {
+    past = it.S - it.n;
+    h = it.g * G + wave % G;
+    q0 = it.qtile * ROWS + (wave / G) * 32;
+    wave_active = q0 < it.n;
+    wave_max_pos = past + min(q0 + 31, it.n - 1);
+    my_pos = past + min(q0 + l32, it.n - 1);
+  };
+  // Q of the compute side's item, loaded in place (see g_load16): the first before the
+  // ring's first tiles, so the first iteration's wait covers it; each later one in the last
+  // tile of the item before, once that tile's QK products have read the old Q, and then the
+  // next iteration waits for every load of this wave (the Q loads are its newest).
+  u32x4 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = u32x4{0u, 0u, 0u, 0u};
+  load_q(C, qf);
+  enter(C);
+  Item Cn = C;                               // the compute side's next item
+  if (J > 1) Cn = item(1);
+  bool q_next = false;                       // this iteration loads the next item's Q
+  bool q_wait = false;                       // this iteration waits for all loads
+
   float m_run = -INFINITY, l_run = 0.f;      // raw-score max of query l32; this lane's partial sum
   const bf16x2 kOnes = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   f32x16 o[4];                               // O^T[dim blk*32 + (i/4)*8 + lh*4 + i%4][query l32]
@@ -273,14 +385,15 @@ void prefill_kernel(AttnArgs a) {
 
   auto compute = [&](int t, int slot) __attribute__((always_inline)) {
     const int kb0 = t * kTileK;
-    if (!(wave_active && kb0 <= wave_max_pos)) return;
+    const bool act = wave_active && kb0 <= wave_max_pos;   // uniform
     const uint32_t sbase = ring_b + static_cast<uint32_t>(slot * kStageBytes);
+    // ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K operands
+    //      read RA steps ahead
+    f32x16 s[2];
+    if (act) {
     uint32_t ka_[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ka_[ks] = sbase + kofs[ks];
-    // ---- S^T = K Q^T: two 32-key blocks, their MFMA chains interleaved and the K operands
-    //      read one step ahead
-    f32x16 s[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
     constexpr int RA = 3;                    // steps of K operands in flight ahead of the MFMAs
@@ -294,11 +407,16 @@ void prefill_kernel(AttnArgs a) {
     static_for<0, 8>([&](auto KSc) __attribute__((always_inline)) {
       constexpr int ks = decltype(KSc)::value;
       if constexpr (ks + RA < 8) kread(ic<ks + RA>());
-      auto& x = kr[ks % (RA + 1)];
-      lgkm_wait<2 * (ks + RA < 8 ? RA : 7 - ks)>(x[0], x[1]);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[0]), qf[ks], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[1]), qf[ks], s[1], 0, 0, 0);
+      auto& xk = kr[ks % (RA + 1)];
+      lgkm_wait<2 * (ks + RA < 8 ? RA : 7 - ks)>(xk[0], xk[1]);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xk[0]), as_bf16x8(qf[ks]), s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xk[1]), as_bf16x8(qf[ks]), s[1], 0, 0, 0);
     });
+    }
+    // The last tile of an item: the next item's Q replaces this one's (one program point
+    // for every wave, so the registers the loads write are the ones the products read).
+    if (q_next) load_q(Cn, qf);
+    if (!act) return;
     // ---- causal mask on tiles that cross this wave's diagonal (or the end of the keys)
     if (kb0 + kTileK - 1 > past + q0) {
       const int lim = my_pos - kb0 - lh * 4;                 // key offset kb*32+(i/4)*8+i%4 <= lim
@@ -317,15 +435,11 @@ void prefill_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 1; j < 8; ++j) m4[k] = fmaxf(m4[k], s[k / 2][(k % 2) * 8 + j]);
     }
-    float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
+    const float tmax = xor_max<32>(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     // Lazy rescaling: the running maximum used as the exponent offset only moves when a
     // score exceeds it by more than 2^8 in exp2 units, so P stays <= 256 (exact enough in
     // fp32 sums and bf16 products) and most tiles skip the rescale of O.  The first tile
-    // always sets it (m_run starts at -inf).
+    // of an item always sets it (m_run starts at -inf).
     if (__any((tmax - m_run) * c > kLazyLog2)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -383,90 +497,178 @@ void prefill_kernel(AttnArgs a) {
     });
   };
 
-  // ---- the ring: tile t lives in stage t % NS.  Iteration t waits for this wave's loads of
-  //      tile t (the NS-2 later tiles may stay in flight), meets the other waves at the
-  //      barrier -- after which tile t is complete in LDS and stage (t-1) % NS is no longer
-  //      read -- refills that stage with tile t+NS-1 and computes tile t.  Past the last tile
-  //      the loads repeat it, so every iteration has the same loads in flight.
-  const int tl = ntiles - 1;
-  {
-    Ids x[NS - 1];
+  // ---- normalise and store the compute side's item: lane owns query l32 and dims
+  //      blk*32 + (i/4)*8 + lh*4 + i%4
+  //      (st_*: the finished item's rows, kept until the next iteration stores them)
+  int st_n = 0, st_row0 = 0, st_h = 0, st_q0 = 0;
+  bool st_active = false;
+  auto store = [&]() __attribute__((always_inline)) {
+    if (!st_active) return;
+    const float inv = 1.f / xor_sum<32>(l_run);
+    const int qi = st_q0 + l32;
+    const int64_t row = st_row0 + static_cast<int64_t>(qi);
+    if (qi >= st_n || row >= a.N) return;
+    const int64_t oe = row * static_cast<int64_t>(a.H) * kD + static_cast<int64_t>(st_h) * kD;
+    if (a.out_fmt == F_FP8) {                                  // four e4m3 codes per store
+      uint8_t* op = static_cast<uint8_t*>(a.out) + oe;
+      const float m = a.out_mul;
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) fetch(min(u, tl), x[u]);
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(min(u, tl), u, x[u]);
-  }
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = b * 32 + i4 * 8 + lh * 4;
+          uint32_t wd = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wd |= f32_to_e4m3((o[b][i4 * 4 + e] * inv) * m) << (8 * e);
+          *reinterpret_cast<uint32_t*>(op + d) = wd;
+        }
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(a.out) + oe;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = b * 32 + i4 * 8 + lh * 4;
+          const uint32_t w0 = pack_bf16(o[b][i4 * 4 + 0] * inv, o[b][i4 * 4 + 1] * inv);
+          const uint32_t w1 = pack_bf16(o[b][i4 * 4 + 2] * inv, o[b][i4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+        }
+    }
+  };
+
+  // ---- the ring: this workgroup's items form one stream of tiles, and stream tile t lives
+  //      in stage t % NS.  Iteration t waits for this wave's loads of tile t (the NS-2 later
+  //      tiles may stay in flight), meets the other waves at the barrier -- after which tile
+  //      t is complete in LDS and stage (t-1) % NS is no longer read -- refills that stage
+  //      with stream tile t+NS-1 and computes tile t.  The loads run NS-1 tiles ahead across
+  //      item boundaries; past the stream's last tile they repeat it, so every iteration
+  //      has the same loads in flight.
+  Item L = C;                                // the loader's item and tile
+  int jl = 0, ul = 0;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (ul + 1 < L.ntiles) {
+      ++ul;
+    } else if (jl + 1 < J) {
+      ++jl;
+      ul = 0;
+      L = item(jl);
+    }
+  };
   Ids nx;
-  fetch(min(NS - 1, tl), nx);
-  int slot = 0, fill = NS - 1;
-  for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPW));
+  {
+    // the first NS-1 tiles: all block-ID fetches first (one wait for their latency), then
+    // the loads
+    Item lp[NS - 1];
+    int up[NS - 1];
+    Ids xp[NS - 1];
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+      lp[u] = L;
+      up[u] = ul;
+      fetch(L, ul, xp[u]);
+      advance();
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(lp[u], up[u], u, xp[u]);
+  }
+  fetch(L, ul, nx);
+  int slot = 0, fill = NS - 1, tc = 0, jc = 0;
+  bool st_pending = false;
+  for (;;) {
+    if (q_wait) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPW));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(min(t + NS - 1, tl), fill, nx);
-    fetch(min(t + NS, tl), nx);
-    compute(t, slot);
+    if (st_pending) {                        // the previous item's output, then a fresh state
+      store();
+      st_pending = false;
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
+    }
+    q_wait = false;
+    issue(L, ul, fill, nx);
+    advance();
+    fetch(L, ul, nx);
+    q_next = tc + 1 == C.ntiles && jc + 1 < J;
+    compute(tc, slot);
     slot = slot == NS - 1 ? 0 : slot + 1;
     fill = fill == NS - 1 ? 0 : fill + 1;
+    if (++tc == C.ntiles) {                  // item done: its output is stored next iteration
+      st_n = C.n;
+      st_row0 = C.row0;
+      st_h = h;
+      st_q0 = q0;
+      st_active = wave_active;
+      if (++jc == J) break;
+      st_pending = true;
+      q_wait = true;
+      C = Cn;
+      enter(C);
+      tc = 0;
+      if (jc + 1 < J) Cn = item(jc + 1);
+    }
   }
+  store();
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may still target this workgroup's LDS at exit
-
-  // ---- normalise and store: lane owns query l32 and dims blk*32 + (i/4)*8 + lh*4 + i%4
-  if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  const float inv = 1.f / l_tot;
-  const int qi = q0 + l32;
-  if (qi >= n) return;
-  const int64_t oe = (row0 + qi) * static_cast<int64_t>(a.H) * kD + static_cast<int64_t>(h) * kD;
-  if (a.out_fmt == F_FP8) {                                  // four e4m3 codes per store
-    uint8_t* op = static_cast<uint8_t*>(a.out) + oe;
-    const float m = a.out_mul;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = b * 32 + i4 * 8 + lh * 4;
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w |= f32_to_e4m3((o[b][i4 * 4 + e] * inv) * m) << (8 * e);
-        *reinterpret_cast<uint32_t*>(op + d) = w;
-      }
-  } else {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + oe;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = b * 32 + i4 * 8 + lh * 4;
-        const uint32_t w0 = pack_bf16(o[b][i4 * 4 + 0] * inv, o[b][i4 * 4 + 1] * inv);
-        const uint32_t w1 = pack_bf16(o[b][i4 * 4 + 2] * inv, o[b][i4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
-      }
-  }
 }
 
 template <int NW, int G, int NS>
-hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_t(const AttnArgs& a0, const int32_t* host_n, const int32_t* host_S, hipStream_t s) {
   static_assert(NW % G == 0, "a workgroup holds whole query groups");
   constexpr int ROWS = (NW / G) * 32;
-  const int nq = (a.max_n + ROWS - 1) / ROWS;
-  const dim3 grid(nq * a.Hkv * (a.req_end - a.req_begin));
-  if (a.T % kTileK == 0)   // tokens_per_block is a power of two: whole tiles per block
-    hipLaunchKernelGGL((prefill_kernel<NW, G, NS, true>), grid, dim3(NW * kWave), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<NW, G, NS, false>), grid, dim3(NW * kWave), 0, s, a);
-  return hipGetLastError();
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int groups = a0.Hkv % kXcds == 0 ? kXcds : 1;
+  for (int b0 = a0.req_begin; b0 < a0.req_end; b0 += kPrefillMaxReqs) {
+    AttnArgs a = a0;
+    a.req_begin = b0;
+    a.req_end = std::min(b0 + kPrefillMaxReqs, a0.req_end);
+    PrefillSched sc{};
+    sc.nreq = a.req_end - a.req_begin;
+    sc.groups = groups;
+    sc.hpg = a.Hkv / groups;
+    // requests with the most 64-key tiles first (a close bound: ntq query tiles over
+    // past + ROWS/2 * (ntq + 1) keys on average)
+    int order[kPrefillMaxReqs];
+    int64_t cost[kPrefillMaxReqs];
+    int64_t tiles = 0;                                 // query tiles of all requests
+    for (int i = 0; i < sc.nreq; ++i) {
+      order[i] = i;
+      const int64_t n = host_n[b0 + i], past = host_S[b0 + i] - n, ntq = (n + ROWS - 1) / ROWS;
+      cost[i] = ntq * (2 * past + ROWS * (ntq + 1));
+      tiles += ntq;
+    }
+    std::stable_sort(order, order + sc.nreq, [&](int i, int j) { return cost[i] > cost[j]; });
+    for (int p = 0; p < sc.nreq; ++p) sc.rank[order[p]] = static_cast<uint16_t>(p);
+    const int64_t per_group = tiles * sc.hpg;
+    const int64_t W = std::max<int64_t>(1, std::min<int64_t>(per_group, std::max(1, cus / groups)));
+    const dim3 grid(static_cast<unsigned>(W * groups));
+    if (a.T % kTileK == 0)   // tokens_per_block is a power of two: whole tiles per block
+      hipLaunchKernelGGL((prefill_kernel<NW, G, NS, true>), grid, dim3(NW * kWave), 0, s, a, sc);
+    else
+      hipLaunchKernelGGL((prefill_kernel<NW, G, NS, false>), grid, dim3(NW * kWave), 0, s, a, sc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_prefill(const AttnArgs& a, const int32_t* host_ctx_len, const int32_t* host_seq_len,
+                          hipStream_t s) {
   if (a.T < 16) return hipErrorNotSupported;   // a 64-key tile spans at most 4 blocks
+  if (!host_ctx_len || !host_seq_len || a.req_end <= a.req_begin) return hipErrorInvalidValue;
   switch (a.H / a.Hkv) {
-    case 1: return launch_t<8, 1, 4>(a, s);
-    case 2: return launch_t<8, 2, 4>(a, s);
-    case 4: return launch_t<8, 4, 4>(a, s);
-    case 8: return launch_t<8, 8, 4>(a, s);
+    case 1: return launch_t<8, 1, 4>(a, host_ctx_len, host_seq_len, s);
+    case 2: return launch_t<8, 2, 4>(a, host_ctx_len, host_seq_len, s);
+    case 4: return launch_t<8, 4, 4>(a, host_ctx_len, host_seq_len, s);
+    case 8: return launch_t<8, 8, 4>(a, host_ctx_len, host_seq_len, s);
     default: return hipErrorNotSupported;
   }
 }

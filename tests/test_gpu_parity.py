@@ -390,6 +390,35 @@ def test_context_chunks_blocks_and_groups(H, T, G):
     compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
 
 
+# The context kernel is persistent: it orders up to 512 requests per launch by their number
+# of tiles and deals the (request, KV head, query tile) items to its workgroups in rounds.
+# Cases: more requests than one launch takes (two launches, one query tile each), KV heads
+# that do not split over the 8 XCD groups, and one chunk far longer than the rest (its
+# items span several rounds); blocks of 16 and 32 tokens take the multi-block tile path.
+PERSIST_CASES = [
+    # (Hkv, G, T, requests, longest random chunk, one long chunk)
+    (8, 1, 16, 520, 40, 40),
+    (3, 2, 32, 40, 600, 600),
+    (8, 2, 16, 24, 200, 1100),
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(PERSIST_CASES)))
+def test_context_persistent_schedule(H, case_i):
+    Hkv, G, T, R, nmax, nlong = PERSIST_CASES[case_i]
+    rng = np.random.default_rng(7000 + case_i)
+    ns = rng.integers(1, nmax + 1, size=R)
+    ns[R // 2] = nlong
+    pasts = T * rng.integers(0, 4, size=R)
+    sh = W.Shape(f"persist-{case_i}", Hkv * G, Hkv, 128, T, W.BF16, W.BF16, 5e5, max_num_tokens=int(ns.sum()) + 1)
+    b = W.make_batch(sh, ctx=list(zip(ns.tolist(), pasts.tolist())), gen_past=[77], seed=7100 + case_i)
+    case("persistent", sh.name, R, int(ns.sum()))
+    st = run_step(H, b)
+    ref = O.run(b)
+    assert_bits_equal(st.q_out_host(), ref["q_out"], "q_out")
+    compare_attention(st.out_host(), ref["out"], sh, sh.name)
+
+
 def test_fp64_to_bf16_store_edge_values(H):
     # fp32 io into a bf16 cache: every stored element is one fp64 -> bf16 rounding.
     # History values hit exact bf16 ties (both parities), fp32 subnormals, values at the
