@@ -317,6 +317,35 @@ def test_decode_lengths_blocks_and_groups(H, T, G, kv):
     compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
 
 
+# The same length edges with 4 and 8 KV heads (several heads' pieces in every cache row):
+# tiles that span two blocks (T = 16), one block, or part of one, for bf16, fp8 and int8
+# caches, with single tokens and with draft tokens.
+HEAD_GROUP_CASES = [
+    # (Hkv, T, G, kv, draft tokens per request or None)
+    (4, 16, 1, W.BF16, None),
+    (8, 32, 2, W.FP8_E4M3, None),
+    (4, 64, 4, W.INT8, None),
+    (4, 128, 3, W.BF16, None),
+    (4, 16, 8, W.FP8_E4M3, None),
+    (8, 256, 2, W.BF16, None),
+    (4, 64, 2, W.BF16, 3),
+    (8, 16, 1, W.INT8, 5),
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(HEAD_GROUP_CASES)))
+def test_decode_head_groups(H, case_i):
+    Hkv, T, G, kv, draft = HEAD_GROUP_CASES[case_i]
+    sh = W.Shape(f"decgrp-{case_i}", Hkv * G, Hkv, 128, T, W.BF16, kv, 1e4, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    pasts = [0, 1, 15, 63, 64, 127, 511, 512, 1000, 2500]
+    gen_new = None if draft is None else [1 + (i % draft) for i in range(len(pasts))]
+    b = W.make_batch(sh, gen_past=pasts, seed=4000 + case_i, pool_blocks_min=3, gen_new=gen_new)
+    case("decode head groups", sh.name, kv, draft)
+    st = run_step(H, b)
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(kv)), "pool")
+    compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
+
+
 def test_decode_fp8_saturating_values(H):
     # values beyond 448 * scale saturate on write; the oracle reads the same codes
     sh = W.Shape("fp8-sat", 8, 2, 128, 64, W.BF16, W.FP8_E4M3, 1e4, k_scale=2.0 ** -9, v_scale=2.0 ** -9)
