@@ -9,9 +9,12 @@
 // block table ("TensorRT-LLM source teardown part 1", KV cache manager interfaces).
 //
 // CDNA4 mapping:
-//  * one workgroup = one KV head's whole GQA group (G = 1, 2, 4 or 8 query heads) for a
-//    block of query positions: NW waves, each owning 32 query rows of one query head,
-//    so every K/V tile staged in LDS feeds NW waves (all G heads that share it);
+//  * one item = one KV head's whole GQA group (G = 1, 2, 4 or 8 query heads) for a block
+//    of query positions of one request: NW waves, each owning 32 query rows of one query
+//    head, so every K/V tile staged in LDS feeds NW waves (all G heads that share it);
+//  * persistent workgroups, at most one per CU: each works through a fixed, balanced
+//    list of items (see the schedule below) as one stream of tiles, so start-up, output
+//    stores and the next item's loads overlap the tiles of the item before;
 //  * K/V tiles (64 keys x 128 dims each) travel from the pool straight into LDS with
 //    global_load_lds_dwordx4 (no register staging, no LDS store instructions) through
 //    a ring of NS stages, so NS-1 tiles are in flight while one is computed; each
@@ -178,9 +181,9 @@ void prefill_kernel(AttnArgs a, PrefillSched sc) {
   {
     const int64_t base = block_prefix(a.ctx_len, a.req_begin);
     int n = 0, S = 0;
-    if (tid < nreq) {
-      n = a.ctx_len[a.req_begin + tid];
-      S = a.seq_len[a.req_begin + tid];
+    if (tid < nreq) {      // device lengths, kept to n >= 1 and S >= n whatever they hold
+      n = max(a.ctx_len[a.req_begin + tid], 1);
+      S = max(a.seq_len[a.req_begin + tid], n);
     }
     const int ex = block_excl_scan<NT>(n, s_part);
     if (tid < nreq) {
@@ -230,7 +233,7 @@ void prefill_kernel(AttnArgs a, PrefillSched sc) {
     it.g = gl * groups + x;
     it.qtile = max(ntq - 1 - k, 0);
     const int kv_end = (it.S - it.n) + min(it.qtile * ROWS + ROWS, it.n);
-    it.ntiles = (kv_end + kTileK - 1) / kTileK;
+    it.ntiles = max((kv_end + kTileK - 1) / kTileK, 1);
     return it;
   };
 
