@@ -107,8 +107,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // side, so together they read each block's K and V rows as contiguous memory.
   const int g = blockIdx.x % a.Hkv, cb = blockIdx.x / a.Hkv, split = blockIdx.y, rg = blockIdx.z;
   const int r = a.req_begin + rg;
-  const int S = a.seq_len[r];
-  const int n = a.ctx_len[r];                                  // 1, or 1 + draft tokens
+  // device lengths, kept to n >= 1 and S >= n whatever they hold
+  const int n = max(a.ctx_len[r], 1);                          // 1, or 1 + draft tokens
+  const int S = max(a.seq_len[r], n);
   const int G = a.H / a.Hkv;
   const int k0 = split * a.chunk;
   if (k0 >= S || split >= a.max_splits || cb * 16 >= G * n) return;   // uniform over the block
@@ -123,6 +124,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bool col_ok = tok < n;
   const int key_lim = col_ok ? S - n + tok : -1;               // keys 0 .. key_lim
   const int64_t row0 = a.max_n == 1 ? static_cast<int64_t>(a.row_begin) + rg : wave_prefix(a.ctx_len, r);
+  if (row0 < a.row_begin || row0 + n > a.N) return;             // rows outside the generation rows: skip
   const int64_t row = row0 + min(tok, n - 1);
   const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
   // The block table is read-only here: reading it through the constant address space
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int ntiles = (kend - k0 + kTile - 1) / kTile;
   const int tshift = a.tshift, tmask = a.T - 1;
-  const int last_blk = (kend - 1) >> tshift;
+  const int last_blk = min((kend - 1) >> tshift, a.mbps - 1);
   const int64_t blk_bytes = 2 * static_cast<int64_t>(a.T) * kv_row * (KV == F_BF16 ? 2 : 1);   // K and V of T slots
   uint16_t* vt = vtile[wave];
   uint16_t* kt = ktile[wave];
@@ -394,6 +396,7 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
   const int S = a.seq_len[r];
   const int ns = min((S + a.chunk - 1) / a.chunk, a.max_splits);
   const int64_t row = (a.max_n == 1 ? static_cast<int64_t>(a.row_begin) + rg : wave_prefix(a.ctx_len, r)) + tok;
+  if (row < a.row_begin || row >= a.N) return;                      // uniform: outside the generation rows
   const int64_t base = ((row - a.row_begin) * a.H + h) * a.max_splits;
   __shared__ float s_w[kD];
   __shared__ float s_red[kD / kWave];
