@@ -8,8 +8,13 @@
 // second pass with the same rescaling identity FlashAttention uses to merge tiles
 // (study notes 6.2, update of acc_o by the new running max).
 //
-// Pass 1, one workgroup per (generation request, KV head, chunk); 4 waves, each
-// streaming 64-key tiles of the chunk:
+// Pass 1, 4 waves per workgroup.  A workgroup takes one (generation request, KV head,
+// chunk) and its waves stream alternate tiles of the chunk, their states merged in LDS at
+// the end -- or, for a one-byte cache (fp8 / int8) with the KV heads in fours, 4
+// neighbouring KV heads, one wave each, every wave streaming all tiles of the chunk for
+// its head: the four waves of a CU then read the neighbouring 128-byte pieces of the same
+// cache rows at about the same time, which HBM serves faster than one head's pieces
+// alone.  Per wave and tile:
 //   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, loaded straight
 //     from HBM in operand layout; B = the G query heads of the KV head (GQA group,
 //     G <= 16, padded with zero heads), kept in registers for the whole chunk.
@@ -101,11 +106,16 @@ struct TileRegs {
   uint4 v[KV == F_BF16 ? 8 : 4];
 };
 
-template <int KV>
+// B: KV heads per workgroup (1, or kWaves: one per wave).
+template <int KV, int B>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
-  // KV head fastest: the workgroups of every head of one (request, chunk) run side by
-  // side, so together they read each block's K and V rows as contiguous memory.
-  const int g = blockIdx.x % a.Hkv, cb = blockIdx.x / a.Hkv, split = blockIdx.y, rg = blockIdx.z;
+  static_assert(B == 1 || B == kWaves, "one head per workgroup, or one per wave");
+  // KV head (group) fastest: the workgroups of every head of one (request, chunk) run
+  // side by side.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  const int hgs = a.Hkv / B;                                   // head groups
+  const int g = (blockIdx.x % hgs) * B + (B == 1 ? 0 : wave);  // this wave's KV head
+  const int cb = blockIdx.x / hgs, split = blockIdx.y, rg = blockIdx.z;
   const int r = a.req_begin + rg;
   // device lengths, kept to n >= 1 and S >= n whatever they hold
   const int n = max(a.ctx_len[r], 1);                          // 1, or 1 + draft tokens
@@ -114,7 +124,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int k0 = split * a.chunk;
   if (k0 >= S || split >= a.max_splits || cb * 16 >= G * n) return;   // uniform over the block
   const int kend = min(k0 + a.chunk, S);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
   // Columns of the score tile: (token, query head) pairs, 16 per column block.  Lane
@@ -326,24 +335,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Software pipeline: tile t+4 is in flight while tile t is computed.  Loads and ID
-  // fetches run unconditionally (past the wave's last tile they repeat the chunk's last
-  // tile), so every path has the same loads in flight and the compiler's wait before a
-  // tile's compute covers that tile only, not the one issued after it.
+  // Software pipeline: the wave's next tile is in flight while a tile is computed (B = 1:
+  // the wave's tiles are w, w + 4, ...; B = 4: every tile).  Loads and ID fetches run
+  // unconditionally (past the wave's last tile they repeat the chunk's last tile), so
+  // every path has the same loads in flight and the compiler's wait before a tile's
+  // compute covers that tile only, not the one issued after it.
+  constexpr int TS = B == 1 ? kWaves : 1;                      // tile stride of a wave
   TileRegs<KV> ra, rb;
   int32_t ids_a[2], ids_b[2];
   const int tl = ntiles - 1;
-  int t = wave;
+  int t = B == 1 ? wave : 0;
   fetch_ids(min(t, tl), ids_a);
   issue(min(t, tl), ids_a, ra);
-  fetch_ids(min(t + kWaves, tl), ids_b);
-  for (; t < ntiles; t += 2 * kWaves) {
-    issue(min(t + kWaves, tl), ids_b, rb);
-    fetch_ids(min(t + 2 * kWaves, tl), ids_a);
+  fetch_ids(min(t + TS, tl), ids_b);
+  for (; t < ntiles; t += 2 * TS) {
+    issue(min(t + TS, tl), ids_b, rb);
+    fetch_ids(min(t + 2 * TS, tl), ids_a);
     compute(t, ra);
-    issue(min(t + 2 * kWaves, tl), ids_a, ra);
-    fetch_ids(min(t + 3 * kWaves, tl), ids_b);
-    if (t + kWaves < ntiles) compute(t + kWaves, rb);
+    issue(min(t + 2 * TS, tl), ids_a, ra);
+    fetch_ids(min(t + 3 * TS, tl), ids_b);
+    if (t + TS < ntiles) compute(t + TS, rb);
+  }
+  const int ncol = min(16, G * n - cb * 16);                     // valid columns of the block
+  if constexpr (B > 1) {
+    // ---- this wave alone holds its head's state for the chunk: write (m, l, o) as they are
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lg * 4 + i, cc = cb * 16 + c;
+      if (c < ncol) {
+        const int64_t part = ((row0 - a.row_begin + cc / G) * a.H + g * G + cc % G) * a.max_splits + split;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) a.ws_o[part * kD + nb * 16 + li] = o[nb][i];
+      }
+    }
+    if (lg == 0 && li < ncol) {
+      const int cc = cb * 16 + li;
+      const int64_t part = ((row0 - a.row_begin + cc / G) * a.H + g * G + cc % G) * a.max_splits + split;
+      a.ws_ml[part * 2] = m_run;
+      a.ws_ml[part * 2 + 1] = l_run;
+    }
+    return;
   }
 
   // ---- merge the 4 waves' partial states, then write the chunk's (m, l, o)
@@ -359,7 +390,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     ml[wave][li][1] = l_run;
   }
   __syncthreads();
-  const int ncol = min(16, G * n - cb * 16);                     // valid columns of the block
   for (int e = threadIdx.x; e < ncol * kD; e += kThreads) {
     const int c = e / kD, d = e % kD;
     const int cc = cb * 16 + c;                                 // (token cc / G, head g*G + cc % G)
@@ -439,13 +469,17 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.Hkv * a.col_blocks, a.max_splits, a.req_end - a.req_begin);
-  if (a.kv_fmt == F_FP8)
-    hipLaunchKernelGGL(decode_split_kernel<F_FP8>, grid, dim3(kThreads), 0, s, a);
-  else if (a.kv_fmt == F_INT8)
-    hipLaunchKernelGGL(decode_split_kernel<F_INT8>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<F_BF16>, grid, dim3(kThreads), 0, s, a);
+  const int B = decode_heads_per_wg(a.kv_fmt == F_BF16 ? 2 : 1, a.Hkv);
+  const dim3 grid(a.Hkv / B * a.col_blocks, a.max_splits, a.req_end - a.req_begin);
+  if (a.kv_fmt == F_FP8) {
+    if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_FP8, kWaves>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<F_FP8, 1>), grid, dim3(kThreads), 0, s, a);
+  } else if (a.kv_fmt == F_INT8) {
+    if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_INT8, kWaves>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

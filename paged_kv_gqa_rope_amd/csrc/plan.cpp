@@ -180,8 +180,10 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
     return tot * d.num_kv_heads;
   };
   const int64_t lo = std::max<int64_t>(64, T);
+  const int64_t min_items = decode_heads_per_wg(io_bytes(d.kv_dtype), d.num_kv_heads) == 4 ? 2 * kMinDecodeItems
+                                                                                           : kMinDecodeItems;
   int64_t c = std::max<int64_t>(kMaxChunk, T), mx = 0;
-  while (count(c, &mx) < kMinDecodeItems && c > lo) c /= 2;
+  while (count(c, &mx) < min_items && c > lo) c /= 2;
   int64_t items = count(c, &mx);
   while (mx > kMaxSplits) {
     c *= 2;
