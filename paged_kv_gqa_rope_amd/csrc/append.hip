@@ -280,6 +280,54 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
   }
 }
 
+// (mean, 1/sqrt(var + eps)) of one head's D elements: fp64 sums in index order.  The
+// row's loads are issued together (all of a bf16 row, half of an fp32 row of 128 at a
+// time) so that one memory latency covers them, and a bf16 row loaded for the mean is
+// reused for the variance.
+template <int IO, int D>
+__device__ __forceinline__ void row_stats(const void* src, int64_t off, bool layer, double eps, double& mean,
+                                          double& inv) {
+  constexpr int NG = D / 8;                       // groups of 8 elements
+  constexpr int BATCH = IO == F_BF16 ? NG : 8;    // groups held in registers at once
+  Raw8 r[BATCH];
+  auto fetch = [&](int g0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) r[b] = load_raw8<IO>(src, off + static_cast<int64_t>(g0 + b) * 8);
+  };
+  mean = 0.0;
+  if (layer) {
+    double s = 0.0;
+#pragma unroll
+    for (int g0 = 0; g0 < NG; g0 += BATCH) {
+      fetch(g0);
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        double x[8];
+        widen8<IO>(r[b], x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += x[i];
+      }
+    }
+    mean = s / static_cast<double>(D);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int g0 = 0; g0 < NG; g0 += BATCH) {
+    if (!(layer && BATCH == NG)) fetch(g0);      // a whole bf16 row is still in r
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      double x[8];
+      widen8<IO>(r[b], x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double d = x[i] - mean;
+        ss += d * d;
+      }
+    }
+  }
+  inv = 1.0 / __builtin_sqrt(ss / static_cast<double>(D) + eps);
+}
+
 __device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row, int r, int i) {
   TokenSlot tk;
   tk.row = row;
@@ -367,27 +415,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
         const void* src = isq ? a.q : a.k;
         const int64_t off = isq ? tk.row * a.q_stride + static_cast<int64_t>(head) * a.D
                                 : tk.row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
-        if (layer) {
-          double s = 0.0;
-          for (int j = 0; j < a.D; j += 8) {
-            double x[8];
-            load8<IO>(src, off + j, x);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s += x[i];
-          }
-          mean = s / static_cast<double>(a.D);
-        }
-        double ss = 0.0;
-        for (int j = 0; j < a.D; j += 8) {
-          double x[8];
-          load8<IO>(src, off + j, x);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const double d = x[i] - mean;
-            ss += d * d;
-          }
-        }
-        inv = 1.0 / __builtin_sqrt(ss / static_cast<double>(a.D) + a.norm_eps);
+        if (a.D == 128) row_stats<IO, 128>(src, off, layer, a.norm_eps, mean, inv);
+        else row_stats<IO, 64>(src, off, layer, a.norm_eps, mean, inv);
       }
       s_stat[u] = make_double2(mean, inv);
     }
