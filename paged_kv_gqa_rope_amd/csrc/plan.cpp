@@ -161,7 +161,8 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   p->ws_ml_off = p->ws_o_off = p->ws_bytes = 0;
   if (!p->fast_decode) return;
   // Split-KV policy: the longest splits (a power of two of at most kMaxChunk keys) that
-  // still give at least kMinDecodeItems (request, kv head, split) items, then doubled
+  // still give at least kMinDecodeItems (request, kv head, split) items (twice that with
+  // 4-head workgroups, see decode_heads_per_wg), then doubled
   // until no request needs more than kMaxSplits splits.  Every split pays a start-up
   // (its first tiles' memory latency) and a merge, so fewer, longer splits stream better,
   // while 5.5 items per CU keep the last round of workgroups short.  Measured on MI355X
