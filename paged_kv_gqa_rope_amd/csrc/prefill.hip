@@ -379,7 +379,6 @@ void prefill_kernel(AttnArgs a, PrefillSched sc) {
   bool q_wait = false;                       // this iteration waits for all loads
 
   float m_run = -INFINITY, l_run = 0.f;      // raw-score max of query l32; this lane's partial sum
-  const bf16x2 kOnes = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   f32x16 o[4];                               // O^T[dim blk*32 + (i/4)*8 + lh*4 + i%4][query l32]
 #pragma unroll
   for (int b = 0; b < 4; ++b)
@@ -465,13 +464,11 @@ void prefill_kernel(AttnArgs a, PrefillSched sc) {
       for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + j], c, -mc));
       const uint32_t w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]), w2 = pack_bf16(p[4], p[5]),
                      w3 = pack_bf16(p[6], p[7]);
-      // The row sum takes the same bf16-rounded P that enters the product, two keys per
-      // dot2.  Its operands are the scalar words: fed lanes of the packed vector, hipcc
-      // emitted v_dot2c_f32_bf16 on the vector's first register four times.
-      float l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, 0.f, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, l, false);
-      l4[ks2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, l, false);
+      // Row sums in plain fp32 adds of the unrounded P (the normaliser then differs from
+      // the sum of the bf16-rounded P by at most 2^-9 relative).  v_dot2c_f32_bf16 would sum
+      // the rounded values, but on gfx950 it waits for the matrix core, so the other wave's
+      // MFMAs in flight stall it; adds issue beside them.
+      l4[ks2] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pb[ks2] = as_bf16x8(u32x4{w0, w1, w2, w3});
     }
     l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
