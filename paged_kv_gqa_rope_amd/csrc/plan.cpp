@@ -161,14 +161,14 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   p->ws_ml_off = p->ws_o_off = p->ws_bytes = 0;
   if (!p->fast_decode) return;
   // Split-KV policy: the longest splits (a power of two of at most kMaxChunk keys) that
-  // still give at least kMinDecodeItems (request, kv head, split) items (twice that with
-  // 4-head workgroups, see decode_heads_per_wg), then doubled
+  // still give at least kMinDecodeItems (request, kv head, split) items, then doubled
   // until no request needs more than kMaxSplits splits.  Every split pays a start-up
   // (its first tiles' memory latency) and a merge, so fewer, longer splits stream better,
   // while 5.5 items per CU keep the last round of workgroups short.  Measured on MI355X
   // (split pass, us, at 1024 / 2048 / 4096-key splits): 64 MHA requests of 512..4096 keys
   // 373 / 372 / 380; 128 GQA-8 requests of 256..4096 keys 249 / 220 / 219; 16 fp8 requests
-  // of 16K..32K keys 165 / 161 / 162 (512: 186).  Deterministic in the lengths.
+  // of 16K..32K keys 165 / 161 / 162 (512: 186) with one-head workgroups, 150 / 143 with
+  // 4-head workgroups (at 512: 160).  Deterministic in the lengths.
   const int64_t T = d.tokens_per_block;
   auto count = [&](int64_t c, int64_t* max_s) {
     int64_t tot = 0, mx = 0;
@@ -181,10 +181,8 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
     return tot * d.num_kv_heads;
   };
   const int64_t lo = std::max<int64_t>(64, T);
-  const int64_t min_items = decode_heads_per_wg(io_bytes(d.kv_dtype), d.num_kv_heads) == 4 ? 2 * kMinDecodeItems
-                                                                                           : kMinDecodeItems;
   int64_t c = std::max<int64_t>(kMaxChunk, T), mx = 0;
-  while (count(c, &mx) < min_items && c > lo) c /= 2;
+  while (count(c, &mx) < kMinDecodeItems && c > lo) c /= 2;
   int64_t items = count(c, &mx);
   while (mx > kMaxSplits) {
     c *= 2;

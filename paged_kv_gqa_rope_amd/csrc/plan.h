@@ -48,10 +48,9 @@ constexpr int32_t kMaxDecodeCols = 64;
 constexpr int32_t kPrefillMaxReqs = 512;
 // The split pass gives a workgroup 4 neighbouring KV heads, one wave each, for a one-byte
 // cache (fp8 / int8) whose KV heads come in fours; otherwise one head, its waves streaming
-// alternate tiles.  A 4-head workgroup holds 4 (request, kv head, split) items and each of
-// its waves streams a whole split, and the split policy then aims at 2 * kMinDecodeItems
-// items (704 workgroups): measured on MI355X, 16 fp8 requests of 16K..32K keys take 150 us
-// at 1024-key splits against 161 us for the one-head workgroups at 2048.
+// alternate tiles.  Measured on MI355X, 16 fp8 requests of 16K..32K keys take 143 us with
+// 4-head workgroups at 2048-key splits, against 150 us at 1024 and 161 us for one-head
+// workgroups at 2048.
 inline int32_t decode_heads_per_wg(int32_t kv_bytes, int32_t num_kv_heads) {
   return kv_bytes == 1 && num_kv_heads % 4 == 0 ? 4 : 1;
 }
