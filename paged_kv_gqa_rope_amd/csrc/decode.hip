@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
   const int kv_bytes = a.kv_fmt == F_FP8 || a.kv_fmt == F_INT8 ? 1 : a.kv_fmt == F_BF16 ? 2 : 4;
-  const int B = a.kv_fmt == F_BF16 ? 1 : decode_heads_per_wg(kv_bytes, a.Hkv);   // the plan's choice
+  const int B = decode_heads_per_wg(kv_bytes, a.Hkv, a.H / a.Hkv, a.col_blocks);
   const dim3 grid(a.Hkv / B * a.col_blocks, a.max_splits, a.req_end - a.req_begin);
   if (a.kv_fmt == F_FP8) {
     if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_FP8, kWaves>), grid, dim3(kThreads), 0, s, a);
@@ -479,7 +479,8 @@ hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
     if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_INT8, kWaves>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1>), grid, dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1>), grid, dim3(kThreads), 0, s, a);
+    if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_BF16, kWaves>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -46,13 +46,18 @@ constexpr int32_t kMaxDecodeCols = 64;
 // The persistent context kernel orders up to kPrefillMaxReqs requests per launch (larger
 // batches take several launches).
 constexpr int32_t kPrefillMaxReqs = 512;
-// The split pass gives a workgroup 4 neighbouring KV heads, one wave each, for a one-byte
-// cache (fp8 / int8) whose KV heads come in fours; otherwise one head, its waves streaming
-// alternate tiles.  Measured on MI355X, 16 fp8 requests of 16K..32K keys take 143 us with
-// 4-head workgroups at 2048-key splits, against 150 us at 1024 and 161 us for one-head
-// workgroups at 2048.
-inline int32_t decode_heads_per_wg(int32_t kv_bytes, int32_t num_kv_heads) {
-  return kv_bytes == 1 && num_kv_heads % 4 == 0 ? 4 : 1;
+// The split pass gives a workgroup 4 neighbouring KV heads, one wave each, when the KV
+// heads come in fours and either the cache is one byte per element (fp8 / int8) or it is
+// bf16 with groups of at least 8 query heads and one block of 16 columns; otherwise one
+// head, its waves streaming alternate tiles.  Measured on MI355X at 2048-key splits (split
+// pass): 16 fp8 requests of 16K..32K keys 143 us against 161 with one-head workgroups (150
+// at 1024-key splits); 128 bf16 GQA-8 requests of 256..4096 keys 203 against 219; but 64
+// bf16 MHA requests 397 against 370, and the GQA-8 requests with 4 draft tokens each (two
+// column blocks) 492 against 415, so those keep one head per workgroup.
+inline int32_t decode_heads_per_wg(int32_t kv_bytes, int32_t num_kv_heads, int32_t group, int32_t col_blocks) {
+  if (num_kv_heads % 4 != 0) return 1;
+  if (kv_bytes == 1) return 4;
+  return kv_bytes == 2 && group >= 8 && col_blocks == 1 ? 4 : 1;
 }
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
 constexpr bool kHaveFastDecode = true;

@@ -330,6 +330,10 @@ HEAD_GROUP_CASES = [
     (8, 256, 2, W.BF16, None),
     (4, 64, 2, W.BF16, 3),
     (8, 16, 1, W.INT8, 5),
+    (4, 16, 8, W.BF16, None),        # bf16 with 4-head workgroups (groups of 8+, one column block)
+    (8, 64, 16, W.BF16, None),
+    (4, 32, 8, W.BF16, 2),           # 16 columns: still one block
+    (4, 64, 8, W.BF16, 3),           # two column blocks: one head per workgroup
 ]
 
 
