@@ -10,10 +10,11 @@
 //
 // Pass 1, 4 waves per workgroup.  A workgroup takes one (generation request, KV head,
 // chunk) and its waves stream alternate tiles of the chunk, their states merged in LDS at
-// the end -- or, for a one-byte cache (fp8 / int8) with the KV heads in fours, 4
-// neighbouring KV heads, one wave each, every wave streaming all tiles of the chunk for
-// its head: the four waves of a CU then read the neighbouring 128-byte pieces of the same
-// cache rows at about the same time, which HBM serves faster than one head's pieces
+// the end -- or, with the KV heads in fours and a one-byte cache (fp8 / int8), or a bf16
+// cache read by GQA groups of 8 or more query heads in one block of columns (see
+// decode_heads_per_wg), 4 neighbouring KV heads, one wave each, every wave streaming all
+// tiles of the chunk for its head: the four waves then read the neighbouring pieces of the
+// same cache rows at about the same time, which HBM serves faster than one head's pieces
 // alone.  Per wave and tile:
 //   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, loaded straight
 //     from HBM in operand layout; B = the G query heads of the KV head (GQA group,
