@@ -360,20 +360,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
     const int b0 = threadIdx.x * per, b1 = min(b0 + per, B);
     int32_t local = 0;
     for (int b = b0; b < b1; ++b) local += a.ctx_len[b];
-    __shared__ int32_t s_part[kAppendThreads];
-    s_part[threadIdx.x] = local;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int32_t run = 0;
-      for (int w = 0; w < kAppendThreads; ++w) {
-        const int32_t x = s_part[w];
-        s_part[w] = run;
-        run += x;
-      }
-      s_cu[0] = 0;
+    // exclusive prefix of `local` over the threads: a shuffle scan inside each wave, then
+    // the totals of the waves before
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    int32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t y = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += y;
     }
+    __shared__ int32_t s_wave[kAppendThreads / kWave];
+    if (lane == kWave - 1) s_wave[wv] = incl;
+    if (threadIdx.x == 0) s_cu[0] = 0;
     __syncthreads();
-    int32_t run = s_part[threadIdx.x];
+    int32_t run = incl - local;
+    for (int w = 0; w < wv; ++w) run += s_wave[w];
     for (int b = b0; b < b1; ++b) {
       run += a.ctx_len[b];
       s_cu[b + 1] = run;
