@@ -291,12 +291,15 @@ int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Opt-in per-kernel timing for measurement tools.  While enabled, every kernel launch of
- * the library is bracketed by HIP events recorded on its stream (this adds no
- * synchronisation).  pkv_kernel_timings() synchronises on those events, writes up to
- * max_entries kernel names (static strings) and durations in milliseconds, returns the
- * number of entries recorded since the last pkv_kernel_timing_enable(1) (which clears the
- * record), and may be called only from the thread that launched.  Not graph-capturable.
+ * Opt-in per-kernel timing for measurement tools.  pkv_kernel_timing_enable(1) creates a
+ * pool of 8192 HIP events (once; they are reused) and clears the record; while enabled,
+ * every kernel launch of the library is bracketed by two events of the pool recorded on
+ * its stream (no synchronisation, no allocation inside the entry points).  Once the pool
+ * is used up, further launches are not timed.  pkv_kernel_timings() synchronises on the
+ * recorded events, writes up to max_entries kernel names (static strings) and durations in
+ * milliseconds, returns the number of entries recorded since the last
+ * pkv_kernel_timing_enable(1), sets pkv_last_error() to the number of untimed launches if
+ * any, and may be called only from the thread that launched.  Not graph-capturable.
  */
 int32_t pkv_kernel_timing_enable(int32_t on);
 int32_t pkv_kernel_timings(const char** names, float* milliseconds, int32_t max_entries);

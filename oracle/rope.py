@@ -68,7 +68,10 @@ def rope_gptj(x: np.ndarray, positions: np.ndarray, cos_t: np.ndarray, sin_t: np
 
 
 def rope_apply(style: str, x, positions, cos_t, sin_t, rot_dim: int):
-    """style 'neox' (pairs j, j + R/2) or 'gptj' (pairs 2j, 2j + 1)."""
+    """style 'neox' (pairs j, j + R/2), 'gptj' (pairs 2j, 2j + 1) or 'none' (no rotation:
+    the values as given)."""
+    if style == "none":
+        return np.array(x, dtype=np.float64)
     if style == "neox":
         return rope_neox(x, positions, cos_t, sin_t, rot_dim)
     if style == "gptj":

@@ -21,7 +21,39 @@ int set_err(int code, const std::string& msg) {
   return code;
 }
 
+// ---------------------------------------------------------------- per-device facts
+// Looked up once per device (the first call that launches on it), then read from here.
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+  int cus = 0;   // compute units
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+bool g_dev_ready[kMaxDevices] = {};
+
+hipError_t device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_ready[dev]) {
+    DeviceInfo info;
+    e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_dev[dev] = info;
+    g_dev_ready[dev] = true;
+  }
+  *out = g_dev[dev];
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- opt-in kernel timing
+// pkv_kernel_timing_enable(1) creates the events up front (kTimingEvents of them, kept for
+// reuse); a launch while timing is on takes two from that pool and records them on its
+// stream, so entry points never create events.  When the pool runs dry, later launches are
+// not timed (pkv_kernel_timings reports how many were dropped through pkv_last_error).
+constexpr size_t kTimingEvents = 8192;
 struct TimingRec {
   const char* name;
   hipEvent_t beg, end;
@@ -30,39 +62,30 @@ std::mutex g_tmu;
 bool g_timing = false;
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_spare;
-
-hipEvent_t take_event() {
-  if (!g_spare.empty()) {
-    hipEvent_t e = g_spare.back();
-    g_spare.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
+size_t g_events = 0;        // events created so far (all in g_spare or g_recs)
+size_t g_dropped = 0;       // launches not timed because the pool was empty
 
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
-  bool on;
+  hipEvent_t b = nullptr, e = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
-    on = g_timing;
+    if (!g_timing) return launch();
+    if (g_spare.size() >= 2) {
+      e = g_spare.back();
+      g_spare.pop_back();
+      b = g_spare.back();
+      g_spare.pop_back();
+    } else {
+      ++g_dropped;
+    }
   }
-  if (!on) return launch();
-  hipEvent_t b, e;
-  {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    b = take_event();
-    e = take_event();
-  }
-  if (b) (void)hipEventRecord(b, s);
+  if (!b) return launch();
+  (void)hipEventRecord(b, s);
   const hipError_t err = launch();
-  if (e) (void)hipEventRecord(e, s);
-  if (b && e) {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    g_recs.push_back({name, b, e});
-  }
+  (void)hipEventRecord(e, s);
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_recs.push_back({name, b, e});
   return err;
 }
 
@@ -277,7 +300,10 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
   a.out_fmt = fp8_out ? pkv::F_FP8 : a.io_fmt;
   a.out_mul = fp8_out ? static_cast<float>(1.0 / static_cast<double>(out_scale)) : 1.f;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
+  DeviceInfo dev;
+  hipError_t e = device_info(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  a.num_cus = dev.cus;
   if (plan.num_ctx > 0) {
     a.req_begin = 0;
     a.req_end = plan.num_ctx;
@@ -332,6 +358,15 @@ int32_t pkv_kernel_timing_enable(int32_t on) {
     g_spare.push_back(r.end);
   }
   g_recs.clear();
+  g_dropped = 0;
+  if (on) {
+    while (g_events < kTimingEvents) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return set_err(PKV_ERR_HIP, "event create failed");
+      g_spare.push_back(e);
+      ++g_events;
+    }
+  }
   g_timing = on != 0;
   return PKV_OK;
 }
@@ -347,6 +382,7 @@ int32_t pkv_kernel_timings(const char** names, float* milliseconds, int32_t max_
     if (names) names[i] = g_recs[i].name;
     if (milliseconds) milliseconds[i] = ms;
   }
+  if (g_dropped) g_err = std::to_string(g_dropped) + " launches were not timed (event pool exhausted)";
   return n;
 }
 

@@ -66,6 +66,7 @@ struct AttnArgs {
   int32_t col_blocks;            // blocks of 16 (token, query head) columns per (request, kv head)
   float* ws_ml;             // [generation rows][H][max_splits][2]
   float* ws_o;              // [generation rows][H][max_splits][D]
+  int32_t num_cus;               // compute units of the device
 };
 
 hipError_t launch_rope_table(double base, int32_t rot, int32_t max_pos, double* cos_sin, hipStream_t s);

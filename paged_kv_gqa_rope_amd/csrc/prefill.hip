@@ -620,10 +620,8 @@ template <int NW, int G, int NS>
 hipError_t launch_t(const AttnArgs& a0, const int32_t* host_n, const int32_t* host_S, hipStream_t s) {
   static_assert(NW % G == 0, "a workgroup holds whole query groups");
   constexpr int ROWS = (NW / G) * 32;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
+  const int cus = std::max(a0.num_cus, 1);
+  hipError_t e = hipSuccess;
   const int groups = a0.Hkv % kXcds == 0 ? kXcds : 1;
   for (int b0 = a0.req_begin; b0 < a0.req_end; b0 += kPrefillMaxReqs) {
     AttnArgs a = a0;

@@ -35,7 +35,8 @@ def make_desc(shape, rope: bool = True, max_num_tokens: int | None = None) -> L.
     d.tokens_per_block = shape.tokens_per_block
     d.io_dtype = DTYPE_CODE[shape.io_dtype]
     d.kv_dtype = DTYPE_CODE[shape.kv_dtype]
-    style = {"neox": L.PKV_ROPE_NEOX, "gptj": L.PKV_ROPE_GPTJ}[getattr(shape, "rope_style", "neox")]
+    style = {"neox": L.PKV_ROPE_NEOX, "gptj": L.PKV_ROPE_GPTJ, "none": L.PKV_ROPE_NONE}[
+        getattr(shape, "rope_style", "neox")]
     d.rope_style = style if rope else L.PKV_ROPE_NONE
     d.rotary_dim = shape.rotary_dim
     d.softmax_scale = 0.0
@@ -92,7 +93,9 @@ class PagedStep:
     """Buffers and ABI calls for one batch: history fill, append, attention."""
 
     def __init__(self, batch, device="cuda", sentinel: bool = True, fill_history: bool = True,
-                 history_tokens_per_call: int = 65536):
+                 history_tokens_per_call: int = 65536, rope_table: np.ndarray | None = None):
+        """``rope_table``: optional fp64 [max_pos, rotary_dim/2, 2] cos/sin table handed to the
+        append instead of the one the library's pkv_rope_cos_sin fills."""
         self.batch = batch
         self.device = torch.device(device)
         sh = batch.shape
@@ -120,8 +123,16 @@ class PagedStep:
             self.pool.view(torch.uint8).fill_(0xFF)
         self.max_pos = max(int(batch.sequence_lengths.max()) if batch.num_requests else 1, 1)
         self.rot = sh.rot_dim
-        self.rope = torch.empty((self.max_pos, self.rot // 2, 2), dtype=torch.float64, device=self.device)
-        L.check(L.pkv_rope_cos_sin(float(sh.rope_theta), self.rot, self.max_pos, self.rope.data_ptr(), self.stream))
+        if rope_table is not None:
+            tab = np.ascontiguousarray(rope_table, dtype=np.float64)
+            if tab.ndim != 3 or tab.shape[0] < self.max_pos or tab.shape[1:] != (self.rot // 2, 2):
+                raise ValueError(f"rope_table of shape {tab.shape} does not cover ({self.max_pos}, {self.rot // 2}, 2)")
+            self.max_pos = int(tab.shape[0])
+            self.rope = torch.from_numpy(tab).to(self.device)
+        else:
+            self.rope = torch.empty((self.max_pos, self.rot // 2, 2), dtype=torch.float64, device=self.device)
+            L.check(L.pkv_rope_cos_sin(float(sh.rope_theta), self.rot, self.max_pos, self.rope.data_ptr(),
+                                       self.stream))
         self.norm = None
         if getattr(sh, "qk_norm", "none") != "none":
             prm = batch.norm_params()

@@ -25,6 +25,16 @@ def rand_unit(rng, shape):
 
 
 # ------------------------------------------------------------------ RoPE
+def test_rope_style_none_stores_the_values_as_given():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((9, 2, 64))
+    cos_t, sin_t = R.neox_tables(1e4, 64, 40)
+    y = R.rope_apply("none", x, rng.integers(0, 40, 9), cos_t, sin_t, 64)
+    assert np.array_equal(y, x) and y is not x
+    with pytest.raises(ValueError):
+        R.rope_apply("rotate", x, np.zeros(9, int), cos_t, sin_t, 64)
+
+
 @pytest.mark.parametrize("rot", [64, 128, 32])
 def test_rope_identity_at_position_zero_and_norm_preserving(rot):
     rng = np.random.default_rng(1)

@@ -53,3 +53,24 @@ def test_values_are_exact_in_the_io_format():
     # bf16 values are the float32 draws truncated to their upper half
     raw = W._rng(b.seed, "q", 0).standard_normal(q.shape, dtype=np.float32)
     assert np.array_equal(q, (raw.view(np.uint32) >> 16).astype(np.uint16))
+
+
+def test_workload5_scales_are_fitted_to_its_values():
+    """Workload 5's stored fp8 scales (and the int8 ones of its variant) are the fit of
+    its drawn values: amax / 448 (int8: amax / 127) for K and V separately."""
+    b = W.workload(5)
+    am = W.kv_amax(b)
+    assert (b.shape.k_scale, b.shape.v_scale) == W.fit_kv_scales(b, W.FP8_E4M3, am)
+    assert W.W5_INT8_SCALES == W.fit_kv_scales(b, W.INT8, am)
+    for s in (b.shape.k_scale, b.shape.v_scale) + W.W5_INT8_SCALES:
+        assert np.frexp(s)[0] != 0.5, "a fitted scale that is a power of two tests nothing new"
+    assert b.shape.k_scale != b.shape.v_scale
+
+
+def test_small_fitted_scales():
+    s5 = W.small_workload(5)
+    ak, av = W.kv_amax(s5)
+    assert s5.shape.k_scale == float(np.float32(ak / 448)) and s5.shape.v_scale == float(np.float32(av / 448))
+    assert 5.0 < ak < 7.0 and 5.0 < av < 7.0
+    i8 = W.fitted(W.small_workload(2), W.INT8)
+    assert i8.shape.kv_dtype == W.INT8 and i8.shape.k_scale == W.fit_kv_scales(i8, W.INT8)[0]

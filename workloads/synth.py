@@ -20,6 +20,12 @@ are returned the same way; they count as already rotated, and each side writes
 them into its own cache representation (for an fp8 or int8 cache that means its
 own quantiser).
 
+Scales of a one-byte cache are fitted to the data (``fit_kv_scales``): for K and
+for V separately, the largest magnitude over every drawn value (history and new
+tokens, as drawn) divided by the largest code magnitude (448 for e4m3, 127 for
+int8), rounded to float32.  Such a scale is generally not a power of two, so the
+quantiser's 1/scale is inexact.
+
 Nothing here rotates, rounds to a storage format, scatters into pages or
 attends: those are the method, and each compared side implements them itself.
 """
@@ -145,6 +151,14 @@ class Batch:
         return {"q_weight": one + quarter * g[0], "k_weight": one + quarter * g[1],
                 "q_bias": quarter * g[2], "k_bias": quarter * g[3]}
 
+    def drawn_float32(self, which: str, r: int) -> np.ndarray:
+        """Request r's draw ``which`` (new_k, hist_v, ...) as the float32 values it
+        stands for: for bf16 the stored upper half widened back (a bit operation)."""
+        x = getattr(self, which)(r)
+        if self.shape.io_dtype == BF16:
+            return (x.astype(np.uint32) << 16).view(np.float32)
+        return x
+
     def packed(self, which: str) -> np.ndarray:
         """Concatenate new_q / new_k / new_v over requests in packed row order."""
         parts = [getattr(self, which)(r) for r in range(self.num_requests)]
@@ -183,6 +197,41 @@ def make_batch(shape: Shape, ctx=(), gen_past=(), seed: int = 0, pool_blocks_min
     return Batch(shape, seed, types, n, s, table, pool, label)
 
 
+CODE_MAX = {FP8_E4M3: 448.0, INT8: 127.0}
+
+
+def kv_amax(batch: Batch) -> tuple[float, float]:
+    """Largest magnitude over every drawn key, and over every drawn value (history and
+    new tokens, as drawn, before any rotation)."""
+    ak = av = 0.0
+    for r in range(batch.num_requests):
+        for which in ("hist_k", "new_k"):
+            x = batch.drawn_float32(which, r)
+            if x.size:
+                ak = max(ak, float(np.max(np.abs(x))))
+        for which in ("hist_v", "new_v"):
+            x = batch.drawn_float32(which, r)
+            if x.size:
+                av = max(av, float(np.max(np.abs(x))))
+    return ak, av
+
+
+def fit_kv_scales(batch: Batch, kv_dtype: str, amax: tuple[float, float] | None = None) -> tuple[float, float]:
+    """(s_K, s_V) that fit the batch's drawn values to the codes of ``kv_dtype``:
+    amax|K| / the largest code magnitude, likewise for V; computed in fp64, rounded to
+    float32.  A rotated new key can exceed amax|K| by up to sqrt(2) and then saturates."""
+    ak, av = kv_amax(batch) if amax is None else amax
+    cm = CODE_MAX[kv_dtype]
+    return float(np.float32(ak / cm)), float(np.float32(av / cm))
+
+
+def fitted(batch: Batch, kv_dtype: str | None = None) -> Batch:
+    """The batch with its cache format (or ``kv_dtype``) and scales fitted to its data."""
+    kv = kv_dtype or batch.shape.kv_dtype
+    sk, sv = fit_kv_scales(batch, kv)
+    return with_shape(batch, kv_dtype=kv, k_scale=sk, v_scale=sv)
+
+
 # ---- the five workloads --------------------------------------------------
 SHAPES = {
     1: Shape("tiny-mixed-fp32", 4, 2, 64, 16, FP32, FP32, 1.0e4),
@@ -190,9 +239,13 @@ SHAPES = {
     # one batch of 8 x 2048 prompt tokens: its token budget is its own size
     3: Shape("prefill-gqa4-bf16", 32, 8, 128, 64, BF16, BF16, 5.0e5, max_num_tokens=16384),
     4: Shape("mixed-gqa8-bf16", 64, 8, 128, 64, BF16, BF16, 5.0e5),
+    # K/V scaled to fit: fit_kv_scales(workload(5), FP8_E4M3), stored because fitting draws
+    # all 0.8 G history values (a CPU test recomputes them)
     5: Shape("longdecode-gqa4-fp8kv", 32, 8, 128, 64, BF16, FP8_E4M3, 5.0e5,
-             k_scale=2.0 ** -6, v_scale=2.0 ** -6),
+             k_scale=0.013392857275903225, v_scale=0.01311383955180645),
 }
+# the same fit of workload 5's values to int8 codes (amax / 127)
+W5_INT8_SCALES = (0.04724409431219101, 0.046259842813014984)
 
 
 def _uniform_pasts(seed: int, count: int, lo: int, hi: int) -> list[int]:
@@ -220,7 +273,8 @@ def workload(k: int) -> Batch:
 def small_workload(k: int, shape: Shape | None = None) -> Batch:
     """Workload k at a size the oracle finishes in seconds: same heads,
     head_dim, block size and dtypes; several blocks and a ragged tail.  ``shape``
-    replaces workload k's shape (same lengths and seeds)."""
+    replaces workload k's shape (same lengths and seeds); without it, workload 5's
+    fp8 scales are fitted to the small batch's own values."""
     seed = 2000 + k
     sh = SHAPES[k] if shape is None else shape
     if k == 1:
@@ -233,7 +287,8 @@ def small_workload(k: int, shape: Shape | None = None) -> Batch:
         return make_batch(sh, ctx=[(128, 0), (192, 128), (100, 384)],
                           gen_past=_uniform_pasts(seed, 6, 20, 500), seed=seed, label="s4")
     if k == 5:
-        return make_batch(sh, gen_past=_uniform_pasts(seed, 4, 1000, 3000), seed=seed, label="s5")
+        b = make_batch(sh, gen_past=_uniform_pasts(seed, 4, 1000, 3000), seed=seed, label="s5")
+        return b if shape is not None else fitted(b)
     raise KeyError(k)
 
 
