@@ -50,6 +50,8 @@ extern "C" {
 #endif
 
 #define PKV_ABI_VERSION 1
+/* bytes of the per-GPU scratch array of pkv_attention_forward_noalloc */
+#define PKV_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -289,6 +291,25 @@ int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch
                                       const void* q, int64_t q_row_stride, const void* kv_pool,
                                       float out_scale_quant_orig, void* out,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_attention_forward for callers that cannot allocate or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  The split-KV
+ * partial results go to the library's own device scratch array instead of a caller
+ * workspace: one array of PKV_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends.  Nothing is allocated; the
+ * array's device address is looked up once per device.  Arguments, results and errors
+ * as for pkv_attention_forward, and additionally PKV_ERR_WORKSPACE (nothing launched)
+ * when the batch needs more scratch than the array holds (pkv_workspace_size_for_batch
+ * gives the need).  Nothing in the array has to start at zero (every partial result a
+ * call reads was written earlier in the same call).  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (several streams, or several threads)
+ * race and must be serialised by the caller.
+ */
+int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch_desc* batch,
+                                      const void* q, int64_t q_row_stride, const void* kv_pool,
+                                      void* out, void* stream);
+
 
 /*
  * Opt-in per-kernel timing for measurement tools.  pkv_kernel_timing_enable(1) creates a

@@ -24,6 +24,7 @@ PKV_ERR_WORKSPACE = -7
 PKV_ERR_HIP = -8
 
 PKV_FP32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
+PKV_SCRATCH_BYTES = 64 << 20        # the per-GPU scratch array of pkv_attention_forward_noalloc
 PKV_REQ_CONTEXT, PKV_REQ_GENERATION = 0, 1
 PKV_ROPE_NONE, PKV_ROPE_NEOX, PKV_ROPE_GPTJ = 0, 1, 2
 PKV_NORM_NONE, PKV_NORM_RMS, PKV_NORM_LAYER = 0, 1, 2
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_attention_forward_fp8_out.argtypes = [D, Bt, vp, i64, vp, ctypes.c_float, vp, vp, sz, vp]
         L.pkv_attention_forward_fp8_out.restype = i32
         L.pkv_attention_forward.restype = i32
+        L.pkv_attention_forward_noalloc.argtypes = [D, Bt, vp, i64, vp, vp, vp]
+        L.pkv_attention_forward_noalloc.restype = i32
         L.pkv_kernel_timing_enable.argtypes = [i32]
         L.pkv_kernel_timing_enable.restype = i32
         L.pkv_kernel_timings.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i32]
@@ -167,6 +170,12 @@ def pkv_attention_forward_fp8_out(desc, batch, q, q_row_stride, kv_pool, out_sca
                                   workspace_bytes, stream) -> int:
     return lib().pkv_attention_forward_fp8_out(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, kv_pool,
                                                out_scale_quant_orig, out, workspace, workspace_bytes, stream)
+
+
+def pkv_attention_forward_noalloc(desc, batch, q, q_row_stride, kv_pool, out, stream) -> int:
+    return lib().pkv_attention_forward_noalloc(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, kv_pool,
+                                               out, stream)
+
 
 
 def pkv_kernel_timing_enable(on: bool) -> int:

@@ -249,9 +249,11 @@ int32_t pkv_append_qknorm_rope(const pkv_attn_desc* desc, const pkv_batch_desc* 
                      kv_pool, stream);
 }
 
+// use_scratch: the split-KV partials go to the library's scratch array instead of the
+// caller's workspace (workspace and workspace_bytes are then ignored).
 static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
                               int64_t q_row_stride, const void* kv_pool, void* out, bool fp8_out, float out_scale,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
   std::string err;
   int rc = pkv::validate_desc(desc, err);
   if (rc != PKV_OK) return set_err(rc, err);
@@ -265,6 +267,19 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
   if (!aligned16(out) || !aligned16(kv_pool)) return set_err(PKV_ERR_INVALID_ARG, "out and kv_pool must be 16-byte aligned");
   if (fp8_out && !(std::isfinite(out_scale) && out_scale > 0.f && std::isfinite(1.0f / out_scale)))
     return set_err(PKV_ERR_INVALID_ARG, "out_scale_quant_orig must be finite and > 0 (with a finite reciprocal)");
+  if (use_scratch) {
+    if (plan.ws_bytes > pkv::kScratchBytes)
+      return set_err(PKV_ERR_WORKSPACE, "this batch needs " + std::to_string(plan.ws_bytes) +
+                                            " bytes of scratch; the library's scratch array holds " +
+                                            std::to_string(pkv::kScratchBytes));
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (plan.ws_bytes > 0) {
+      const hipError_t se = pkv::scratch_device_pointer(&workspace);
+      if (se != hipSuccess) return hip_fail(se, "scratch symbol lookup");
+      workspace_bytes = pkv::kScratchBytes;
+    }
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return set_err(PKV_ERR_WORKSPACE, "workspace of " + std::to_string(plan.ws_bytes) + " bytes required, " +
@@ -349,6 +364,11 @@ int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch
                                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, true, out_scale_quant_orig, workspace,
                         workspace_bytes, stream);
+}
+
+int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
+                                      int64_t q_row_stride, const void* kv_pool, void* out, void* stream) {
+  return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, false, 1.f, nullptr, 0, stream, true);
 }
 
 int32_t pkv_kernel_timing_enable(int32_t on) {

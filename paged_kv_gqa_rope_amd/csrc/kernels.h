@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv.h"
 #include "plan.h"
 
 namespace pkv {
@@ -68,6 +69,12 @@ struct AttnArgs {
   float* ws_o;              // [generation rows][H][max_splits][D]
   int32_t num_cus;               // compute units of the device
 };
+
+// Bytes of the library's device scratch array (one per GPU) used by the entry point that
+// allocates nothing.
+constexpr size_t kScratchBytes = PKV_SCRATCH_BYTES;
+// Device address of this device's scratch array (looked up once per device).
+hipError_t scratch_device_pointer(void** out);
 
 hipError_t launch_rope_table(double base, int32_t rot, int32_t max_pos, double* cos_sin, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);

@@ -215,3 +215,17 @@ def test_workspace_bounds_cover_every_batch():
             if need > 0:
                 expect(L.PKV_ERR_WORKSPACE, forward(d, hb, ws_bytes=need - 1))
                 expect(L.PKV_ERR_WORKSPACE, forward(d, hb, ws=None))
+
+
+def test_noalloc_rejects_a_batch_beyond_its_scratch_before_any_launch():
+    """The scratch entry point checks the batch's need against its array's size on the host."""
+    d = L.pkv_attn_desc()
+    d.num_heads, d.num_kv_heads, d.head_dim, d.tokens_per_block = 64, 8, 128, 64
+    d.io_dtype = d.kv_dtype = L.PKV_BF16
+    d.rope_style, d.max_num_tokens = L.PKV_ROPE_NEOX, 1 << 20
+    B, S = 2048, 4096
+    hb = HostBatch([1] * B, [1] * B, [S] * B, np.arange(B * 64, dtype=np.int32), B * 64)
+    need = L.pkv_workspace_size_for_batch(d, hb.desc)
+    assert need > L.PKV_SCRATCH_BYTES
+    rc = L.pkv_attention_forward_noalloc(d, hb.desc, 16, 128 * 64, 16, 16, None)
+    assert rc == L.PKV_ERR_WORKSPACE and "scratch" in L.pkv_last_error()
