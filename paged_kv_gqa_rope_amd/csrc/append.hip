@@ -27,21 +27,43 @@ constexpr int kAppendThreads = 256;
 constexpr int kMaxTokensPerWg = 8;
 constexpr int kFlatMaxRequests = 4096;
 
+// Streaming accesses: every input element is read once and every output element written
+// once per step, so stores, and loads of inputs nothing reads again, carry the
+// nontemporal hint.  (With a q/k norm the statistics pass reads q and k first; their
+// second read then comes from the caches, so those loads stay ordinary.)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *static_cast<const uint4*>(p);
+  }
+}
+__device__ __forceinline__ void st16(void* p, uint4 u) {
+  __builtin_nontemporal_store(u32x4_t{u.x, u.y, u.z, u.w}, static_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st8(void* p, uint2 u) {
+  __builtin_nontemporal_store(u32x2_t{u.x, u.y}, static_cast<u32x2_t*>(p));
+}
+
 // 8 raw io elements as loaded (bf16: one 16-byte vector; fp32: two)
 struct Raw8 {
   uint4 a, b;
 };
 
-template <int F>
+template <int F, bool NT = false>
 __device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {
   Raw8 r;
   if constexpr (F == F_BF16) {
-    r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    r.a = ld16<NT>(static_cast<const uint16_t*>(base) + off);
     r.b = make_uint4(0, 0, 0, 0);
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
-    r.a = p[0];
-    r.b = p[1];
+    const float* p = static_cast<const float*>(base) + off;
+    r.a = ld16<NT>(p);
+    r.b = ld16<NT>(p + 4);
   }
   return r;
 }
@@ -62,44 +84,32 @@ __device__ __forceinline__ void widen8(const Raw8& r, double (&x)[8]) {
   }
 }
 
-template <int F>
+template <int F, bool NT = false>
 __device__ __forceinline__ void load8(const void* base, int64_t off, double (&x)[8]) {
-  if constexpr (F == F_BF16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = static_cast<double>(bf16_to_f32(w[i] & 0xFFFFu));
-      x[2 * i + 1] = static_cast<double>(bf16_to_f32(w[i] >> 16));
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
+  widen8<F>(load_raw8<F, NT>(base, off), x);
 }
 
 // Round y (times `mul` for fp8 and int8) once to format F and store 8 elements at base+off.
 template <int F>
 __device__ __forceinline__ void store8(void* base, int64_t off, const double (&y)[8], double mul) {
   if constexpr (F == F_FP32) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
-    p[0] = make_float4(static_cast<float>(y[0]), static_cast<float>(y[1]), static_cast<float>(y[2]),
-                       static_cast<float>(y[3]));
-    p[1] = make_float4(static_cast<float>(y[4]), static_cast<float>(y[5]), static_cast<float>(y[6]),
-                       static_cast<float>(y[7]));
+    float* p = static_cast<float*>(base) + off;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = __float_as_uint(static_cast<float>(y[i]));
+    st16(p, make_uint4(w[0], w[1], w[2], w[3]));
+    st16(p + 4, make_uint4(w[4], w[5], w[6], w[7]));
   } else if constexpr (F == F_BF16) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = f64x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    st16(static_cast<uint16_t*>(base) + off, make_uint4(w[0], w[1], w[2], w[3]));
   } else {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       w[i / 4] |= (F == F_INT8 ? f64_to_int8(y[i] * mul) : f64_to_e4m3(y[i] * mul)) << (8 * (i % 4));
-    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + off) = make_uint2(w[0], w[1]);
+    st8(static_cast<uint8_t*>(base) + off, make_uint2(w[0], w[1]));
   }
 }
 
@@ -161,6 +171,7 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
                                             const void* __restrict__ v, const double* __restrict__ cs_base,
                                             void* __restrict__ q_out, void* __restrict__ pool,
                                             const double2* __restrict__ stat) {
+  constexpr bool NTQK = !NORM;               // q/k read only here (no norm statistics pass)
   const int R = RS != kRopeNone ? a.R : 0;
   const int half = R / 2;
   const int rg = R / 16, pg = (a.D - R) / 8, vg = a.D / 8;
@@ -189,7 +200,7 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
   };
   if (t < nhc * rg) {                                       // rotated pair groups
     if (tk.m >= a.max_pos) return;
-    const int hc = t / rg, j0 = (t % rg) * 8;
+    const int hc = t / max(rg, 1), j0 = (t % max(rg, 1)) * 8;
     const int h0 = hc * kHeadsPerRotTask;
     const int nh = min(kHeadsPerRotTask, qk - h0);
     Raw8 r1[kHeadsPerRotTask], r2[kHeadsPerRotTask];
@@ -199,8 +210,8 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
         const void* src;
         int64_t off;
         head_src(h0 + u, src, off);
-        r1[u] = load_raw8<IO>(src, off + off_a(j0));
-        r2[u] = load_raw8<IO>(src, off + off_b(j0));
+        r1[u] = load_raw8<IO, NTQK>(src, off + off_a(j0));
+        r2[u] = load_raw8<IO, NTQK>(src, off + off_b(j0));
       }
     }
     const double2* cs = reinterpret_cast<const double2*>(cs_base) + static_cast<int64_t>(tk.m) * half + j0;
@@ -265,7 +276,7 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
     int64_t off;
     head_src(head, src, off);
     double x[8];
-    load8<IO>(src, off + j, x);
+    load8<IO, NTQK>(src, off + j, x);
     normalise(x, head, j);
     if (head < Hq)
       store8<IO>(q_out, tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D + j, x, 1.0);
@@ -275,7 +286,7 @@ __device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot
     t -= nhc * rg + qk * pg;
     const int g = t / vg, j = (t % vg) * 8;
     double x[8];
-    load8<IO>(v, tk.row * a.kv_stride + static_cast<int64_t>(g) * a.D + j, x);
+    load8<IO, true>(v, tk.row * a.kv_stride + static_cast<int64_t>(g) * a.D + j, x);
     if (tk.blk >= 0) store8<KV>(pool, pool_off(1, g) + j, x, a.inv_v_scale);
   }
 }
