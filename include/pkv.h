@@ -325,6 +325,17 @@ int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch
 int32_t pkv_kernel_timing_enable(int32_t on);
 int32_t pkv_kernel_timings(const char** names, float* milliseconds, int32_t max_entries);
 
+/*
+ * Tuning and testing control of the generation (decode) split pass, which shares the
+ * batch's 32-key tiles among a fixed number of workgroups: by default two per compute unit
+ * of the device (at most 1024), never more than the batch has tiles.  n > 0 caps that
+ * number at n for later calls from any thread of the process; n = 0 restores the default;
+ * n < 0 only queries.  Returns the setting in force before the call.  Results stay within
+ * the documented accuracy for every setting; they are bitwise reproducible for a fixed
+ * setting and device.
+ */
+int32_t pkv_set_decode_workgroups(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

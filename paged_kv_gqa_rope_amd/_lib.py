@@ -116,6 +116,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_attention_forward_noalloc.restype = i32
         L.pkv_kernel_timing_enable.argtypes = [i32]
         L.pkv_kernel_timing_enable.restype = i32
+        L.pkv_set_decode_workgroups.argtypes = [i32]
+        L.pkv_set_decode_workgroups.restype = i32
         L.pkv_kernel_timings.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i32]
         L.pkv_kernel_timings.restype = i32
         _lib = L
@@ -176,6 +178,11 @@ def pkv_attention_forward_noalloc(desc, batch, q, q_row_stride, kv_pool, out, st
     return lib().pkv_attention_forward_noalloc(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, kv_pool,
                                                out, stream)
 
+
+
+def pkv_set_decode_workgroups(n: int) -> int:
+    """Cap the decode split pass's workgroups at n (0: default, < 0: query); returns the old cap."""
+    return lib().pkv_set_decode_workgroups(int(n))
 
 
 def pkv_kernel_timing_enable(on: bool) -> int:

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -53,6 +54,9 @@ hipError_t device_info(DeviceInfo* out) {
 // reuse); a launch while timing is on takes two from that pool and records them on its
 // stream, so entry points never create events.  When the pool runs dry, later launches are
 // not timed (pkv_kernel_timings reports how many were dropped through pkv_last_error).
+// Cap on the decode split pass's workgroups (0: the default, kDecodeWGsPerCU per CU).
+std::atomic<int32_t> g_decode_wgs{0};
+
 constexpr size_t kTimingEvents = 8192;
 struct TimingRec {
   const char* name;
@@ -337,8 +341,13 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
     a.max_n = plan.max_gen_n;
     a.col_blocks = plan.col_blocks;
     if (plan.fast_decode) {
-      a.chunk = plan.chunk;
-      a.max_splits = plan.max_splits;
+      a.dec_heads = plan.dec_heads;
+      a.dec_cols = plan.dec_cols;
+      const int32_t cap = g_decode_wgs.load(std::memory_order_relaxed);
+      const int64_t target = cap > 0 ? cap : static_cast<int64_t>(pkv::kDecodeWGsPerCU) * std::max(dev.cus, 1);
+      a.dec_wgs = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(target, plan.dec_max_wgs)));
+      a.ws_pre = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan.ws_pre_off);
+      a.ws_row = a.ws_pre + (plan.num_gen + 1);
       a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_off);
       a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_off);
       e = timed("decode_split", s, [&] { return pkv::launch_decode_split(a, s); });
@@ -369,6 +378,11 @@ int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch
 int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
                                       int64_t q_row_stride, const void* kv_pool, void* out, void* stream) {
   return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, false, 1.f, nullptr, 0, stream, true);
+}
+
+int32_t pkv_set_decode_workgroups(int32_t n) {
+  if (n < 0) return g_decode_wgs.load();
+  return g_decode_wgs.exchange(n);
 }
 
 int32_t pkv_kernel_timing_enable(int32_t on) {

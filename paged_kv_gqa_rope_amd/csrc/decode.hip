@@ -2,23 +2,26 @@
 //
 // "TensorRT-LLM 1.0 study notes", 6.3: a generation request has one query token that
 // attends to every cached token, reached block by block through the block table; the
-// phase is bound by HBM bandwidth.  This design splits each request's keys into
-// chunks so that even a handful of long requests fills all 256 CUs, and merges the
-// per-chunk partial results (running max m, sum l, unnormalised output o) in a
-// second pass with the same rescaling identity FlashAttention uses to merge tiles
-// (study notes 6.2, update of acc_o by the new running max).
+// phase is bound by HBM bandwidth.  This design cuts the batch's keys into pieces so that
+// even a handful of long requests fills all 256 CUs, and merges the per-piece partial
+// results (running max m, sum l, unnormalised output o) in a second pass with the same
+// rescaling identity FlashAttention uses to merge tiles (study notes 6.2, update of acc_o
+// by the new running max).
 //
-// Pass 1, 4 waves per workgroup.  A workgroup takes one (generation request, KV head,
-// chunk) and its waves stream alternate tiles of the chunk, their states merged in LDS at
-// the end -- or, with the KV heads in fours and a one-byte cache (fp8 / int8), or a bf16
-// cache read by GQA groups of 8 or more query heads in one block of columns (see
-// decode_heads_per_wg), 4 neighbouring KV heads, one wave each, every wave streaming all
-// tiles of the chunk for its head: the four waves then read the neighbouring pieces of the
-// same cache rows at about the same time, which HBM serves faster than one head's pieces
-// alone.  Per wave and tile:
+// Pass 1 is persistent and balanced: a fixed number of workgroups (two per CU) share the
+// batch's 32-key tiles of every (request, KV head group, block of 16 query columns)
+// segment in equal contiguous ranges, so each streams the same number of bytes whatever
+// the mix of lengths, and each XCD takes one contiguous eighth of them.  A workgroup has
+// 4 waves.  With one KV head per segment its waves stream alternate tiles of a piece,
+// their states merged in LDS at the end; with the KV heads in fours and a one-byte cache
+// (fp8 / int8), or a bf16 cache read by GQA groups of 8 or more query heads in one block
+// of columns (see decode_heads_per_wg), a segment holds 4 neighbouring KV heads, one wave
+// each, every wave streaming all tiles of the piece for its head: the four waves then read
+// the neighbouring pieces of the same cache rows at about the same time, which HBM serves
+// faster than one head's pieces alone.  Per wave and tile:
 //   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, loaded straight
 //     from HBM in operand layout; B = the G query heads of the KV head (GQA group,
-//     G <= 16, padded with zero heads), kept in registers for the whole chunk.
+//     G <= 16, padded with zero heads), kept in registers for the whole piece.
 //   * online softmax per head on the accumulators (lanes l, l^16, l^32, l^48 hold the
 //     same head), exp2 with the log2(e) factor folded into the scale.
 //   * O += P V on MFMA: A = P (heads x 32 keys) straight from the score registers,
@@ -26,8 +29,9 @@
 //   * an fp8 or int8 cache is dequantised to bf16 on load (exact: every e4m3 value
 //     and every integer -128 .. 127 is a bf16 value); k_scale folds into the softmax
 //     scale and v_scale into the combine, so the pass works on raw codes times one.
-// Pass 2, one workgroup per (request, query head): M = max m_s, L = sum 2^(m_s-M) l_s,
-// O = sum 2^(m_s-M) o_s / L in a fixed order (no atomics: bitwise reproducible).
+// Pass 2, one workgroup per (request, query head): M = max m_p, L = sum 2^(m_p-M) l_p,
+// O = sum 2^(m_p-M) o_p / L over the segment's pieces in a fixed order (no atomics:
+// bitwise reproducible).
 #include <math.h>
 
 #include "device_common.h"
@@ -46,17 +50,26 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 32;          // keys per wave iteration
 constexpr int kD = 128;            // head_dim handled here
 constexpr int kVStride = 136;      // LDS row stride (bf16 elements) of a staged V tile
+constexpr int kXcds = 8;           // XCDs of the chip, each with its own L2
+constexpr int kPieceBatch = 32;    // pieces listed at a time by the split pass
+constexpr int kCombHeads = 4;      // query heads (one wave each) per combine workgroup
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// 16 bytes of the cache, streamed.  Every K/V byte is read once per step and every load
-// instruction covers whole rows (whole 128-byte lines), so the loads carry the
-// nontemporal hint: lines are not kept for reuse that will not come.
+// 16 bytes of the cache.  With one column block every K/V byte is read once per step and
+// every load instruction covers whole rows (whole 128-byte lines), so the loads carry the
+// nontemporal hint (NT): lines are not kept for reuse that will not come.  With several
+// column blocks (draft tokens) the other blocks read the same lines soon after: plain loads.
+template <bool NT>
 __device__ __forceinline__ uint4 load_kv(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *static_cast<const uint4*>(p);
+  }
 }
 // K tile in LDS: 16-byte chunk c of key row r sits at chunk position c ^ (r & 15), so the
 // 16 rows one MFMA operand read touches at one chunk fall on 16 distinct bank groups.
@@ -107,66 +120,104 @@ struct TileRegs {
   uint4 v[KV == F_BF16 ? 8 : 4];
 };
 
-// B: KV heads per workgroup (1, or kWaves: one per wave).
-template <int KV, int B>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
-  static_assert(B == 1 || B == kWaves, "one head per workgroup, or one per wave");
-  // KV head (group) fastest: the workgroups of every head of one (request, chunk) run
-  // side by side.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
-  const int hgs = a.Hkv / B;                                   // head groups
-  const int g = (blockIdx.x % hgs) * B + (B == 1 ? 0 : wave);  // this wave's KV head
-  const int cb = blockIdx.x / hgs, split = blockIdx.y, rg = blockIdx.z;
-  const int r = a.req_begin + rg;
-  // device lengths, kept to n >= 1 and S >= n whatever they hold
-  const int n = max(a.ctx_len[r], 1);                          // 1, or 1 + draft tokens
-  const int S = max(a.seq_len[r], n);
-  const int G = a.H / a.Hkv;
-  const int k0 = split * a.chunk;
-  if (k0 >= S || split >= a.max_splits || cb * 16 >= G * n) return;   // uniform over the block
-  const int kend = min(k0 + a.chunk, S);
-  const int lane = threadIdx.x % kWave;
-  const int li = lane % 16, lg = lane / 16;
-  // Columns of the score tile: (token, query head) pairs, 16 per column block.  Lane
-  // column li is token tok = gc / G of the request (position S - n + tok; it sees keys up
-  // to that position: causal among a request's draft tokens) and head g*G + gc % G.
-  const int gc = cb * 16 + li, tok = gc / G;
-  const bool col_ok = tok < n;
-  const int key_lim = col_ok ? S - n + tok : -1;               // keys 0 .. key_lim
-  const int64_t row0 = a.max_n == 1 ? static_cast<int64_t>(a.row_begin) + rg : wave_prefix(a.ctx_len, r);
-  if (row0 < a.row_begin || row0 + n > a.N) return;             // rows outside the generation rows: skip
-  const int64_t row = row0 + min(tok, n - 1);
-  const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
-  // The block table is read-only here: reading it through the constant address space
-  // keeps its (wave-uniform) reads on the scalar unit, out of the vector-load queue.
-  const __attribute__((address_space(4))) int32_t* table =
-      (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(r) * a.mbps);
+__device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+__device__ __forceinline__ int64_t max64(int64_t x, int64_t y) { return x > y ? x : y; }
+// End key of tiles [.., t_end) of a request with S keys: min(t_end * 32, S), without
+// forming t_end * 32 when it is past S.
+__device__ __forceinline__ int tiles_end(int t_end, int S) { return t_end > (S - 1) / kTile ? S : t_end * kTile; }
 
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
+// Generation request r as the split pass sees it (device lengths, kept to n >= 1 and
+// S >= n whatever they hold): n new tokens, S keys, `tiles` 32-key tiles, and `cbs` blocks
+// of 16 (token, query head) columns per KV head.  Its work units are its 32-key tiles
+// times its (head group, column block) segments.
+struct ReqGeom {
+  int n, S, tiles, cbs;
+};
+__device__ __forceinline__ ReqGeom req_geom(const AttnArgs& a, int r, int G) {
+  ReqGeom q;
+  q.n = max(a.ctx_len[r], 1);
+  q.S = max(a.seq_len[r], q.n);
+  q.tiles = (q.S - 1) / kTile + 1;
+  q.cbs = static_cast<int>(min64((static_cast<int64_t>(G) * q.n + 15) / 16, a.col_blocks));
+  return q;
+}
+__device__ __forceinline__ int64_t req_units(const ReqGeom& q, int hgs) {
+  return static_cast<int64_t>(hgs) * q.cbs * q.tiles;
+}
 
-  // B operand Q^T: column li, dims ks*32 + lg*8 + j (the dim order inside a
-  // contraction is free as long as K uses the same one).
-  bf16x8 qf[4];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
-                         static_cast<int64_t>(g * G + gc % G) * kD + lg * 8;
+// Exclusive prefix sum of v over the workgroup's kThreads threads; *total gets the sum.
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* total, int64_t* part) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int64_t x = v;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 32);
-      if (!col_ok) u = make_uint4(0, 0, 0, 0);
-      qf[ks] = as_bf16x8(u);
-    }
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
   }
-  const float xscale = a.scale_log2 * a.k_scale;
-  float m_run = -INFINITY, l_run = 0.f;                         // for column li
-  f32x4 o[8];                                                   // O[column lg*4+i][dim nb*16+li]
+  if (lane == kWave - 1) part[w] = x;
+  __syncthreads();
+  int64_t before = 0, tot = 0;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kWaves; ++i) {
+    before += i < w ? part[i] : 0;
+    tot += part[i];
+  }
+  *total = tot;
+  return before + x - v;
+}
 
-  const int ntiles = (kend - k0 + kTile - 1) / kTile;
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Pieces of a workgroup's range, as listed in LDS: (request, head group, column block,
+// first tile) and (tiles, n, S, packed row of the request's first token).
+struct Piece {
+  int r, hg, cb, t0, nt, n, S, row0;
+};
+__device__ __forceinline__ Piece read_piece(const int4* pa, const int4* pb, int p) {
+  const int4 x = pa[p], y = pb[p];
+  Piece q;
+  q.r = __builtin_amdgcn_readfirstlane(x.x);
+  q.hg = __builtin_amdgcn_readfirstlane(x.y);
+  q.cb = __builtin_amdgcn_readfirstlane(x.z);
+  q.t0 = __builtin_amdgcn_readfirstlane(x.w);
+  q.nt = __builtin_amdgcn_readfirstlane(y.x);
+  q.n = __builtin_amdgcn_readfirstlane(y.y);
+  q.S = __builtin_amdgcn_readfirstlane(y.z);
+  q.row0 = __builtin_amdgcn_readfirstlane(y.w);
+  return q;
+}
+
+// The np listed pieces as one tile stream per wave.  B: KV heads per segment (1, or
+// kWaves: one per wave).  With B = kWaves a wave's items are all tiles of every piece for
+// its head; with B = 1 the waves share a piece's tiles (wave w takes tiles w, w + 4, ...),
+// every wave having ceil(tiles / 4) items per piece (items past the piece's tiles load its
+// last tile again and compute nothing), so that all waves reach a piece's end, where their
+// states are merged in LDS, at the same item.  Loads run two items ahead of the compute
+// across piece boundaries: a new piece starts with its first tiles already in flight, and
+// only the softmax state and Q are reset.  Each piece leaves one partial state in its slot.
+// NT: stream the cache with the nontemporal hint (every byte read once) or keep its lines
+// in L2 (several column blocks read the same keys).
+template <int KV, int B, bool NT>
+__device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int lw, const int4* pla,
+                                              const int4* plb, uint16_t (*vtile)[kTile * kVStride],
+                                              uint16_t (*ktile)[kTile * kD], float (*ml)[16][2]) {
+  static_assert(B == 1 || B == kWaves, "one head per workgroup, or one per wave");
+  // The thread index passes through an empty asm statement so that nothing derived from
+  // it is hoisted out of the batch loop and kept live across it (registers are tight).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+  const int lane = tid % kWave;
+  const int li = lane % 16, lg = lane / 16;
+  const int G = a.H / a.Hkv, hgs = a.Hkv / B;
+  constexpr int TS = B == 1 ? kWaves : 1;                      // tile stride of a wave's items
+  const int base = B == 1 ? wave : 0;                           // first tile of a wave's items
+  const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
   const int tshift = a.tshift, tmask = a.T - 1;
-  const int last_blk = min((kend - 1) >> tshift, a.mbps - 1);
   const int64_t blk_bytes = 2 * static_cast<int64_t>(a.T) * kv_row * (KV == F_BF16 ? 2 : 1);   // K and V of T slots
   uint16_t* vt = vtile[wave];
   uint16_t* kt = ktile[wave];
@@ -177,44 +228,176 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int kRows = kWave * 16 / (kD * kEB);               // rows per load instruction
   constexpr int kLanes = kWave / kRows;                        // lanes per row
   const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * kEB;
-  uint32_t lane_off[kLoads];                                   // byte offset inside a tile
-#pragma unroll
-  for (int it = 0; it < kLoads; ++it)
-    lane_off[it] = static_cast<uint32_t>(it * kRows + lane / kLanes) * row_bytes + (lane % kLanes) * 16u;
-  // A tile needs no masking when it lies inside the chunk and inside the causal range of
-  // every valid column of the block (the lowest of them is token cb*16 / G).
-  const int lim_all = S - n + (cb * 16) / G;
+  // byte offset of the lane inside load 0 of a tile; load `it` adds it*kRows rows to the
+  // (scalar) base, so one register serves every load
+  const uint32_t lane_off = static_cast<uint32_t>(lane / kLanes) * row_bytes + (lane % kLanes) * 16u;
+  const float xscale = a.scale_log2 * a.k_scale;
 
-  // Block IDs of a tile: tiles are 32-aligned and T is a power of two >= 16, so a tile
-  // lies in one block (T >= 32) or covers two (T = 16).  Read two tiles ahead.
-  auto fetch_ids = [&](int tile, int32_t (&raw)[2]) {
-    const int kb0 = __builtin_amdgcn_readfirstlane((k0 + tile * kTile) >> tshift);
-    raw[0] = __builtin_amdgcn_readfirstlane(table[min(kb0, last_blk)]);
-    raw[1] = __builtin_amdgcn_readfirstlane(table[min(kb0 + 1, last_blk)]);
+  // ---- fetch cursor (wave-uniform): item f_k of piece f_p, with the piece's facts kept in
+  // scalars (the LDS list is read only when the cursor moves to another piece)
+  int f_p = 0, f_k = 0, f_cnt, f_t0, f_nt, f_r, f_hg, f_last;
+  auto fetch_piece = [&](int p) {
+    const Piece q = read_piece(pla, plb, p);
+    f_cnt = (q.nt + TS - 1) / TS;
+    f_t0 = q.t0;
+    f_nt = q.nt;
+    f_r = q.r;
+    f_hg = q.hg;
+    f_last = min((tiles_end(q.t0 + q.nt, q.S) - 1) >> tshift, a.mbps - 1);
   };
-  // Issue every load of tile `tile` (ids already resolved) into `R`.  Loads it < kLoads/2
-  // cover tile rows 0..15, the others rows 16..31, so every load has one scalar base: B0
-  // (the tile's block at the tile's first slot) or B1 (the block of rows 16..31; the
-  // same block unless T = 16).  Rows past the chunk end are still slots of an allocated
-  // block (in bounds); their scores are masked and their V rows zeroed in compute.
-  auto issue = [&](int tile, const int32_t (&rawid)[2], TileRegs<KV>& R) {
-    const int tb = k0 + tile * kTile;
-    int32_t id0 = __builtin_amdgcn_readfirstlane(rawid[0]);
-    int32_t id1 = __builtin_amdgcn_readfirstlane(rawid[1]);
+  // A ticket carries one item to its loads: the block IDs of its tile, its first key and
+  // the wave's KV head.  Tiles are 32-aligned and T is a power of two >= 16, so a tile lies
+  // in one block (T >= 32) or covers two (T = 16).  The block table is read-only here:
+  // reading it through the constant address space keeps its (wave-uniform) reads on the
+  // scalar unit, out of the vector-load queue.  Past the stream's last item the cursor
+  // stays on it (its loads repeat).
+  struct Ticket {
+    int32_t id0, id1;
+    int tb, g;
+  };
+  auto fetch = [&](Ticket& t) {
+    const int tile = f_t0 + min(base + f_k * TS, f_nt - 1);
+    const int kb0 = (tile * kTile) >> tshift;
+    const __attribute__((address_space(4))) int32_t* table =
+        (const __attribute__((address_space(4))) int32_t*)(a.table + static_cast<int64_t>(f_r) * a.mbps);
+    t.id0 = table[min(kb0, f_last)];
+    t.id1 = table[min(kb0 + 1, f_last)];
+    t.tb = tile * kTile;
+    t.g = f_hg * B + (B == 1 ? 0 : wave);
+    if (f_k + 1 < f_cnt) {
+      ++f_k;
+    } else if (f_p + 1 < np) {
+      ++f_p;
+      f_k = 0;
+      fetch_piece(f_p);
+    }
+  };
+  // Issue every load of a ticket's tile into `R`.  Loads it < kLoads/2 cover tile rows
+  // 0..15, the others rows 16..31, so every load has one scalar base: B0 (the tile's block
+  // at the tile's first slot) or B1 (the block of rows 16..31; the same block unless
+  // T = 16).  Rows past the piece end are still slots of an allocated block (in bounds);
+  // their scores are masked and their V rows zeroed in compute.
+  auto issue = [&](const Ticket& t, TileRegs<KV>& R) {
+    int32_t id0 = __builtin_amdgcn_readfirstlane(t.id0);
+    int32_t id1 = __builtin_amdgcn_readfirstlane(t.id1);
     id0 = (id0 >= 0 && id0 < a.num_blocks) ? id0 : 0;
     id1 = (id1 >= 0 && id1 < a.num_blocks) ? id1 : 0;
-    const char* head = static_cast<const char*>(a.pool) + g * (kD * kEB);
-    const char* b0 = head + static_cast<int64_t>(id0) * blk_bytes + static_cast<int64_t>(tb & tmask) * row_bytes;
+    const char* head = static_cast<const char*>(a.pool) + t.g * (kD * kEB);
+    const char* b0 = head + static_cast<int64_t>(id0) * blk_bytes + static_cast<int64_t>(t.tb & tmask) * row_bytes;
     const char* b1 = a.T >= kTile ? b0 : head + static_cast<int64_t>(id1) * blk_bytes - 16 * static_cast<int64_t>(row_bytes);
     const int64_t vofs = static_cast<int64_t>(a.T) * row_bytes;
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) R.k[it] = load_kv((it < kLoads / 2 ? b0 : b1) + lane_off[it]);
+    for (int it = 0; it < kLoads; ++it)
+      R.k[it] = load_kv<NT>((it < kLoads / 2 ? b0 : b1) + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) R.v[it] = load_kv((it < kLoads / 2 ? b0 : b1) + vofs + lane_off[it]);
+    for (int it = 0; it < kLoads; ++it)
+      R.v[it] = load_kv<NT>((it < kLoads / 2 ? b0 : b1) + vofs + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
   };
-  // Online-softmax update and O += P V for tile `tile` held in `R`.
-  auto compute = [&](int tile, const TileRegs<KV>& R) {
-    const int tb = k0 + tile * kTile;
+
+  // ---- state of the piece being computed
+  bf16x8 qf[4];
+  float m_run, l_run;                                           // for column li
+  f32x4 o[8];                                                   // O[column lg*4+i][dim nb*16+li]
+  int key_lim;                                                  // keys 0 .. key_lim for column li
+  int c_t0, c_nt, c_cnt, c_kend, c_lim, c_ncol, c_valid, c_n, c_g, c_cb;
+  int64_t c_slot;
+  auto start_piece = [&](int p) {
+    const Piece q = read_piece(pla, plb, p);
+    const int n = q.n, S = q.S;
+    c_t0 = q.t0;
+    c_nt = q.nt;
+    c_cnt = (q.nt + TS - 1) / TS;
+    c_n = n;
+    c_cb = q.cb;
+    c_g = q.hg * B + (B == 1 ? 0 : wave);                       // this wave's KV head
+    c_kend = tiles_end(q.t0 + q.nt, S);
+    // A tile needs no masking when it lies inside the piece and inside the causal range
+    // of every valid column of the block (the lowest of them is token cb*16 / G).
+    c_lim = S - n + (q.cb * 16) / G;
+    c_ncol = min(min(16, G * n - q.cb * 16), a.dec_cols);       // valid columns of the block
+    c_slot = (static_cast<int64_t>(q.r - a.req_begin) * hgs + q.hg) * a.col_blocks + q.cb + lw;
+    // Columns of the score tile: (token, query head) pairs, 16 per column block.  Lane
+    // column li is token tok = gc / G of the request (position S - n + tok; it sees keys
+    // up to that position: causal among a request's draft tokens) and head g*G + gc % G.
+    const int gc = q.cb * 16 + li, tok = gc / G;
+    const bool col_ok = tok < n;
+    key_lim = col_ok ? S - n + tok : -1;
+    const int64_t row0 = q.row0;
+    c_valid = row0 >= a.row_begin && row0 + n <= a.N;           // rows outside the generation rows: no output
+    const int64_t row = c_valid ? row0 + min(tok, n - 1) : a.row_begin;
+    // B operand Q^T: column li, dims ks*32 + lg*8 + j (the dim order inside a
+    // contraction is free as long as K uses the same one).
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
+                         static_cast<int64_t>(c_g * G + gc % G) * kD + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 32);
+      if (!col_ok) u = make_uint4(0, 0, 0, 0);
+      qf[ks] = as_bf16x8(u);
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Write the piece's partial state (m, l, o) to its slot.
+  auto end_piece = [&]() {
+    const int ncol = c_ncol;
+    if constexpr (B > 1) {
+      // this wave alone holds its head's state for the piece
+      if (c_valid) {
+        const int64_t e0 = (c_slot * B + wave) * a.dec_cols;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = lg * 4 + i;
+          if (c < ncol) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) a.ws_o[(e0 + c) * kD + nb * 16 + li] = o[nb][i];
+          }
+        }
+        if (lg == 0 && li < ncol) {
+          a.ws_ml[(e0 + li) * 2] = m_run;
+          a.ws_ml[(e0 + li) * 2 + 1] = l_run;
+        }
+      }
+    } else {
+      // merge the 4 waves' states in LDS, then write the piece's (m, l, o)
+      __syncthreads();
+      float* red = reinterpret_cast<float*>(&vtile[0][0]);      // [wave][16 columns][kD]
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(wave * 16 + lg * 4 + i) * kD + nb * 16 + li] = o[nb][i];
+      if (lg == 0) {
+        ml[wave][li][0] = m_run;
+        ml[wave][li][1] = l_run;
+      }
+      __syncthreads();
+      if (c_valid) {
+        const int64_t e0 = c_slot * a.dec_cols;
+        for (int e = tid; e < ncol * kD; e += kThreads) {
+          const int c = e / kD, d = e % kD;
+          float M = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w][c][0]);
+          float L = 0.f, O = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float s = ml[w][c][0] == -INFINITY ? 0.f : exp2f(ml[w][c][0] - M);
+            L += s * ml[w][c][1];
+            O += s * red[(w * 16 + c) * kD + d];
+          }
+          a.ws_o[(e0 + c) * kD + d] = O;
+          if (d == 0) {
+            a.ws_ml[(e0 + c) * 2] = M;
+            a.ws_ml[(e0 + c) * 2 + 1] = L;
+          }
+        }
+      }
+      __syncthreads();                                          // LDS free for the next tiles
+    }
+  };
+  auto compute = [&](const int tb, const int kend, const int lim_all, const TileRegs<KV>& R) {
     // K and V rows into this wave's LDS tiles (bf16; an fp8 / int8 cache is dequantised here)
     wave_lds_fence();
     if constexpr (KV == F_BF16) {
@@ -238,7 +421,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if (tb + kTile > kend) {
-      // wave-uniform, last tile of a chunk only: rows at or past the chunk end were read
+      // wave-uniform, last tile of a piece only: rows at or past the piece end were read
       // from unwritten slots; zero their V so that P = 0 times them stays 0
 #pragma unroll
       for (int it = 0; it < kLoads; ++it) {
@@ -336,159 +519,267 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // Software pipeline: the wave's next tile is in flight while a tile is computed (B = 1:
-  // the wave's tiles are w, w + 4, ...; B = 4: every tile).  Loads and ID fetches run
-  // unconditionally (past the wave's last tile they repeat the chunk's last tile), so
-  // every path has the same loads in flight and the compiler's wait before a tile's
-  // compute covers that tile only, not the one issued after it.
-  constexpr int TS = B == 1 ? kWaves : 1;                      // tile stride of a wave
-  TileRegs<KV> ra, rb;
-  int32_t ids_a[2], ids_b[2];
-  const int tl = ntiles - 1;
-  int t = B == 1 ? wave : 0;
-  fetch_ids(min(t, tl), ids_a);
-  issue(min(t, tl), ids_a, ra);
-  fetch_ids(min(t + TS, tl), ids_b);
-  for (; t < ntiles; t += 2 * TS) {
-    issue(min(t + TS, tl), ids_b, rb);
-    fetch_ids(min(t + 2 * TS, tl), ids_a);
-    compute(t, ra);
-    issue(min(t + 2 * TS, tl), ids_a, ra);
-    fetch_ids(min(t + 3 * TS, tl), ids_b);
-    if (t + TS < ntiles) compute(t + TS, rb);
-  }
-  const int ncol = min(16, G * n - cb * 16);                     // valid columns of the block
-  if constexpr (B > 1) {
-    // ---- this wave alone holds its head's state for the chunk: write (m, l, o) as they are
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = lg * 4 + i, cc = cb * 16 + c;
-      if (c < ncol) {
-        const int64_t part = ((row0 - a.row_begin + cc / G) * a.H + g * G + cc % G) * a.max_splits + split;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) a.ws_o[part * kD + nb * 16 + li] = o[nb][i];
-      }
-    }
-    if (lg == 0 && li < ncol) {
-      const int cc = cb * 16 + li;
-      const int64_t part = ((row0 - a.row_begin + cc / G) * a.H + g * G + cc % G) * a.max_splits + split;
-      a.ws_ml[part * 2] = m_run;
-      a.ws_ml[part * 2 + 1] = l_run;
-    }
-    return;
-  }
+  // Compute item k of the current piece from R (nothing for an item past its tiles).
+  auto compute_item = [&](int k, const TileRegs<KV>& R) {
+    const int tile = base + k * TS;
+    if (tile < c_nt && c_valid) compute((c_t0 + tile) * kTile, c_kend, c_lim, R);
+  };
 
-  // ---- merge the 4 waves' partial states, then write the chunk's (m, l, o)
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(&vtile[0][0]);          // [wave][16 heads][kD]
-  __shared__ float ml[kWaves][16][2];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * 16 + lg * 4 + i) * kD + nb * 16 + li] = o[nb][i];
-  if (lg == 0) {
-    ml[wave][li][0] = m_run;
-    ml[wave][li][1] = l_run;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < ncol * kD; e += kThreads) {
-    const int c = e / kD, d = e % kD;
-    const int cc = cb * 16 + c;                                 // (token cc / G, head g*G + cc % G)
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w][c][0]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float s = ml[w][c][0] == -INFINITY ? 0.f : exp2f(ml[w][c][0] - M);
-      L += s * ml[w][c][1];
-      O += s * red[(w * 16 + c) * kD + d];
+  // Software pipeline over the stream: the next item's loads are in flight while an item
+  // is computed and its block IDs are read one item further ahead; every path has the same
+  // loads in flight, so the compiler's wait before an item's compute covers that item only.
+  TileRegs<KV> ra, rb;
+  Ticket ta, tb;
+  fetch_piece(0);
+  fetch(ta);
+  issue(ta, ra);                                                // item 0
+  fetch(tb);                                                    // item 1
+  int cp = 0, ck = 0;                                           // item in compute
+  start_piece(0);
+  while (true) {
+    issue(tb, rb);
+    fetch(ta);
+    compute_item(ck, ra);
+    if (ck + 1 == c_cnt) {
+      end_piece();
+      if (cp + 1 >= np) break;
+      ++cp;
+      ck = 0;
+      start_piece(cp);
+    } else {
+      ++ck;
     }
-    const int64_t tok_row = row0 - a.row_begin + cc / G;        // generation row of the token
-    const int64_t part = (tok_row * a.H + g * G + cc % G) * a.max_splits + split;
-    a.ws_o[part * kD + d] = O;
-    if (d == 0) {
-      a.ws_ml[part * 2] = M;
-      a.ws_ml[part * 2 + 1] = L;
+    issue(ta, ra);
+    fetch(tb);
+    compute_item(ck, rb);
+    if (ck + 1 == c_cnt) {
+      end_piece();
+      if (cp + 1 >= np) break;
+      ++cp;
+      ck = 0;
+      start_piece(cp);
+    } else {
+      ++ck;
     }
   }
 }
 
-// One workgroup of kD threads per (generation token, query head).  Thread s < ns
-// first loads split s's (m, l); a fixed-shape tree gives M = max m and L = sum 2^(m-M) l;
-// then thread d sums 2^(m_s-M) o_s[d] over the splits in order, eight loads in flight.
-// Splits past a draft token's position hold m = -inf and weigh nothing; split 0 always
-// holds key 0, so M is finite.
-__global__ __launch_bounds__(kD) void decode_combine_kernel(AttnArgs a) {
-  static_assert(kD >= 128, "one thread per split needs kD >= kMaxSplits");
-  const int h = blockIdx.x, rg = blockIdx.y, tok = blockIdx.z, t = threadIdx.x;
-  const int r = a.req_begin + rg;
-  if (tok >= a.ctx_len[r]) return;                                  // uniform
-  const int S = a.seq_len[r];
-  const int ns = min((S + a.chunk - 1) / a.chunk, a.max_splits);
-  const int64_t row = (a.max_n == 1 ? static_cast<int64_t>(a.row_begin) + rg : wave_prefix(a.ctx_len, r)) + tok;
-  if (row < a.row_begin || row >= a.N) return;                      // uniform: outside the generation rows
-  const int64_t base = ((row - a.row_begin) * a.H + h) * a.max_splits;
-  __shared__ float s_w[kD];
-  __shared__ float s_red[kD / kWave];
-  const float m_t = t < ns ? a.ws_ml[(base + t) * 2] : -INFINITY;
-  const float l_t = t < ns ? a.ws_ml[(base + t) * 2 + 1] : 0.f;   // 0 wherever m_t = -inf
-  float M = wave_max(m_t);
-  if (t % kWave == 0) s_red[t / kWave] = M;
-  __syncthreads();
-  M = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kD / kWave; ++w) M = fmaxf(M, s_red[w]);
-  const float w_t = t < ns && m_t != -INFINITY ? exp2f(m_t - M) : 0.f;
-  s_w[t] = w_t;
-  float L = wave_sum(w_t * l_t);
-  __syncthreads();
-  if (t % kWave == 0) s_red[t / kWave] = L;
-  __syncthreads();
-  L = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kD / kWave; ++w) L += s_red[w];
-  float o = 0.f;
-  const float* op = a.ws_o + base * kD + t;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = op[static_cast<int64_t>(s + u) * kD];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) o += s_w[s + u] * v[u];
+// Persistent split pass: gridDim.x workgroups share the batch's work units (32-key tiles
+// of every (request, head group, column block) segment, requests in order, then head
+// group, then column block, then keys) in equal contiguous ranges, so every workgroup
+// streams the same number of K/V bytes whatever the mix of lengths.  A workgroup's range
+// cuts the segments it touches into pieces; each piece leaves one partial state in slot
+// (segment index + workgroup index), which is unique because both grow along the units.
+// Launched workgroup w runs on XCD w % 8 (round-robin dispatch); it takes range
+// (w % 8) * (W / 8) + w / 8, so each XCD (one L2) works through one contiguous eighth.
+template <int KV, int B, bool NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
+  __shared__ float ml[kWaves][16][2];
+  __shared__ int64_t part[2 * kWaves];
+  __shared__ int64_t start[3], walk[4];
+  __shared__ int4 pla[kPieceBatch], plb[kPieceBatch];
+  __shared__ int pcount;
+  const int G = a.H / a.Hkv, hgs = a.Hkv / B;
+  const int R = a.req_end - a.req_begin;
+  // units of this thread's run of requests, and where the run starts in the unit order
+  const int per = (R + kThreads - 1) / kThreads;
+  const int i0 = min(static_cast<int>(threadIdx.x) * per, R), i1 = min(i0 + per, R);
+  int64_t mine = 0, mrows = 0;
+  for (int i = i0; i < i1; ++i) {
+    mine += req_units(req_geom(a, a.req_begin + i, G), hgs);
+    mrows += a.ctx_len[a.req_begin + i];
   }
-  for (; s < ns; ++s) o += s_w[s] * op[static_cast<int64_t>(s) * kD];
-  const float val = o * (a.v_scale / L);
-  const int64_t oi = row * a.H * kD + static_cast<int64_t>(h) * kD + t;
-  if (a.out_fmt == F_FP8)
-    static_cast<uint8_t*>(a.out)[oi] = static_cast<uint8_t>(f32_to_e4m3(val * a.out_mul));
-  else
-    static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16(val));
+  int64_t U, rows_total;
+  const int64_t before = block_exclusive_scan(mine, &U, part);
+  const int64_t rows_before = block_exclusive_scan(mrows, &rows_total, part + kWaves);
+  const int W = gridDim.x, w = blockIdx.x;
+  const int lw = W % kXcds == 0 ? (w % kXcds) * (W / kXcds) + w / kXcds : w;
+  const int64_t u0 = static_cast<int64_t>(lw) * U / W, u1 = static_cast<int64_t>(lw + 1) * U / W;
+  // The thread whose run holds unit u0 records its request, offset and first row;
+  // workgroup 0 also records every request's first unit (and the total) and first packed
+  // row for the combine.  Rows: the generation rows follow each other in request order.
+  if ((u0 >= before && u0 < before + mine) || w == 0) {
+    int64_t acc = before, racc = a.row_begin + rows_before;
+    for (int i = i0; i < i1; ++i) {
+      const int64_t units = req_units(req_geom(a, a.req_begin + i, G), hgs);
+      if (w == 0) {
+        a.ws_pre[i] = acc;
+        a.ws_row[i] = racc;
+      }
+      if (u0 >= acc && u0 < acc + units) {
+        start[0] = i;
+        start[1] = u0 - acc;
+        start[2] = racc;
+      }
+      acc += units;
+      racc += a.ctx_len[a.req_begin + i];
+    }
+    if (w == 0 && threadIdx.x == 0) {
+      a.ws_pre[R] = U;
+      a.ws_row[R] = a.row_begin + rows_total;
+    }
+  }
+  __syncthreads();
+  if (u0 >= u1) return;                                         // empty range (uniform)
+  if (threadIdx.x == 0) {
+    walk[0] = start[0];
+    walk[1] = start[1];
+    walk[2] = u1 - u0;
+    walk[3] = start[2];
+  }
+  // Thread 0 cuts the range into pieces, kPieceBatch at a time, into LDS; the waves then
+  // stream them.  Only the LDS list lives across batches.
+  while (true) {
+    if (threadIdx.x == 0) {
+      int r = a.req_begin + static_cast<int>(walk[0]);
+      int64_t off = walk[1], left = walk[2], row0 = walk[3];
+      int np = 0;
+      while (left > 0 && r < a.req_end && np < kPieceBatch) {
+        const ReqGeom q = req_geom(a, r, G);
+        const int64_t units = req_units(q, hgs);
+        if (off < units) {
+          const int64_t j = off / q.tiles;                       // segment of the request
+          const int t0 = static_cast<int>(off - j * q.tiles);
+          const int take = static_cast<int>(min64(q.tiles - t0, left));
+          pla[np] = make_int4(r, static_cast<int>(j / q.cbs), static_cast<int>(j % q.cbs), t0);
+          plb[np] = make_int4(take, q.n, q.S, static_cast<int>(min64(max64(row0, -1), a.N)));
+          ++np;
+          left -= take;
+          off += take;
+        }
+        if (off >= units) {
+          row0 += a.ctx_len[r];
+          ++r;
+          off = 0;
+        }
+      }
+      walk[0] = r - a.req_begin;
+      walk[1] = off;
+      walk[2] = left;
+      walk[3] = row0;
+      pcount = np;
+    }
+    __syncthreads();
+    const int np = __builtin_amdgcn_readfirstlane(pcount);
+    if (np == 0) return;                                        // uniform
+    decode_stream<KV, B, NT>(a, np, lw, pla, plb, vtile, ktile, ml);
+    __syncthreads();                                            // the list is read before it is refilled
+  }
+}
+
+// One wave per (generation token, query head), kCombHeads query heads per workgroup, two
+// dimensions per lane.  The pieces of the token's segment are the workgroups whose unit
+// ranges meet the segment's units (found from the recorded first units and the same range
+// arithmetic).  M = max m_p and L = sum 2^(m_p-M) l_p over them, then lane d sums
+// 2^(m_p-M) o_p[2d, 2d+1] over the pieces in order.  64 pieces at a time: lane p holds
+// piece p's (m, l), butterfly reductions give M and L in a fixed order, and the first
+// eight o_p are loaded before the weights are known.  Every metadata load is issued
+// before the first use.  Pieces past a draft token's position hold m = -inf and weigh
+// nothing; the piece holding key 0 makes M finite.
+__global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(AttnArgs a) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int h = blockIdx.x * kCombHeads + wave, rg = blockIdx.y, tok = blockIdx.z;
+  const int r = a.req_begin + rg;
+  const int R = a.req_end - a.req_begin, W = a.dec_wgs;
+  const int n_dev = a.ctx_len[r], s_dev = a.seq_len[r];
+  const int64_t P = a.ws_pre[rg], U = a.ws_pre[R], row0 = a.ws_row[rg];
+  if (h >= a.H || tok >= n_dev) return;                             // wave-uniform
+  const int G = a.H / a.Hkv, B = a.dec_heads, hgs = a.Hkv / B;
+  const int n = max(n_dev, 1), S = max(s_dev, n);                   // as the split pass keeps them
+  const int tiles = (S - 1) / kTile + 1;
+  const int cbs = static_cast<int>(min64((static_cast<int64_t>(G) * n + 15) / 16, a.col_blocks));
+  const int64_t row = row0 + tok;
+  if (row < a.row_begin || row >= a.N) return;                      // outside the generation rows
+  const int g = h / G, hg = g / B, wv = g % B;
+  const int c = tok * G + h % G, cb = c / 16, col = c % 16;
+  if (cb >= cbs || col >= a.dec_cols || U <= 0 || W <= 0) return;
+  const int64_t s0 = P + (static_cast<int64_t>(hg) * cbs + cb) * tiles, s1 = s0 + tiles;
+  const int64_t f = ((s0 + 1) * W - 1) / U, l = (s1 * W - 1) / U;  // first and last range
+  const int lwf = static_cast<int>(min64(max64(f, 0), W - 1));
+  const int np = static_cast<int>(min64(max64(l, lwf), W - 1)) - lwf + 1;
+  const int64_t seg = (static_cast<int64_t>(rg) * hgs + hg) * a.col_blocks + cb;
+  const int64_t stride = static_cast<int64_t>(B) * a.dec_cols;      // entries between pieces
+  const int64_t e0 = ((seg + lwf) * B + wv) * a.dec_cols + col;    // entry of the first piece
+  const float2* op = reinterpret_cast<const float2*>(a.ws_o + e0 * kD) + lane;
+  const int64_t ps = stride * (kD / 2);                             // float2 steps between pieces
+  const float* mlp = a.ws_ml + e0 * 2;
+  float2 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = k < np ? op[k * ps] : make_float2(0.f, 0.f);
+  float M = -INFINITY;
+  for (int pb = 0; pb < np; pb += kWave) {
+    const int p = pb + lane;
+    M = fmaxf(M, wave_max(p < np ? mlp[p * stride * 2] : -INFINITY));
+  }
+  float L = 0.f, ox = 0.f, oy = 0.f;
+  for (int pb = 0; pb < np; pb += kWave) {
+    const int p = pb + lane;
+    float wt = 0.f, lp = 0.f;
+    if (p < np) {
+      const float2 mlv = *reinterpret_cast<const float2*>(mlp + p * stride * 2);
+      wt = mlv.x == -INFINITY ? 0.f : exp2f(mlv.x - M);
+      lp = mlv.y;
+    }
+    L += wave_sum(wt * lp);
+    const int cnt = min(kWave, np - pb);
+    int k = 0;
+    if (pb == 0) {
+#pragma unroll
+      for (; k < 8; ++k) {
+        const float w = __shfl(wt, k, kWave);                      // 0 past the last piece
+        ox += w * v[k].x;
+        oy += w * v[k].y;
+      }
+    }
+    for (; k < cnt; k += 8) {                                      // eight loads in flight
+      float2 u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = k + e < cnt ? op[(pb + k + e) * ps] : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = __shfl(wt, k + e, kWave);                  // u[e] = 0 past the last piece
+        ox += w * u[e].x;
+        oy += w * u[e].y;
+      }
+    }
+  }
+  const float sc = a.v_scale / L;
+  const int64_t oi = (row * a.H + h) * kD + 2 * lane;
+  if (a.out_fmt == F_FP8) {
+    const uint32_t lo = f32_to_e4m3(ox * sc * a.out_mul), hi = f32_to_e4m3(oy * sc * a.out_mul);
+    *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + oi) = static_cast<uint16_t>(lo | (hi << 8));
+  } else {
+    const uint32_t lo = f32_to_bf16(ox * sc), hi = f32_to_bf16(oy * sc);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) = lo | (hi << 16);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  const int kv_bytes = a.kv_fmt == F_FP8 || a.kv_fmt == F_INT8 ? 1 : a.kv_fmt == F_BF16 ? 2 : 4;
-  const int B = decode_heads_per_wg(kv_bytes, a.Hkv, a.H / a.Hkv, a.col_blocks);
-  const dim3 grid(a.Hkv / B * a.col_blocks, a.max_splits, a.req_end - a.req_begin);
+  const dim3 grid(a.dec_wgs);
+  const bool nt = a.col_blocks == 1;
   if (a.kv_fmt == F_FP8) {
-    if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_FP8, kWaves>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<F_FP8, 1>), grid, dim3(kThreads), 0, s, a);
+    if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_FP8, kWaves, true>), grid, dim3(kThreads), 0, s, a);
+    else if (nt) hipLaunchKernelGGL((decode_split_kernel<F_FP8, 1, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<F_FP8, 1, false>), grid, dim3(kThreads), 0, s, a);
   } else if (a.kv_fmt == F_INT8) {
-    if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_INT8, kWaves>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1>), grid, dim3(kThreads), 0, s, a);
+    if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_INT8, kWaves, true>), grid, dim3(kThreads), 0, s, a);
+    else if (nt) hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (B == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_BF16, kWaves>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1>), grid, dim3(kThreads), 0, s, a);
+    if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_BF16, kWaves, true>), grid, dim3(kThreads), 0, s, a);
+    else if (nt) hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.H, a.req_end - a.req_begin, a.max_n);
-  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kD), 0, s, a);
+  const dim3 grid((a.H + kCombHeads - 1) / kCombHeads, a.req_end - a.req_begin, a.max_n);
+  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kCombHeads * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -62,11 +62,15 @@ struct AttnArgs {
   int32_t req_begin, req_end;    // requests [begin, end) handled by this launch
   int32_t row_begin;             // packed row of request req_begin
   int32_t max_n;                 // largest n_r among the handled requests
-  // split-KV decode
-  int32_t chunk, max_splits;
+  // split-KV decode (persistent, balanced split pass)
   int32_t col_blocks;            // blocks of 16 (token, query head) columns per (request, kv head)
-  float* ws_ml;             // [generation rows][H][max_splits][2]
-  float* ws_o;              // [generation rows][H][max_splits][D]
+  int32_t dec_heads;             // KV heads per segment (1, or 4: one per wave)
+  int32_t dec_cols;              // columns stored per (piece, KV head): min(16, G * max_n)
+  int32_t dec_wgs;               // workgroups of the split pass
+  int64_t* ws_pre;               // [generation requests + 1] first unit of each request, total last
+  int64_t* ws_row;               // [generation requests + 1] first packed row of each request
+  float* ws_ml;                  // [slots][dec_heads][dec_cols][2]  (m, l) per piece
+  float* ws_o;                   // [slots][dec_heads][dec_cols][D]  o per piece
   int32_t num_cus;               // compute units of the device
 };
 

@@ -155,61 +155,50 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   p->fast_decode = p->num_gen > 0 && desc_fast_decode(d) && G * p->max_gen_n <= kMaxDecodeCols;
   p->col_blocks = (G * p->max_gen_n + 15) / 16;
   p->fast_prefill = p->num_ctx > 0 && desc_fast_prefill(d);
-  p->chunk = 0;
-  p->max_splits = 0;
-  p->decode_items = 0;
-  p->ws_ml_off = p->ws_o_off = p->ws_bytes = 0;
+  p->dec_heads = p->dec_cols = 0;
+  p->dec_units = p->dec_segments = p->dec_max_wgs = 0;
+  p->ws_pre_off = p->ws_ml_off = p->ws_o_off = p->ws_bytes = 0;
   if (!p->fast_decode) return;
-  // Split-KV policy: the longest splits (a power of two of at most kMaxChunk keys) that
-  // still give at least kMinDecodeItems (request, kv head, split) items, then doubled
-  // until no request needs more than kMaxSplits splits.  Every split pays a start-up
-  // (its first tiles' memory latency) and a merge, so fewer, longer splits stream better,
-  // while 5.5 items per CU keep the last round of workgroups short.  Measured on MI355X
-  // (split pass, us, at 1024 / 2048 / 4096-key splits): 64 MHA requests of 512..4096 keys
-  // 373 / 372 / 380; 128 GQA-8 requests of 256..4096 keys 249 / 220 / 219; 16 fp8 requests
-  // of 16K..32K keys 165 / 161 / 162 (512: 186) with one-head workgroups, 150 / 143 with
-  // 4-head workgroups (at 512: 160).  Deterministic in the lengths.
-  const int64_t T = d.tokens_per_block;
-  auto count = [&](int64_t c, int64_t* max_s) {
-    int64_t tot = 0, mx = 0;
-    for (int32_t r = p->num_ctx; r < p->B; ++r) {
-      const int64_t s = (static_cast<int64_t>(b.host_sequence_lengths[r]) + c - 1) / c;
-      tot += s;
-      mx = std::max(mx, s);
-    }
-    *max_s = mx;
-    return tot * d.num_kv_heads;
-  };
-  const int64_t lo = std::max<int64_t>(64, T);
-  int64_t c = std::max<int64_t>(kMaxChunk, T), mx = 0;
-  while (count(c, &mx) < kMinDecodeItems && c > lo) c /= 2;
-  int64_t items = count(c, &mx);
-  while (mx > kMaxSplits) {
-    c *= 2;
-    items = count(c, &mx);
+  // Work units of the balanced split pass: request r has ceil(S_r / 32) tiles in each of its
+  // (head group, column block) segments, with ceil(G * n_r / 16) column blocks of its own.
+  // The kernel derives the same count from the device lengths.
+  const int32_t kv_bytes = d.kv_dtype == PKV_BF16 ? 2 : 1;
+  p->dec_heads = decode_heads_per_wg(kv_bytes, d.num_kv_heads, G, p->col_blocks);
+  const int64_t hgs = d.num_kv_heads / p->dec_heads;
+  int64_t units = 0;
+  for (int32_t r = p->num_ctx; r < p->B; ++r) {
+    const int64_t n = b.host_context_lengths[r];
+    const int64_t S = std::max<int64_t>(b.host_sequence_lengths[r], n);
+    units += hgs * ((G * n + 15) / 16) * ((S - 1) / kDecodeTile + 1);
   }
-  p->chunk = static_cast<int32_t>(c);
-  p->max_splits = static_cast<int32_t>(mx);
-  p->decode_items = items;
-  const int64_t rows = static_cast<int64_t>(p->gen_tokens) * d.num_heads * mx;
-  const size_t ml = static_cast<size_t>(rows) * 2 * sizeof(float);
-  p->ws_ml_off = 0;
-  p->ws_o_off = ((ml + 255) / 256) * 256;
-  p->ws_bytes = p->ws_o_off + static_cast<size_t>(rows) * d.head_dim * sizeof(float);
+  p->dec_units = units;
+  p->dec_segments = static_cast<int64_t>(p->num_gen) * hgs * p->col_blocks;
+  p->dec_max_wgs = std::min<int64_t>(kDecodeMaxWGs, units);
+  p->dec_cols = std::min(16, G * p->max_gen_n);
+  const int64_t entries = (p->dec_segments + p->dec_max_wgs) * p->dec_heads * p->dec_cols;
+  auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
+  p->ws_pre_off = 0;
+  p->ws_ml_off = up(static_cast<size_t>(p->num_gen + 1) * 2 * sizeof(int64_t));   // first units, first rows
+  p->ws_o_off = p->ws_ml_off + up(static_cast<size_t>(entries) * 2 * sizeof(float));
+  p->ws_bytes = p->ws_o_off + static_cast<size_t>(entries) * d.head_dim * sizeof(float);
 }
 
 size_t workspace_upper_bound(const pkv_attn_desc& d, int32_t max_num_requests, int32_t max_seq_len) {
   if (max_num_requests <= 0 || max_seq_len <= 0) return 0;
   if (!desc_fast_decode(d)) return 0;
-  const int64_t min_chunk = std::max<int64_t>(64, d.tokens_per_block);
-  const int64_t splits = std::min<int64_t>(kMaxSplits, (max_seq_len + min_chunk - 1) / min_chunk);
-  // generation rows: at most kMaxGenTokens per request and at most the token budget
-  const int64_t gen_rows = std::min<int64_t>(static_cast<int64_t>(max_num_requests) * kMaxGenTokens,
-                                             std::max<int64_t>(d.max_num_tokens, max_num_requests));
-  const int64_t rows = gen_rows * d.num_heads * splits;
-  const size_t ml = static_cast<size_t>(rows) * 2 * sizeof(float);
-  const size_t o = static_cast<size_t>(rows) * d.head_dim * sizeof(float);
-  return ((ml + 255) / 256) * 256 + o;
+  // Worst case over the batches of at most max_num_requests generation requests of at
+  // most max_seq_len keys: every request with the most column blocks, and per slot 16
+  // columns of 4 KV heads (one head per segment has Hkv segments per column block, four
+  // heads have Hkv / 4 and a single column block).
+  const int64_t G = d.num_heads / d.num_kv_heads;
+  const int64_t R = max_num_requests;
+  const int64_t cbmax = (std::min<int64_t>(G * kMaxGenTokens, kMaxDecodeCols) + 15) / 16;
+  const int64_t tiles = (static_cast<int64_t>(max_seq_len) - 1) / kDecodeTile + 1;
+  const int64_t W = std::min<int64_t>(kDecodeMaxWGs, R * d.num_kv_heads * cbmax * tiles);
+  const int64_t entries = (R * d.num_kv_heads * cbmax + 4 * W) * 16;
+  auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
+  return up(static_cast<size_t>(R + 1) * 2 * sizeof(int64_t)) + up(static_cast<size_t>(entries) * 2 * sizeof(float)) +
+         static_cast<size_t>(entries) * d.head_dim * sizeof(float);
 }
 
 }  // namespace pkv

@@ -26,18 +26,21 @@ struct BatchPlan {
   // split-KV decode policy (generation rows on the MFMA decode path)
   bool fast_decode = false;
   bool fast_prefill = false;
-  int32_t chunk = 0;          // keys per split, a multiple of tokens_per_block
-  int32_t max_splits = 0;     // max over generation requests of ceil(S_r / chunk)
-  int64_t decode_items = 0;   // (request, kv head, split) work items
   int32_t col_blocks = 0;     // blocks of 16 (token, query head) columns per (request, kv head)
+  int32_t dec_heads = 0;      // KV heads per segment (decode_heads_per_wg)
+  int32_t dec_cols = 0;       // columns stored per (piece, KV head): min(16, G * max_gen_n)
+  int64_t dec_units = 0;      // 32-key tiles summed over all (request, head group, column block) segments
+  int64_t dec_segments = 0;   // generation requests x head groups x col_blocks
+  int64_t dec_max_wgs = 0;    // split-pass workgroups the workspace has room for: min(kDecodeMaxWGs, units)
   // workspace layout (bytes)
-  size_t ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
+  size_t ws_pre_off = 0, ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
 };
 
-// Numeric limits of the split policy.
-constexpr int32_t kMaxSplits = 128;       // splits per generation request
-constexpr int32_t kMaxChunk = 2048;        // keys per split, at most
-constexpr int64_t kMinDecodeItems = 1408;  // (request, kv head, split) items, at least: 5.5 per CU
+// The persistent split pass runs kDecodeWGsPerCU workgroups per CU (all resident at
+// once), at most kDecodeMaxWGs, and never more than the batch has 32-key tile units.
+constexpr int32_t kDecodeWGsPerCU = 2;
+constexpr int32_t kDecodeMaxWGs = 1024;
+constexpr int32_t kDecodeTile = 32;        // keys per work unit
 // Generation requests carry 1 .. kMaxGenTokens new tokens (a token and its draft tokens).
 constexpr int32_t kMaxGenTokens = 64;
 // The split pass takes (token, query head) columns of one KV head in blocks of 16; with
@@ -46,14 +49,13 @@ constexpr int32_t kMaxDecodeCols = 64;
 // The persistent context kernel orders up to kPrefillMaxReqs requests per launch (larger
 // batches take several launches).
 constexpr int32_t kPrefillMaxReqs = 512;
-// The split pass gives a workgroup 4 neighbouring KV heads, one wave each, when the KV
-// heads come in fours and either the cache is one byte per element (fp8 / int8) or it is
-// bf16 with groups of at least 8 query heads and one block of 16 columns; otherwise one
-// head, its waves streaming alternate tiles.  Measured on MI355X at 2048-key splits (split
-// pass): 16 fp8 requests of 16K..32K keys 143 us against 161 with one-head workgroups (150
-// at 1024-key splits); 128 bf16 GQA-8 requests of 256..4096 keys 203 against 219; but 64
-// bf16 MHA requests 397 against 370, and the GQA-8 requests with 4 draft tokens each (two
-// column blocks) 492 against 415, so those keep one head per workgroup.
+// The split pass gives a segment 4 neighbouring KV heads, one wave each, when the KV heads
+// come in fours and either the cache is one byte per element (fp8 / int8) or it is bf16
+// with groups of at least 8 query heads and one block of 16 columns; otherwise one head,
+// its waves sharing the tiles.  Four waves reading the neighbouring heads' pieces of the
+// same cache rows at about the same time are served faster by HBM; one-head segments win
+// where a segment has few query columns per KV head and bf16 rows (MHA, draft tokens with
+// several column blocks), measured on MI355X.
 inline int32_t decode_heads_per_wg(int32_t kv_bytes, int32_t num_kv_heads, int32_t group, int32_t col_blocks) {
   if (num_kv_heads % 4 != 0) return 1;
   if (kv_bytes == 1) return 4;

@@ -205,9 +205,15 @@ int main(int argc, char** argv) {
       return 1;
     }
     if (p.fast_decode) {
-      int64_t mx = 0;
-      for (size_t r = p.num_ctx; r < b.S.size(); ++r) mx = std::max<int64_t>(mx, (b.S[r] + p.chunk - 1) / p.chunk);
-      if (mx != p.max_splits || p.max_splits > pkv::kMaxSplits || p.chunk % T) {
+      // work units recounted from the lengths: ceil(S/32) tiles per (head group, column block)
+      const int64_t Gq = x.num_heads / x.num_kv_heads, hgs = x.num_kv_heads / p.dec_heads;
+      int64_t units = 0;
+      for (size_t r = p.num_ctx; r < b.S.size(); ++r)
+        units += hgs * ((Gq * b.n[r] + 15) / 16) * ((b.S[r] + 31) / 32);
+      const bool heads_ok = p.dec_heads == 1 || (p.dec_heads == 4 && x.num_kv_heads % 4 == 0);
+      if (units != p.dec_units || !heads_ok || p.dec_max_wgs != std::min<int64_t>(pkv::kDecodeMaxWGs, units) ||
+          p.dec_cols != std::min<int64_t>(16, Gq * p.max_gen_n) ||
+          p.dec_segments != static_cast<int64_t>(p.num_gen) * hgs * p.col_blocks) {
         std::printf("FAIL split plan (iteration %d)\n", it);
         return 1;
       }

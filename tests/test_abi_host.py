@@ -229,3 +229,11 @@ def test_noalloc_rejects_a_batch_beyond_its_scratch_before_any_launch():
     assert need > L.PKV_SCRATCH_BYTES
     rc = L.pkv_attention_forward_noalloc(d, hb.desc, 16, 128 * 64, 16, 16, None)
     assert rc == L.PKV_ERR_WORKSPACE and "scratch" in L.pkv_last_error()
+
+
+def test_decode_workgroup_cap_set_and_query():
+    assert L.pkv_set_decode_workgroups(-1) == 0          # default
+    assert L.pkv_set_decode_workgroups(7) == 0
+    assert L.pkv_set_decode_workgroups(-1) == 7
+    assert L.pkv_set_decode_workgroups(0) == 7
+    assert L.pkv_set_decode_workgroups(-1) == 0

@@ -350,6 +350,43 @@ def test_decode_head_groups(H, case_i):
     compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
 
 
+# The split pass shares the batch's 32-key tiles among W workgroups in equal ranges; a
+# range cuts segments into pieces and each wave streams its pieces back to back.  Small
+# batches normally give one tile per workgroup, so these cases cap W (process-wide) to
+# force long ranges: many pieces per workgroup (W = 1 also lists them in several
+# batches), pieces of one tile next to long ones, ranges that start and end inside
+# segments, with and without the XCD-contiguous range order (W a multiple of 8 or not).
+STREAM_CASES = [
+    # (Hkv, T, G, kv, draft tokens per request or None, context chunks)
+    (4, 16, 1, W.BF16, None, []),         # one head per workgroup, tiles over two blocks
+    (8, 64, 8, W.BF16, None, []),         # four heads per workgroup (bf16, GQA-8)
+    (8, 32, 4, W.FP8_E4M3, None, []),
+    (4, 64, 2, W.INT8, None, []),
+    (4, 32, 8, W.BF16, 4, []),            # draft tokens: up to 3 column blocks, plain loads
+    (4, 16, 1, W.BF16, 6, []),            # draft tokens, one column block
+    (8, 64, 8, W.BF16, None, [(100, 0), (64, 128)]),   # context requests first
+]
+
+
+@pytest.mark.parametrize("wgs", [1, 3, 8, 13, 24])
+@pytest.mark.parametrize("case_i", range(len(STREAM_CASES)))
+def test_decode_split_workgroup_counts(H, case_i, wgs):
+    from paged_kv_gqa_rope_amd import _lib as L
+    Hkv, T, G, kv, draft, ctx = STREAM_CASES[case_i]
+    sh = W.Shape(f"stream-{case_i}", Hkv * G, Hkv, 128, T, W.BF16, kv, 1e4, k_scale=2.0 ** -6, v_scale=2.0 ** -6,
+                 max_num_tokens=1 << 16)
+    pasts = [0, 1, 15, 31, 32, 63, 64, 127, 511, 512, 700, 1000, 2500, 5]
+    gen_new = None if draft is None else [1 + (i % draft) for i in range(len(pasts))]
+    b = W.make_batch(sh, ctx=ctx, gen_past=pasts, seed=5000 + 10 * case_i + wgs, pool_blocks_min=3, gen_new=gen_new)
+    case("decode split workgroups", sh.name, kv, draft, ctx, "W", wgs)
+    old = L.pkv_set_decode_workgroups(wgs)
+    try:
+        st = run_step(H, b)
+    finally:
+        L.pkv_set_decode_workgroups(old)
+    compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
+
+
 def test_decode_fp8_saturating_values(H):
     # values beyond 448 * scale saturate on write; the oracle reads the same codes
     sh = W.Shape("fp8-sat", 8, 2, 128, 64, W.BF16, W.FP8_E4M3, 1e4, k_scale=2.0 ** -9, v_scale=2.0 ** -9)
