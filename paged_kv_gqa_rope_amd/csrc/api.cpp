@@ -342,6 +342,8 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
     a.col_blocks = plan.col_blocks;
     if (plan.fast_decode) {
       a.dec_heads = plan.dec_heads;
+      a.dec_cbw = plan.dec_cbw;
+      a.dec_allcols = plan.dec_allcols ? 1 : 0;
       a.dec_cols = plan.dec_cols;
       const int32_t cap = g_decode_wgs.load(std::memory_order_relaxed);
       const int64_t target = cap > 0 ? cap : static_cast<int64_t>(pkv::kDecodeWGsPerCU) * std::max(dev.cus, 1);

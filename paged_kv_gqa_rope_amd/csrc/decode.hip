@@ -9,19 +9,22 @@
 // by the new running max).
 //
 // Pass 1 is persistent and balanced: a fixed number of workgroups (two per CU) share the
-// batch's 32-key tiles of every (request, KV head group, block of 16 query columns)
-// segment in equal contiguous ranges, so each streams the same number of bytes whatever
-// the mix of lengths, and each XCD takes one contiguous eighth of them.  A workgroup has
-// 4 waves.  With one KV head per segment its waves stream alternate tiles of a piece,
-// their states merged in LDS at the end; with the KV heads in fours and a one-byte cache
-// (fp8 / int8), or a bf16 cache read by GQA groups of 8 or more query heads in one block
-// of columns (see decode_heads_per_wg), a segment holds 4 neighbouring KV heads, one wave
-// each, every wave streaming all tiles of the piece for its head: the four waves then read
-// the neighbouring pieces of the same cache rows at about the same time, which HBM serves
-// faster than one head's pieces alone.  Per wave and tile:
-//   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, loaded straight
-//     from HBM in operand layout; B = the G query heads of the KV head (GQA group,
-//     G <= 16, padded with zero heads), kept in registers for the whole piece.
+// batch's 32-key tiles of every segment in equal contiguous ranges, so each streams the
+// same number of bytes whatever the mix of lengths, and each XCD takes one contiguous
+// eighth of them.  A workgroup has 4 waves.  When the KV heads come in fours, every wave
+// streams all tiles of a piece for its own (KV head, block of 16 query columns): with one
+// column block a segment is (request, 4 neighbouring KV heads, column block), and the four
+// waves read the neighbouring heads' pieces of the same cache rows at about the same time,
+// which HBM serves faster than one head's pieces alone; with 2 (or 3-4) column blocks
+// (draft tokens) a segment is (request, 2 (or 1) KV heads) with all column blocks, and the
+// waves of one head load the same tiles at about the same time, so HBM serves each tile
+// once and L2 the repeats.  Otherwise a segment is (request, one KV head, column block),
+// its waves sharing the tiles and merging their states in LDS at the end of each piece.
+// Per wave and tile:
+//   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, read in operand
+//     layout from an LDS copy of the tile (XOR-swizzled 16-byte chunks); B = the G query
+//     heads of the KV head (GQA group, G <= 16, padded with zero heads), kept in
+//     registers for the whole piece.
 //   * online softmax per head on the accumulators (lanes l, l^16, l^32, l^48 hold the
 //     same head), exp2 with the log2(e) factor folded into the scale.
 //   * O += P V on MFMA: A = P (heads x 32 keys) straight from the score registers,
@@ -29,7 +32,7 @@
 //   * an fp8 or int8 cache is dequantised to bf16 on load (exact: every e4m3 value
 //     and every integer -128 .. 127 is a bf16 value); k_scale folds into the softmax
 //     scale and v_scale into the combine, so the pass works on raw codes times one.
-// Pass 2, one workgroup per (request, query head): M = max m_p, L = sum 2^(m_p-M) l_p,
+// Pass 2, one wave per (generation token, query head): M = max m_p, L = sum 2^(m_p-M) l_p,
 // O = sum 2^(m_p-M) o_p / L over the segment's pieces in a fixed order (no atomics:
 // bitwise reproducible).
 #include <math.h>
@@ -57,6 +60,7 @@ constexpr int kCombHeads = 4;      // query heads (one wave each) per combine wo
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // 16 bytes of the cache.  With one column block every K/V byte is read once per step and
 // every load instruction covers whole rows (whole 128-byte lines), so the loads carry the
@@ -201,11 +205,14 @@ __device__ __forceinline__ Piece read_piece(const int4* pa, const int4* pb, int 
 // only the softmax state and Q are reset.  Each piece leaves one partial state in its slot.
 // NT: stream the cache with the nontemporal hint (every byte read once) or keep its lines
 // in L2 (several column blocks read the same keys).
-template <int KV, int B, bool NT>
+template <int KV, int HPS, int CBW, bool NT>
 __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int lw, const int4* pla,
                                               const int4* plb, uint16_t (*vtile)[kTile * kVStride],
                                               uint16_t (*ktile)[kTile * kD], float (*ml)[16][2]) {
-  static_assert(B == 1 || B == kWaves, "one head per workgroup, or one per wave");
+  // ALT: one KV head per segment, its waves sharing the tiles; otherwise every wave streams
+  // all tiles for its own (KV head, column block): HPS heads x CBW column blocks.
+  constexpr bool ALT = HPS == 1 && CBW == 1;
+  static_assert(ALT || HPS * CBW == kWaves, "a workgroup's waves cover its heads and column blocks");
   // The thread index passes through an empty asm statement so that nothing derived from
   // it is hoisted out of the batch loop and kept live across it (registers are tight).
   int tid = threadIdx.x;
@@ -213,9 +220,11 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
   const int lane = tid % kWave;
   const int li = lane % 16, lg = lane / 16;
-  const int G = a.H / a.Hkv, hgs = a.Hkv / B;
-  constexpr int TS = B == 1 ? kWaves : 1;                      // tile stride of a wave's items
-  const int base = B == 1 ? wave : 0;                           // first tile of a wave's items
+  const int G = a.H / a.Hkv, hgs = a.Hkv / HPS;
+  constexpr int TS = ALT ? kWaves : 1;                         // tile stride of a wave's items
+  const int base = ALT ? wave : 0;                              // first tile of a wave's items
+  const int wh = ALT ? 0 : wave / CBW;                          // the wave's head in the segment
+  const int wcb = CBW > 1 ? wave % CBW : 0;                     // the wave's column block (CBW > 1)
   const int64_t kv_row = static_cast<int64_t>(a.Hkv) * kD;     // elements per (block, K|V, slot)
   const int tshift = a.tshift, tmask = a.T - 1;
   const int64_t blk_bytes = 2 * static_cast<int64_t>(a.T) * kv_row * (KV == F_BF16 ? 2 : 1);   // K and V of T slots
@@ -263,7 +272,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     t.id0 = table[min(kb0, f_last)];
     t.id1 = table[min(kb0 + 1, f_last)];
     t.tb = tile * kTile;
-    t.g = f_hg * B + (B == 1 ? 0 : wave);
+    t.g = f_hg * HPS + wh;
     if (f_k + 1 < f_cnt) {
       ++f_k;
     } else if (f_p + 1 < np) {
@@ -308,22 +317,25 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     c_nt = q.nt;
     c_cnt = (q.nt + TS - 1) / TS;
     c_n = n;
-    c_cb = q.cb;
-    c_g = q.hg * B + (B == 1 ? 0 : wave);                       // this wave's KV head
+    c_cb = CBW > 1 ? wcb : q.cb;
+    c_g = q.hg * HPS + wh;                                      // this wave's KV head
     c_kend = tiles_end(q.t0 + q.nt, S);
     // A tile needs no masking when it lies inside the piece and inside the causal range
     // of every valid column of the block (the lowest of them is token cb*16 / G).
-    c_lim = S - n + (q.cb * 16) / G;
-    c_ncol = min(min(16, G * n - q.cb * 16), a.dec_cols);       // valid columns of the block
-    c_slot = (static_cast<int64_t>(q.r - a.req_begin) * hgs + q.hg) * a.col_blocks + q.cb + lw;
+    c_lim = S - n + (c_cb * 16) / G;
+    c_ncol = min(16, G * n - c_cb * 16);                        // valid columns of the block
+    if (CBW == 1) c_ncol = min(c_ncol, a.dec_cols);
+    c_slot = CBW > 1 ? static_cast<int64_t>(q.r - a.req_begin) * hgs + q.hg + lw
+                     : (static_cast<int64_t>(q.r - a.req_begin) * hgs + q.hg) * a.col_blocks + q.cb + lw;
     // Columns of the score tile: (token, query head) pairs, 16 per column block.  Lane
     // column li is token tok = gc / G of the request (position S - n + tok; it sees keys
     // up to that position: causal among a request's draft tokens) and head g*G + gc % G.
-    const int gc = q.cb * 16 + li, tok = gc / G;
+    const int gc = c_cb * 16 + li, tok = gc / G;
     const bool col_ok = tok < n;
     key_lim = col_ok ? S - n + tok : -1;
     const int64_t row0 = q.row0;
-    c_valid = row0 >= a.row_begin && row0 + n <= a.N;           // rows outside the generation rows: no output
+    // rows outside the generation rows, or a column block the request does not have: no output
+    c_valid = row0 >= a.row_begin && row0 + n <= a.N && c_ncol > 0;
     const int64_t row = c_valid ? row0 + min(tok, n - 1) : a.row_begin;
     // B operand Q^T: column li, dims ks*32 + lg*8 + j (the dim order inside a
     // contraction is free as long as K uses the same one).
@@ -343,10 +355,10 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   // Write the piece's partial state (m, l, o) to its slot.
   auto end_piece = [&]() {
     const int ncol = c_ncol;
-    if constexpr (B > 1) {
-      // this wave alone holds its head's state for the piece
+    if constexpr (!ALT) {
+      // this wave alone holds its (head, column block) state for the piece
       if (c_valid) {
-        const int64_t e0 = (c_slot * B + wave) * a.dec_cols;
+        const int64_t e0 = (c_slot * HPS + wh) * a.dec_cols + (CBW > 1 ? c_cb * 16 : 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = lg * 4 + i;
@@ -564,54 +576,61 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   }
 }
 
-// Persistent split pass: gridDim.x workgroups share the batch's work units (32-key tiles
-// of every (request, head group, column block) segment, requests in order, then head
-// group, then column block, then keys) in equal contiguous ranges, so every workgroup
-// streams the same number of K/V bytes whatever the mix of lengths.  A workgroup's range
-// cuts the segments it touches into pieces; each piece leaves one partial state in slot
-// (segment index + workgroup index), which is unique because both grow along the units.
-// Launched workgroup w runs on XCD w % 8 (round-robin dispatch); it takes range
-// (w % 8) * (W / 8) + w / 8, so each XCD (one L2) works through one contiguous eighth.
-template <int KV, int B, bool NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
-  __shared__ float ml[kWaves][16][2];
-  __shared__ int64_t part[2 * kWaves];
-  __shared__ int64_t start[3], walk[4];
-  __shared__ int4 pla[kPieceBatch], plb[kPieceBatch];
-  __shared__ int pcount;
-  const int G = a.H / a.Hkv, hgs = a.Hkv / B;
+// ---- range bookkeeping shared by the split passes
+//
+// gridDim.x workgroups share the batch's work units (32-key tiles of every segment,
+// requests in order, then segments, then keys) in equal contiguous ranges, so every
+// workgroup streams the same number of K/V bytes whatever the mix of lengths.  A segment
+// is (request, head group, column block), or (request, head group) when one workgroup
+// carries every column block (RING).  A workgroup's range cuts the segments it touches
+// into pieces; each piece leaves one partial state in slot (segment index + workgroup
+// index), which is unique because both grow along the units.  Launched workgroup w runs
+// on XCD w % 8 (round-robin dispatch); it takes range (w % 8) * (W / 8) + w / 8, so each
+// XCD (one L2) works through one contiguous eighth.
+struct RangeLds {
+  int64_t part[2 * kWaves];
+  int64_t start[3], walk[4];
+  int4 pla[kPieceBatch], plb[kPieceBatch];
+  int pcount;
+};
+template <bool RING>
+__device__ __forceinline__ int64_t units_of(const ReqGeom& q, int hgs) {
+  return RING ? static_cast<int64_t>(hgs) * q.tiles : req_units(q, hgs);
+}
+// Prefix sums of the units (and of the rows) over the requests, this workgroup's range
+// and where it starts; workgroup 0 also records every request's first unit (and the
+// total) and first packed row for the combine.  Returns false for an empty range.
+template <bool RING>
+__device__ __forceinline__ bool range_begin(const AttnArgs& a, const int hgs, RangeLds& L, int& lw) {
+  const int G = a.H / a.Hkv;
   const int R = a.req_end - a.req_begin;
-  // units of this thread's run of requests, and where the run starts in the unit order
   const int per = (R + kThreads - 1) / kThreads;
   const int i0 = min(static_cast<int>(threadIdx.x) * per, R), i1 = min(i0 + per, R);
   int64_t mine = 0, mrows = 0;
   for (int i = i0; i < i1; ++i) {
-    mine += req_units(req_geom(a, a.req_begin + i, G), hgs);
+    mine += units_of<RING>(req_geom(a, a.req_begin + i, G), hgs);
     mrows += a.ctx_len[a.req_begin + i];
   }
   int64_t U, rows_total;
-  const int64_t before = block_exclusive_scan(mine, &U, part);
-  const int64_t rows_before = block_exclusive_scan(mrows, &rows_total, part + kWaves);
+  const int64_t before = block_exclusive_scan(mine, &U, L.part);
+  const int64_t rows_before = block_exclusive_scan(mrows, &rows_total, L.part + kWaves);
   const int W = gridDim.x, w = blockIdx.x;
-  const int lw = W % kXcds == 0 ? (w % kXcds) * (W / kXcds) + w / kXcds : w;
+  lw = W % kXcds == 0 ? (w % kXcds) * (W / kXcds) + w / kXcds : w;
   const int64_t u0 = static_cast<int64_t>(lw) * U / W, u1 = static_cast<int64_t>(lw + 1) * U / W;
-  // The thread whose run holds unit u0 records its request, offset and first row;
-  // workgroup 0 also records every request's first unit (and the total) and first packed
-  // row for the combine.  Rows: the generation rows follow each other in request order.
+  // The thread whose run holds unit u0 records its request, offset and first row.  Rows:
+  // the generation rows follow each other in request order.
   if ((u0 >= before && u0 < before + mine) || w == 0) {
     int64_t acc = before, racc = a.row_begin + rows_before;
     for (int i = i0; i < i1; ++i) {
-      const int64_t units = req_units(req_geom(a, a.req_begin + i, G), hgs);
+      const int64_t units = units_of<RING>(req_geom(a, a.req_begin + i, G), hgs);
       if (w == 0) {
         a.ws_pre[i] = acc;
         a.ws_row[i] = racc;
       }
       if (u0 >= acc && u0 < acc + units) {
-        start[0] = i;
-        start[1] = u0 - acc;
-        start[2] = racc;
+        L.start[0] = i;
+        L.start[1] = u0 - acc;
+        L.start[2] = racc;
       }
       acc += units;
       racc += a.ctx_len[a.req_begin + i];
@@ -622,49 +641,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   __syncthreads();
-  if (u0 >= u1) return;                                         // empty range (uniform)
+  if (u0 >= u1) return false;                                   // empty range (uniform)
   if (threadIdx.x == 0) {
-    walk[0] = start[0];
-    walk[1] = start[1];
-    walk[2] = u1 - u0;
-    walk[3] = start[2];
+    L.walk[0] = L.start[0];
+    L.walk[1] = L.start[1];
+    L.walk[2] = u1 - u0;
+    L.walk[3] = L.start[2];
   }
-  // Thread 0 cuts the range into pieces, kPieceBatch at a time, into LDS; the waves then
-  // stream them.  Only the LDS list lives across batches.
-  while (true) {
-    if (threadIdx.x == 0) {
-      int r = a.req_begin + static_cast<int>(walk[0]);
-      int64_t off = walk[1], left = walk[2], row0 = walk[3];
-      int np = 0;
-      while (left > 0 && r < a.req_end && np < kPieceBatch) {
-        const ReqGeom q = req_geom(a, r, G);
-        const int64_t units = req_units(q, hgs);
-        if (off < units) {
-          const int64_t j = off / q.tiles;                       // segment of the request
-          const int t0 = static_cast<int>(off - j * q.tiles);
-          const int take = static_cast<int>(min64(q.tiles - t0, left));
-          pla[np] = make_int4(r, static_cast<int>(j / q.cbs), static_cast<int>(j % q.cbs), t0);
-          plb[np] = make_int4(take, q.n, q.S, static_cast<int>(min64(max64(row0, -1), a.N)));
-          ++np;
-          left -= take;
-          off += take;
-        }
-        if (off >= units) {
-          row0 += a.ctx_len[r];
-          ++r;
-          off = 0;
-        }
+  return true;
+}
+// Thread 0 cuts the next part of the range into at most kPieceBatch pieces, listed in LDS
+// as (request, head group, column block, first tile) and (tiles, n, S, first row); every
+// thread gets their number (0: the range is done).
+template <bool RING>
+__device__ __forceinline__ int list_pieces(const AttnArgs& a, const int hgs, RangeLds& L) {
+  const int G = a.H / a.Hkv;
+  if (threadIdx.x == 0) {
+    int r = a.req_begin + static_cast<int>(L.walk[0]);
+    int64_t off = L.walk[1], left = L.walk[2], row0 = L.walk[3];
+    int np = 0;
+    while (left > 0 && r < a.req_end && np < kPieceBatch) {
+      const ReqGeom q = req_geom(a, r, G);
+      const int64_t units = units_of<RING>(q, hgs);
+      if (off < units) {
+        const int64_t j = off / q.tiles;                         // segment of the request
+        const int t0 = static_cast<int>(off - j * q.tiles);
+        const int take = static_cast<int>(min64(q.tiles - t0, left));
+        const int hg = RING ? static_cast<int>(j) : static_cast<int>(j / q.cbs);
+        const int cb = RING ? 0 : static_cast<int>(j % q.cbs);
+        L.pla[np] = make_int4(r, hg, cb, t0);
+        L.plb[np] = make_int4(take, q.n, q.S, static_cast<int>(min64(max64(row0, -1), a.N)));
+        ++np;
+        left -= take;
+        off += take;
       }
-      walk[0] = r - a.req_begin;
-      walk[1] = off;
-      walk[2] = left;
-      walk[3] = row0;
-      pcount = np;
+      if (off >= units) {
+        row0 += a.ctx_len[r];
+        ++r;
+        off = 0;
+      }
     }
-    __syncthreads();
-    const int np = __builtin_amdgcn_readfirstlane(pcount);
+    L.walk[0] = r - a.req_begin;
+    L.walk[1] = off;
+    L.walk[2] = left;
+    L.walk[3] = row0;
+    L.pcount = np;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(L.pcount);
+}
+
+// Split pass with register-staged tiles (any KV head count, any cache format).  With
+// CBW > 1 a segment carries all column blocks of its heads (the waves of one head load
+// the same tiles at about the same time; HBM serves them once, L2 the repeats).
+template <int KV, int HPS, int CBW, bool NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kTile * kVStride];
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
+  __shared__ float ml[kWaves][16][2];
+  __shared__ RangeLds L;
+  const int hgs = a.Hkv / HPS;
+  int lw;
+  if (!range_begin<(CBW > 1)>(a, hgs, L, lw)) return;
+  while (true) {
+    const int np = list_pieces<(CBW > 1)>(a, hgs, L);
     if (np == 0) return;                                        // uniform
-    decode_stream<KV, B, NT>(a, np, lw, pla, plb, vtile, ktile, ml);
+    decode_stream<KV, HPS, CBW, NT>(a, np, lw, L.pla, L.plb, vtile, ktile, ml);
     __syncthreads();                                            // the list is read before it is refilled
   }
 }
@@ -693,13 +735,18 @@ __global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(Attn
   const int64_t row = row0 + tok;
   if (row < a.row_begin || row >= a.N) return;                      // outside the generation rows
   const int g = h / G, hg = g / B, wv = g % B;
-  const int c = tok * G + h % G, cb = c / 16, col = c % 16;
-  if (cb >= cbs || col >= a.dec_cols || U <= 0 || W <= 0) return;
-  const int64_t s0 = P + (static_cast<int64_t>(hg) * cbs + cb) * tiles, s1 = s0 + tiles;
+  // segment and stored column of (token, head): (request, head group, column block) and
+  // the column within its block, or, when segments carry all column blocks, (request,
+  // head group) and the column
+  const bool all = a.dec_allcols != 0;
+  const int c = tok * G + h % G, cb = all ? 0 : c / 16, col = all ? c : c % 16;
+  const int segs = all ? 1 : cbs;                                   // segments per head group
+  if (cb >= segs || col >= a.dec_cols || U <= 0 || W <= 0) return;
+  const int64_t s0 = P + (static_cast<int64_t>(hg) * segs + cb) * tiles, s1 = s0 + tiles;
   const int64_t f = ((s0 + 1) * W - 1) / U, l = (s1 * W - 1) / U;  // first and last range
   const int lwf = static_cast<int>(min64(max64(f, 0), W - 1));
   const int np = static_cast<int>(min64(max64(l, lwf), W - 1)) - lwf + 1;
-  const int64_t seg = (static_cast<int64_t>(rg) * hgs + hg) * a.col_blocks + cb;
+  const int64_t seg = (static_cast<int64_t>(rg) * hgs + hg) * (all ? 1 : a.col_blocks) + cb;
   const int64_t stride = static_cast<int64_t>(B) * a.dec_cols;      // entries between pieces
   const int64_t e0 = ((seg + lwf) * B + wv) * a.dec_cols + col;    // entry of the first piece
   const float2* op = reinterpret_cast<const float2*>(a.ws_o + e0 * kD) + lane;
@@ -758,22 +805,20 @@ __global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(Attn
 
 }  // namespace
 
+template <int KV>
+void launch_split_t(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.dec_wgs), block(kThreads);
+  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, false>), grid, block, 0, s, a);
+  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, false>), grid, block, 0, s, a);
+  else if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<KV, 4, 1, true>), grid, block, 0, s, a);
+  else if (a.col_blocks == 1) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, false>), grid, block, 0, s, a);
+}
+
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.dec_wgs);
-  const bool nt = a.col_blocks == 1;
-  if (a.kv_fmt == F_FP8) {
-    if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_FP8, kWaves, true>), grid, dim3(kThreads), 0, s, a);
-    else if (nt) hipLaunchKernelGGL((decode_split_kernel<F_FP8, 1, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<F_FP8, 1, false>), grid, dim3(kThreads), 0, s, a);
-  } else if (a.kv_fmt == F_INT8) {
-    if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_INT8, kWaves, true>), grid, dim3(kThreads), 0, s, a);
-    else if (nt) hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<F_INT8, 1, false>), grid, dim3(kThreads), 0, s, a);
-  } else {
-    if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<F_BF16, kWaves, true>), grid, dim3(kThreads), 0, s, a);
-    else if (nt) hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<F_BF16, 1, false>), grid, dim3(kThreads), 0, s, a);
-  }
+  if (a.kv_fmt == F_FP8) launch_split_t<F_FP8>(a, s);
+  else if (a.kv_fmt == F_INT8) launch_split_t<F_INT8>(a, s);
+  else launch_split_t<F_BF16>(a, s);
   return hipGetLastError();
 }
 

@@ -64,8 +64,10 @@ struct AttnArgs {
   int32_t max_n;                 // largest n_r among the handled requests
   // split-KV decode (persistent, balanced split pass)
   int32_t col_blocks;            // blocks of 16 (token, query head) columns per (request, kv head)
-  int32_t dec_heads;             // KV heads per segment (1, or 4: one per wave)
-  int32_t dec_cols;              // columns stored per (piece, KV head): min(16, G * max_n)
+  int32_t dec_heads;             // KV heads per segment (1, 2 or 4)
+  int32_t dec_cbw;               // waves per head, one column block each (1, 2 or 4)
+  int32_t dec_allcols;           // 1: segments (request, head group) carry all column blocks
+  int32_t dec_cols;              // columns stored per (piece, KV head): min(16, G * max_n), or G * max_n (dec_allcols)
   int32_t dec_wgs;               // workgroups of the split pass
   int64_t* ws_pre;               // [generation requests + 1] first unit of each request, total last
   int64_t* ws_row;               // [generation requests + 1] first packed row of each request

@@ -162,19 +162,20 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   // Work units of the balanced split pass: request r has ceil(S_r / 32) tiles in each of its
   // (head group, column block) segments, with ceil(G * n_r / 16) column blocks of its own.
   // The kernel derives the same count from the device lengths.
-  const int32_t kv_bytes = d.kv_dtype == PKV_BF16 ? 2 : 1;
-  p->dec_heads = decode_heads_per_wg(kv_bytes, d.num_kv_heads, G, p->col_blocks);
+  p->dec_cbw = decode_column_waves(d.num_kv_heads, p->col_blocks);
+  p->dec_allcols = p->dec_cbw > 1;
+  p->dec_heads = p->dec_cbw > 1 ? 4 / p->dec_cbw : decode_heads_per_wg(d.num_kv_heads);
   const int64_t hgs = d.num_kv_heads / p->dec_heads;
   int64_t units = 0;
   for (int32_t r = p->num_ctx; r < p->B; ++r) {
     const int64_t n = b.host_context_lengths[r];
     const int64_t S = std::max<int64_t>(b.host_sequence_lengths[r], n);
-    units += hgs * ((G * n + 15) / 16) * ((S - 1) / kDecodeTile + 1);
+    units += hgs * (p->dec_allcols ? 1 : (G * n + 15) / 16) * ((S - 1) / kDecodeTile + 1);
   }
   p->dec_units = units;
-  p->dec_segments = static_cast<int64_t>(p->num_gen) * hgs * p->col_blocks;
+  p->dec_segments = static_cast<int64_t>(p->num_gen) * hgs * (p->dec_allcols ? 1 : p->col_blocks);
   p->dec_max_wgs = std::min<int64_t>(kDecodeMaxWGs, units);
-  p->dec_cols = std::min(16, G * p->max_gen_n);
+  p->dec_cols = p->dec_allcols ? G * p->max_gen_n : std::min(16, G * p->max_gen_n);
   const int64_t entries = (p->dec_segments + p->dec_max_wgs) * p->dec_heads * p->dec_cols;
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
   p->ws_pre_off = 0;
@@ -195,7 +196,10 @@ size_t workspace_upper_bound(const pkv_attn_desc& d, int32_t max_num_requests, i
   const int64_t cbmax = (std::min<int64_t>(G * kMaxGenTokens, kMaxDecodeCols) + 15) / 16;
   const int64_t tiles = (static_cast<int64_t>(max_seq_len) - 1) / kDecodeTile + 1;
   const int64_t W = std::min<int64_t>(kDecodeMaxWGs, R * d.num_kv_heads * cbmax * tiles);
-  const int64_t entries = (R * d.num_kv_heads * cbmax + 4 * W) * 16;
+  // segments carrying all column blocks: at most Hkv segments per request, at most 4 heads
+  // x G * kMaxGenTokens columns per slot
+  const int64_t all_cols = std::min<int64_t>(G * kMaxGenTokens, kMaxDecodeCols);
+  const int64_t entries = std::max((R * d.num_kv_heads * cbmax + 4 * W) * 16, (R * d.num_kv_heads + 4 * W) * all_cols);
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
   return up(static_cast<size_t>(R + 1) * 2 * sizeof(int64_t)) + up(static_cast<size_t>(entries) * 2 * sizeof(float)) +
          static_cast<size_t>(entries) * d.head_dim * sizeof(float);

@@ -27,10 +27,13 @@ struct BatchPlan {
   bool fast_decode = false;
   bool fast_prefill = false;
   int32_t col_blocks = 0;     // blocks of 16 (token, query head) columns per (request, kv head)
-  int32_t dec_heads = 0;      // KV heads per segment (decode_heads_per_wg)
-  int32_t dec_cols = 0;       // columns stored per (piece, KV head): min(16, G * max_gen_n)
-  int64_t dec_units = 0;      // 32-key tiles summed over all (request, head group, column block) segments
-  int64_t dec_segments = 0;   // generation requests x head groups x col_blocks
+  int32_t dec_heads = 0;      // KV heads per segment
+  int32_t dec_cbw = 1;        // waves per head, one column block each
+  bool dec_allcols = false;   // segments (request, head group) carry all column blocks
+  int32_t dec_cols = 0;       // columns stored per (piece, KV head): min(16, G * max_gen_n), or G * max_gen_n
+                              // when segments carry all column blocks
+  int64_t dec_units = 0;      // 32-key tiles summed over all segments
+  int64_t dec_segments = 0;   // generation requests x head groups (x col_blocks unless dec_allcols)
   int64_t dec_max_wgs = 0;    // split-pass workgroups the workspace has room for: min(kDecodeMaxWGs, units)
   // workspace layout (bytes)
   size_t ws_pre_off = 0, ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
@@ -50,16 +53,23 @@ constexpr int32_t kMaxDecodeCols = 64;
 // batches take several launches).
 constexpr int32_t kPrefillMaxReqs = 512;
 // The split pass gives a segment 4 neighbouring KV heads, one wave each, when the KV heads
-// come in fours and either the cache is one byte per element (fp8 / int8) or it is bf16
-// with groups of at least 8 query heads and one block of 16 columns; otherwise one head,
-// its waves sharing the tiles.  Four waves reading the neighbouring heads' pieces of the
-// same cache rows at about the same time are served faster by HBM; one-head segments win
-// where a segment has few query columns per KV head and bf16 rows (MHA, draft tokens with
-// several column blocks), measured on MI355X.
-inline int32_t decode_heads_per_wg(int32_t kv_bytes, int32_t num_kv_heads, int32_t group, int32_t col_blocks) {
-  if (num_kv_heads % 4 != 0) return 1;
-  if (kv_bytes == 1) return 4;
-  return kv_bytes == 2 && group >= 8 && col_blocks == 1 ? 4 : 1;
+// come in fours; otherwise one head, its waves sharing the tiles.  Four waves reading the
+// neighbouring heads' pieces of the same cache rows at about the same time are served
+// faster by HBM.  Measured on MI355X with the balanced split pass (split pass, us, four
+// heads against one): 64 bf16 MHA requests of 528..4022 keys 344 / 348; 128 GQA-8
+// requests with 4 draft tokens each (two column blocks) 365 / 402; 128 GQA-8 requests
+// 179 / 180; 16 fp8 requests of 16K..32K keys 142 / 141.
+inline int32_t decode_heads_per_wg(int32_t num_kv_heads) { return num_kv_heads % 4 == 0 ? 4 : 1; }
+// With several column blocks (draft tokens) and KV heads in fours, a segment carries all
+// column blocks of 4 / cbw heads, one wave per (head, column block), cbw = 2 or 4: the
+// waves of one head load the same tiles at about the same time, HBM serving them once.
+// Measured (128 GQA-8 requests with 4 draft tokens, two column blocks, split pass): 244 us
+// against 363 with one segment per column block, and 294 for a pass that streams the
+// tiles of 4 heads through an LDS ring shared by all column blocks (its in-flight bytes
+// are bounded by LDS).
+inline int32_t decode_column_waves(int32_t num_kv_heads, int32_t col_blocks) {
+  if (num_kv_heads % 4 != 0 || col_blocks <= 1) return 1;
+  return col_blocks == 2 ? 2 : 4;
 }
 // Which specialised kernels this build dispatches to (the generic kernel covers the rest).
 constexpr bool kHaveFastDecode = true;

@@ -207,13 +207,17 @@ int main(int argc, char** argv) {
     if (p.fast_decode) {
       // work units recounted from the lengths: ceil(S/32) tiles per (head group, column block)
       const int64_t Gq = x.num_heads / x.num_kv_heads, hgs = x.num_kv_heads / p.dec_heads;
+      const bool all = p.dec_allcols;
       int64_t units = 0;
       for (size_t r = p.num_ctx; r < b.S.size(); ++r)
-        units += hgs * ((Gq * b.n[r] + 15) / 16) * ((b.S[r] + 31) / 32);
-      const bool heads_ok = p.dec_heads == 1 || (p.dec_heads == 4 && x.num_kv_heads % 4 == 0);
-      if (units != p.dec_units || !heads_ok || p.dec_max_wgs != std::min<int64_t>(pkv::kDecodeMaxWGs, units) ||
-          p.dec_cols != std::min<int64_t>(16, Gq * p.max_gen_n) ||
-          p.dec_segments != static_cast<int64_t>(p.num_gen) * hgs * p.col_blocks) {
+        units += hgs * (all ? 1 : (Gq * b.n[r] + 15) / 16) * ((b.S[r] + 31) / 32);
+      // heads x column waves fill the 4 waves (or one head whose waves share the tiles)
+      const bool heads_ok = (p.dec_heads == 1 && p.dec_cbw == 1) || p.dec_heads * p.dec_cbw == 4;
+      const bool waves_ok = p.dec_cbw == 1 || (x.num_kv_heads % 4 == 0 && p.dec_cbw >= p.col_blocks && all);
+      const int64_t cols = all ? Gq * p.max_gen_n : std::min<int64_t>(16, Gq * p.max_gen_n);
+      if (!waves_ok || x.num_kv_heads % p.dec_heads != 0 || units != p.dec_units || !heads_ok ||
+          p.dec_max_wgs != std::min<int64_t>(pkv::kDecodeMaxWGs, units) || p.dec_cols != cols ||
+          p.dec_segments != static_cast<int64_t>(p.num_gen) * hgs * (all ? 1 : p.col_blocks)) {
         std::printf("FAIL split plan (iteration %d)\n", it);
         return 1;
       }
