@@ -105,14 +105,34 @@ def variant_batch(name: str):
 VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "fp8out3", "spec4-gqa8", "int8kv5")
 
 
-def decode_us(kern: dict) -> float:
-    """Decode attention time: the split pass plus its combine (each from its own event pair)."""
+def decode_us(res: dict) -> float:
+    """Decode attention time: the split pass and its combine as one span (one event pair
+    around both launches), else the sum of their own event pairs."""
+    if "decode" in res.get("phases", {}):
+        return res["phases"]["decode"]["avg_us"]
+    kern = res["kernels"]
     return kern["decode_split"]["avg_us"] + kern.get("decode_combine", {"avg_us": 0.0})["avg_us"]
 
 
+def _timed_pass(L, st, steps: int, level: int) -> dict:
+    """K steps with the library's timing at `level` (1: launches, 2: phases); average per name."""
+    import torch
+    L.check(L.pkv_kernel_timing_enable(level))
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    timings = L.pkv_kernel_timings()
+    L.check(L.pkv_kernel_timing_enable(0))
+    per: dict[str, list[float]] = {}
+    for name, ms in timings:
+        per.setdefault(name, []).append(ms)
+    return {n: dict(avg_us=1e3 * sum(v) / len(v), launches=len(v)) for n, v in per.items()}
+
+
 def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:
-    """Warm-up, then K timed steps with the library's kernel timing off (ms_per_step), then
-    K more steps with it on, for the per-kernel durations only."""
+    """Warm-up, then K timed steps with the library's timing off (ms_per_step), then K
+    steps with an event pair around every launch (per-kernel durations) and K with one
+    around every phase (the decode span: split pass and combine with nothing between)."""
     import torch
 
     from paged_kv_gqa_rope_amd import _lib as L
@@ -136,23 +156,14 @@ def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = beg.elapsed_time(end) / steps
-    # per-kernel durations: a separate pass with HIP events around every launch
-    L.check(L.pkv_kernel_timing_enable(True))
-    for _ in range(steps):
-        st.step()
-    torch.cuda.synchronize()
-    timings = L.pkv_kernel_timings()
-    L.check(L.pkv_kernel_timing_enable(False))
-    per_kernel: dict[str, list[float]] = {}
-    for name, ms in timings:
-        per_kernel.setdefault(name, []).append(ms)
-    kern = {n: dict(avg_us=1e3 * sum(v) / len(v), launches=len(v)) for n, v in per_kernel.items()}
+    kern = _timed_pass(L, st, steps, 1)
+    phases = _timed_pass(L, st, steps, 2)
     w = algorithmic(batch)
     step_bytes = w["append_bytes"] + w["decode_bytes"]
     res = dict(workload=describe(batch), setup_s=round(setup_s, 2), ms_per_step=ms_per_step,
-               tok_per_s=w["tokens"] / (ms_per_step * 1e-3), kernels=kern, work=w)
+               tok_per_s=w["tokens"] / (ms_per_step * 1e-3), kernels=kern, phases=phases, work=w)
     if "decode_split" in kern:
-        span = decode_us(kern) * 1e-6
+        span = decode_us(res) * 1e-6
         res["decode_GBps"] = w["decode_bytes"] / span / 1e9
         res["decode_split_GBps"] = w["decode_bytes"] / (kern["decode_split"]["avg_us"] * 1e-6) / 1e9
     for name in ("prefill_mfma", "attn_generic_ctx"):
@@ -188,19 +199,22 @@ TARGET_FRAC = {"hbm": 0.70, "mfma": 0.45}
 
 
 def roofline_for(res: dict, k: int) -> dict:
-    """Roofline of the dominant kernel.  Decode: algorithmic bytes over the split pass plus
-    its combine; context: causal flops over the context kernel."""
+    """Roofline of the dominant kernel.  Decode: algorithmic bytes over the split pass's
+    average launch, and over the whole decode phase (split pass and combine, one event
+    pair around both), the phase deciding the target; context: causal flops over the
+    context kernel."""
     kern = res["kernels"]
     w = res["work"]
     if "decode_split" in kern and w["decode_bytes"] > 0 and w["ctx_flops"] == 0:
-        name = "decode_split+decode_combine" if "decode_combine" in kern else "decode_split"
-        us = decode_us(kern)
-        ach = w["decode_bytes"] / (us * 1e-6) / 1e9
-        split = w["decode_bytes"] / (kern["decode_split"]["avg_us"] * 1e-6) / 1e9
-        return dict(kernel=name, bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=ach / HBM_PEAK_GBS, traffic=measured_traffic("decode_split", k),
-                    avg_us=us, split_only_frac=split / HBM_PEAK_GBS,
-                    target_frac=TARGET_FRAC["hbm"], meets_target=ach / HBM_PEAK_GBS >= TARGET_FRAC["hbm"])
+        split_us = kern["decode_split"]["avg_us"]
+        ach = w["decode_bytes"] / (split_us * 1e-6) / 1e9
+        phase_us = decode_us(res)
+        phase = w["decode_bytes"] / (phase_us * 1e-6) / 1e9
+        return dict(kernel="decode_split", bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBS, traffic=measured_traffic("decode_split", k), avg_us=split_us,
+                    phase=dict(name="decode_split + decode_combine", avg_us=phase_us, achieved=phase,
+                               frac=phase / HBM_PEAK_GBS),
+                    target_frac=TARGET_FRAC["hbm"], meets_target=phase / HBM_PEAK_GBS >= TARGET_FRAC["hbm"])
     name = "prefill_mfma" if "prefill_mfma" in kern else "attn_generic_ctx"
     ach = w["ctx_flops"] / (kern[name]["avg_us"] * 1e-6) / 1e12
     return dict(kernel=name, bound="mfma", achieved=ach, peak=BF16_DENSE_PEAK_TFLOPS, unit="TFLOP/s",
@@ -348,7 +362,8 @@ def main() -> int:
         print(f"[bench] workload {k} ...", file=sys.stderr, flush=True)
         results[k] = run_workload(k, args.steps, args.warmup)
         print(f"[bench] workload {k}: {results[k]['ms_per_step']:.3f} ms/step "
-              f"{ {n: round(v['avg_us'], 1) for n, v in results[k]['kernels'].items()} }", file=sys.stderr, flush=True)
+              f"{ {n: round(v['avg_us'], 1) for n, v in results[k]['kernels'].items()} } phases "
+              f"{ {n: round(v['avg_us'], 1) for n, v in results[k]['phases'].items()} }", file=sys.stderr, flush=True)
     head_k = HEADLINE if HEADLINE in results else ks[0]
     head = results[head_k]
     line = {
@@ -366,7 +381,8 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) values, seeded lengths and block permutation)",
         "config": {"workload": head["workload"], "tok_per_s": head["tok_per_s"],
                    "decode_GBps": head.get("decode_GBps"), "pct_hbm_peak": 100 * head.get("decode_GBps", 0) / HBM_PEAK_GBS,
-                   "kernels_us": {n: round(v["avg_us"], 2) for n, v in head["kernels"].items()}},
+                   "kernels_us": {n: round(v["avg_us"], 2) for n, v in head["kernels"].items()},
+                   "phases_us": {n: round(v["avg_us"], 2) for n, v in head["phases"].items()}},
         "roofline": roofline_for(head, head_k),
     }
     others = {}
@@ -374,7 +390,8 @@ def main() -> int:
         if k == head_k:
             continue
         o = dict(workload=r["workload"], ms_per_step=r["ms_per_step"], tok_per_s=r["tok_per_s"],
-                 kernels_us={n: round(v["avg_us"], 2) for n, v in r["kernels"].items()})
+                 kernels_us={n: round(v["avg_us"], 2) for n, v in r["kernels"].items()},
+                 phases_us={n: round(v["avg_us"], 2) for n, v in r["phases"].items()})
         for f in ("decode_GBps", "prefill_TFLOPs", "append_GBps", "prefill_kernel"):
             if f in r:
                 o[f] = r[f]
@@ -390,9 +407,11 @@ def main() -> int:
         print(f"[bench] variant {name} ...", file=sys.stderr, flush=True)
         r = run_workload(0, args.steps, args.warmup, batch=variant_batch(name))
         print(f"[bench] variant {name}: {r['ms_per_step']:.3f} ms/step "
-              f"{ {n: round(v['avg_us'], 1) for n, v in r['kernels'].items()} }", file=sys.stderr, flush=True)
+              f"{ {n: round(v['avg_us'], 1) for n, v in r['kernels'].items()} } phases "
+              f"{ {n: round(v['avg_us'], 1) for n, v in r['phases'].items()} }", file=sys.stderr, flush=True)
         o = dict(workload=r["workload"], ms_per_step=r["ms_per_step"], tok_per_s=r["tok_per_s"],
-                 kernels_us={n: round(v["avg_us"], 2) for n, v in r["kernels"].items()})
+                 kernels_us={n: round(v["avg_us"], 2) for n, v in r["kernels"].items()},
+                 phases_us={n: round(v["avg_us"], 2) for n, v in r["phases"].items()})
         for f in ("decode_GBps", "prefill_TFLOPs", "append_GBps", "prefill_kernel"):
             if f in r:
                 o[f] = r[f]

@@ -312,15 +312,18 @@ int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch
 
 
 /*
- * Opt-in per-kernel timing for measurement tools.  pkv_kernel_timing_enable(1) creates a
- * pool of 8192 HIP events (once; they are reused) and clears the record; while enabled,
- * every kernel launch of the library is bracketed by two events of the pool recorded on
+ * Opt-in timing for measurement tools.  pkv_kernel_timing_enable(1) times every kernel
+ * launch, pkv_kernel_timing_enable(2) every phase instead: the append, the context
+ * attention, and the generation attention (named "decode": the split pass and its
+ * combine as one span, with no events between them); 0 switches timing off.  Enabling
+ * creates a pool of 8192 HIP events (once; they are reused) and clears the record; while
+ * enabled, each timed launch or phase is bracketed by two events of the pool recorded on
  * its stream (no synchronisation, no allocation inside the entry points).  Once the pool
  * is used up, further launches are not timed.  pkv_kernel_timings() synchronises on the
- * recorded events, writes up to max_entries kernel names (static strings) and durations in
- * milliseconds, returns the number of entries recorded since the last
- * pkv_kernel_timing_enable(1), sets pkv_last_error() to the number of untimed launches if
- * any, and may be called only from the thread that launched.  Not graph-capturable.
+ * recorded events, writes up to max_entries names (static strings) and durations in
+ * milliseconds, returns the number of entries recorded since timing was last enabled,
+ * sets pkv_last_error() to the number of untimed launches if any, and may be called only
+ * from the thread that launched.  Not graph-capturable.
  */
 int32_t pkv_kernel_timing_enable(int32_t on);
 int32_t pkv_kernel_timings(const char** names, float* milliseconds, int32_t max_entries);

@@ -185,8 +185,10 @@ def pkv_set_decode_workgroups(n: int) -> int:
     return lib().pkv_set_decode_workgroups(int(n))
 
 
-def pkv_kernel_timing_enable(on: bool) -> int:
-    return lib().pkv_kernel_timing_enable(1 if on else 0)
+def pkv_kernel_timing_enable(on) -> int:
+    """0 / False: off; 1 / True: every kernel launch; 2: every phase (append, context
+    attention, generation attention as one span)."""
+    return lib().pkv_kernel_timing_enable(int(on))
 
 
 def pkv_kernel_timings(max_entries: int = 4096) -> list[tuple[str, float]]:

@@ -63,25 +63,31 @@ struct TimingRec {
   hipEvent_t beg, end;
 };
 std::mutex g_tmu;
-bool g_timing = false;
+// 0: off; 1: one record per kernel launch; 2: one record per phase (the append, the
+// context attention, the generation attention: split pass and combine as one span)
+int g_timing = 0;
+enum TimeLevel { kLaunch = 1, kPhase = 2 };
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_spare;
 size_t g_events = 0;        // events created so far (all in g_spare or g_recs)
 size_t g_dropped = 0;       // launches not timed because the pool was empty
 
+// Record the launches `launch` makes under `name` when timing is at `level`.
+// The lock is never held while `launch` runs (it may time launches of its own).
 template <class F>
-hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+hipError_t timed_at(int level, const char* name, hipStream_t s, F&& launch) {
   hipEvent_t b = nullptr, e = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
-    if (!g_timing) return launch();
-    if (g_spare.size() >= 2) {
-      e = g_spare.back();
-      g_spare.pop_back();
-      b = g_spare.back();
-      g_spare.pop_back();
-    } else {
-      ++g_dropped;
+    if (g_timing == level) {
+      if (g_spare.size() >= 2) {
+        e = g_spare.back();
+        g_spare.pop_back();
+        b = g_spare.back();
+        g_spare.pop_back();
+      } else {
+        ++g_dropped;
+      }
     }
   }
   if (!b) return launch();
@@ -91,6 +97,11 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   std::lock_guard<std::mutex> lk(g_tmu);
   g_recs.push_back({name, b, e});
   return err;
+}
+// One kernel that is also a phase of its own.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  return timed_at(kPhase, name, s, [&] { return timed_at(kLaunch, name, s, launch); });
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -352,10 +363,18 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
       a.ws_row = a.ws_pre + (plan.num_gen + 1);
       a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_off);
       a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_off);
-      e = timed("decode_split", s, [&] { return pkv::launch_decode_split(a, s); });
-      if (e != hipSuccess) return hip_fail(e, "decode launch");
-      e = timed("decode_combine", s, [&] { return pkv::launch_decode_combine(a, s); });
-      if (e != hipSuccess) return hip_fail(e, "decode combine launch");
+      const char* failed = nullptr;
+      e = timed_at(kPhase, "decode", s, [&] {
+        hipError_t le = timed_at(kLaunch, "decode_split", s, [&] { return pkv::launch_decode_split(a, s); });
+        if (le != hipSuccess) {
+          failed = "decode launch";
+          return le;
+        }
+        le = timed_at(kLaunch, "decode_combine", s, [&] { return pkv::launch_decode_combine(a, s); });
+        if (le != hipSuccess) failed = "decode combine launch";
+        return le;
+      });
+      if (e != hipSuccess) return hip_fail(e, failed ? failed : "decode launch");
     } else {
       e = timed("attn_generic_gen", s, [&] { return pkv::launch_attn_generic(a, s); });
       if (e != hipSuccess) return hip_fail(e, "generation attention launch");
@@ -403,7 +422,7 @@ int32_t pkv_kernel_timing_enable(int32_t on) {
       ++g_events;
     }
   }
-  g_timing = on != 0;
+  g_timing = on == 2 ? kPhase : on ? kLaunch : 0;
   return PKV_OK;
 }
 

@@ -237,3 +237,22 @@ def test_decode_workgroup_cap_set_and_query():
     assert L.pkv_set_decode_workgroups(-1) == 7
     assert L.pkv_set_decode_workgroups(0) == 7
     assert L.pkv_set_decode_workgroups(-1) == 0
+
+
+def test_timed_launch_wrappers_return(tmp_path):
+    """Every launch goes through the timing wrappers (a phase span around per-kernel
+    records); with timing off, at either level or without a device they must return:
+    run in a child process under a time limit."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes\n"
+        "from paged_kv_gqa_rope_amd import _lib as L\n"
+        "buf = (ctypes.c_double * (8 * 32 * 2))()\n"
+        "rc = L.lib().pkv_rope_cos_sin(1e4, 64, 8, ctypes.addressof(buf), None)\n"
+        "assert rc in (L.PKV_OK, L.PKV_ERR_HIP), rc\n"
+        "print('returned', rc)\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and "returned" in res.stdout, res.stderr[-2000:]
