@@ -356,9 +356,14 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
       a.dec_cbw = plan.dec_cbw;
       a.dec_allcols = plan.dec_allcols ? 1 : 0;
       a.dec_cols = plan.dec_cols;
+      // ranges of tiles, each on one workgroup per lane
       const int32_t cap = g_decode_wgs.load(std::memory_order_relaxed);
       const int64_t target = cap > 0 ? cap : static_cast<int64_t>(pkv::kDecodeWGsPerCU) * std::max(dev.cus, 1);
-      a.dec_wgs = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(target, plan.dec_max_wgs)));
+      const int64_t lanes = std::max(plan.dec_lanes, 1);
+      const int64_t ranges = std::max<int64_t>(1, std::min(target, plan.dec_max_wgs) / lanes);
+      a.dec_wgs = static_cast<int32_t>(ranges * lanes);
+      a.dec_lanes = plan.dec_lanes;
+      a.dec_lane_cbs = plan.dec_lane_cbs;
       a.ws_pre = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan.ws_pre_off);
       a.ws_row = a.ws_pre + (plan.num_gen + 1);
       a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_off);

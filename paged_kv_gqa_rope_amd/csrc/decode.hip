@@ -60,7 +60,6 @@ constexpr int kCombHeads = 4;      // query heads (one wave each) per combine wo
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // 16 bytes of the cache.  With one column block every K/V byte is read once per step and
 // every load instruction covers whole rows (whole 128-byte lines), so the loads carry the
@@ -132,8 +131,7 @@ __device__ __forceinline__ int tiles_end(int t_end, int S) { return t_end > (S -
 
 // Generation request r as the split pass sees it (device lengths, kept to n >= 1 and
 // S >= n whatever they hold): n new tokens, S keys, `tiles` 32-key tiles, and `cbs` blocks
-// of 16 (token, query head) columns per KV head.  Its work units are its 32-key tiles
-// times its (head group, column block) segments.
+// of 16 (token, query head) columns per KV head.  Its work units are its 32-key tiles.
 struct ReqGeom {
   int n, S, tiles, cbs;
 };
@@ -144,9 +142,6 @@ __device__ __forceinline__ ReqGeom req_geom(const AttnArgs& a, int r, int G) {
   q.tiles = (q.S - 1) / kTile + 1;
   q.cbs = static_cast<int>(min64((static_cast<int64_t>(G) * q.n + 15) / 16, a.col_blocks));
   return q;
-}
-__device__ __forceinline__ int64_t req_units(const ReqGeom& q, int hgs) {
-  return static_cast<int64_t>(hgs) * q.cbs * q.tiles;
 }
 
 // Exclusive prefix sum of v over the workgroup's kThreads threads; *total gets the sum.
@@ -170,11 +165,6 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* tota
   return before + x - v;
 }
 
-__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 // Pieces of a workgroup's range, as listed in LDS: (request, head group, column block,
 // first tile) and (tiles, n, S, packed row of the request's first token).
@@ -206,7 +196,7 @@ __device__ __forceinline__ Piece read_piece(const int4* pa, const int4* pb, int 
 // NT: stream the cache with the nontemporal hint (every byte read once) or keep its lines
 // in L2 (several column blocks read the same keys).
 template <int KV, int HPS, int CBW, bool NT>
-__device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int lw, const int4* pla,
+__device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int k, const int plane, const int4* pla,
                                               const int4* plb, uint16_t (*vtile)[kTile * kVStride],
                                               uint16_t (*ktile)[kTile * kD], float (*ml)[16][2]) {
   // ALT: one KV head per segment, its waves sharing the tiles; otherwise every wave streams
@@ -220,7 +210,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
   const int lane = tid % kWave;
   const int li = lane % 16, lg = lane / 16;
-  const int G = a.H / a.Hkv, hgs = a.Hkv / HPS;
+  const int G = a.H / a.Hkv;
   constexpr int TS = ALT ? kWaves : 1;                         // tile stride of a wave's items
   const int base = ALT ? wave : 0;                              // first tile of a wave's items
   const int wh = ALT ? 0 : wave / CBW;                          // the wave's head in the segment
@@ -308,7 +298,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   float m_run, l_run;                                           // for column li
   f32x4 o[8];                                                   // O[column lg*4+i][dim nb*16+li]
   int key_lim;                                                  // keys 0 .. key_lim for column li
-  int c_t0, c_nt, c_cnt, c_kend, c_lim, c_ncol, c_valid, c_n, c_g, c_cb;
+  int c_t0, c_nt, c_cnt, c_kend, c_lim, c_ncol, c_valid, c_g, c_cb;
   int64_t c_slot;
   auto start_piece = [&](int p) {
     const Piece q = read_piece(pla, plb, p);
@@ -316,7 +306,6 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     c_t0 = q.t0;
     c_nt = q.nt;
     c_cnt = (q.nt + TS - 1) / TS;
-    c_n = n;
     c_cb = CBW > 1 ? wcb : q.cb;
     c_g = q.hg * HPS + wh;                                      // this wave's KV head
     c_kend = tiles_end(q.t0 + q.nt, S);
@@ -325,8 +314,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     c_lim = S - n + (c_cb * 16) / G;
     c_ncol = min(16, G * n - c_cb * 16);                        // valid columns of the block
     if (CBW == 1) c_ncol = min(c_ncol, a.dec_cols);
-    c_slot = CBW > 1 ? static_cast<int64_t>(q.r - a.req_begin) * hgs + q.hg + lw
-                     : (static_cast<int64_t>(q.r - a.req_begin) * hgs + q.hg) * a.col_blocks + q.cb + lw;
+    c_slot = static_cast<int64_t>(q.r - a.req_begin + k) * a.dec_lanes + plane;
     // Columns of the score tile: (token, query head) pairs, 16 per column block.  Lane
     // column li is token tok = gc / G of the request (position S - n + tok; it sees keys
     // up to that position: causal among a request's draft tokens) and head g*G + gc % G.
@@ -576,53 +564,55 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   }
 }
 
-// ---- range bookkeeping shared by the split passes
+// ---- range bookkeeping of the split pass
 //
-// gridDim.x workgroups share the batch's work units (32-key tiles of every segment,
-// requests in order, then segments, then keys) in equal contiguous ranges, so every
-// workgroup streams the same number of K/V bytes whatever the mix of lengths.  A segment
-// is (request, head group, column block), or (request, head group) when one workgroup
-// carries every column block (RING).  A workgroup's range cuts the segments it touches
-// into pieces; each piece leaves one partial state in slot (segment index + workgroup
-// index), which is unique because both grow along the units.  Launched workgroup w runs
-// on XCD w % 8 (round-robin dispatch); it takes range (w % 8) * (W / 8) + w / 8, so each
-// XCD (one L2) works through one contiguous eighth.
+// The batch's work is its generation requests' 32-key tiles, in request order (U units).
+// NL lanes (a.dec_lanes) run in lockstep: a lane is a head group (times a column block
+// where one head's segment holds a single block), and each of the Wr = gridDim.x / NL
+// ranges of about U / Wr consecutive units goes to NL workgroups, one per lane, which
+// stream the same tiles for their lanes' heads at about the same time: the neighbouring
+// head groups' pieces of a request's cache rows then leave HBM together.  Launched
+// workgroup w runs on XCD w % 8 (round-robin dispatch); it takes logical index
+// lw = (w % 8) * (W / 8) + w / 8, range lw / NL and lane lw % NL, so the lanes of a range
+// share an XCD and each XCD works through one contiguous eighth.  A range cuts the
+// requests it touches into pieces; the piece of request r (r-th generation request) and
+// range k on lane l leaves its partial state in slot (r + k) * NL + l, unique because
+// r + k grows along the units.
 struct RangeLds {
   int64_t part[2 * kWaves];
   int64_t start[3], walk[4];
   int4 pla[kPieceBatch], plb[kPieceBatch];
   int pcount;
 };
-template <bool RING>
-__device__ __forceinline__ int64_t units_of(const ReqGeom& q, int hgs) {
-  return RING ? static_cast<int64_t>(hgs) * q.tiles : req_units(q, hgs);
-}
-// Prefix sums of the units (and of the rows) over the requests, this workgroup's range
+// Prefix sums of the tiles (and of the rows) over the requests, this workgroup's range
 // and where it starts; workgroup 0 also records every request's first unit (and the
 // total) and first packed row for the combine.  Returns false for an empty range.
-template <bool RING>
-__device__ __forceinline__ bool range_begin(const AttnArgs& a, const int hgs, RangeLds& L, int& lw) {
+__device__ __forceinline__ bool range_begin(const AttnArgs& a, RangeLds& L, int& k, int& lane) {
   const int G = a.H / a.Hkv;
   const int R = a.req_end - a.req_begin;
   const int per = (R + kThreads - 1) / kThreads;
   const int i0 = min(static_cast<int>(threadIdx.x) * per, R), i1 = min(i0 + per, R);
   int64_t mine = 0, mrows = 0;
   for (int i = i0; i < i1; ++i) {
-    mine += units_of<RING>(req_geom(a, a.req_begin + i, G), hgs);
+    mine += req_geom(a, a.req_begin + i, G).tiles;
     mrows += a.ctx_len[a.req_begin + i];
   }
   int64_t U, rows_total;
   const int64_t before = block_exclusive_scan(mine, &U, L.part);
   const int64_t rows_before = block_exclusive_scan(mrows, &rows_total, L.part + kWaves);
-  const int W = gridDim.x, w = blockIdx.x;
-  lw = W % kXcds == 0 ? (w % kXcds) * (W / kXcds) + w / kXcds : w;
-  const int64_t u0 = static_cast<int64_t>(lw) * U / W, u1 = static_cast<int64_t>(lw + 1) * U / W;
+  const int W = gridDim.x, w = blockIdx.x, NL = max(a.dec_lanes, 1);
+  const int Wr = max(W / NL, 1);
+  const int lw = W % kXcds == 0 ? (w % kXcds) * (W / kXcds) + w / kXcds : w;
+  k = lw / NL;
+  lane = lw % NL;
+  const int kk = min(k, Wr - 1);
+  const int64_t u0 = static_cast<int64_t>(kk) * U / Wr, u1 = k < Wr ? static_cast<int64_t>(kk + 1) * U / Wr : u0;
   // The thread whose run holds unit u0 records its request, offset and first row.  Rows:
   // the generation rows follow each other in request order.
   if ((u0 >= before && u0 < before + mine) || w == 0) {
     int64_t acc = before, racc = a.row_begin + rows_before;
     for (int i = i0; i < i1; ++i) {
-      const int64_t units = units_of<RING>(req_geom(a, a.req_begin + i, G), hgs);
+      const int64_t units = req_geom(a, a.req_begin + i, G).tiles;
       if (w == 0) {
         a.ws_pre[i] = acc;
         a.ws_row[i] = racc;
@@ -650,32 +640,32 @@ __device__ __forceinline__ bool range_begin(const AttnArgs& a, const int hgs, Ra
   }
   return true;
 }
-// Thread 0 cuts the next part of the range into at most kPieceBatch pieces, listed in LDS
-// as (request, head group, column block, first tile) and (tiles, n, S, first row); every
-// thread gets their number (0: the range is done).
-template <bool RING>
-__device__ __forceinline__ int list_pieces(const AttnArgs& a, const int hgs, RangeLds& L) {
+// Thread 0 cuts the next part of the range into at most kPieceBatch pieces for `lane`,
+// listed in LDS as (request, head group, column block, first tile) and (tiles, n, S,
+// first row); every thread gets their number (0: the range is done).  A lane's column
+// block that a request does not have gets no piece.
+__device__ __forceinline__ int list_pieces(const AttnArgs& a, const int lane, RangeLds& L) {
   const int G = a.H / a.Hkv;
+  const int ncb = max(a.dec_lane_cbs, 1);
+  const int hg = lane / ncb, cb = lane % ncb;
   if (threadIdx.x == 0) {
     int r = a.req_begin + static_cast<int>(L.walk[0]);
     int64_t off = L.walk[1], left = L.walk[2], row0 = L.walk[3];
     int np = 0;
     while (left > 0 && r < a.req_end && np < kPieceBatch) {
       const ReqGeom q = req_geom(a, r, G);
-      const int64_t units = units_of<RING>(q, hgs);
-      if (off < units) {
-        const int64_t j = off / q.tiles;                         // segment of the request
-        const int t0 = static_cast<int>(off - j * q.tiles);
+      if (off < q.tiles) {
+        const int t0 = static_cast<int>(off);
         const int take = static_cast<int>(min64(q.tiles - t0, left));
-        const int hg = RING ? static_cast<int>(j) : static_cast<int>(j / q.cbs);
-        const int cb = RING ? 0 : static_cast<int>(j % q.cbs);
-        L.pla[np] = make_int4(r, hg, cb, t0);
-        L.plb[np] = make_int4(take, q.n, q.S, static_cast<int>(min64(max64(row0, -1), a.N)));
-        ++np;
+        if (cb < q.cbs) {
+          L.pla[np] = make_int4(r, hg, cb, t0);
+          L.plb[np] = make_int4(take, q.n, q.S, static_cast<int>(min64(max64(row0, -1), a.N)));
+          ++np;
+        }
         left -= take;
         off += take;
       }
-      if (off >= units) {
+      if (off >= q.tiles) {
         row0 += a.ctx_len[r];
         ++r;
         off = 0;
@@ -700,13 +690,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kWaves][kTile * kD];
   __shared__ float ml[kWaves][16][2];
   __shared__ RangeLds L;
-  const int hgs = a.Hkv / HPS;
-  int lw;
-  if (!range_begin<(CBW > 1)>(a, hgs, L, lw)) return;
+  int k, lane;
+  if (!range_begin(a, L, k, lane)) return;
   while (true) {
-    const int np = list_pieces<(CBW > 1)>(a, hgs, L);
+    const int np = list_pieces(a, lane, L);
     if (np == 0) return;                                        // uniform
-    decode_stream<KV, HPS, CBW, NT>(a, np, lw, L.pla, L.plb, vtile, ktile, ml);
+    decode_stream<KV, HPS, CBW, NT>(a, np, k, lane, L.pla, L.plb, vtile, ktile, ml);
     __syncthreads();                                            // the list is read before it is refilled
   }
 }
@@ -728,7 +717,7 @@ __global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(Attn
   const int n_dev = a.ctx_len[r], s_dev = a.seq_len[r];
   const int64_t P = a.ws_pre[rg], U = a.ws_pre[R], row0 = a.ws_row[rg];
   if (h >= a.H || tok >= n_dev) return;                             // wave-uniform
-  const int G = a.H / a.Hkv, B = a.dec_heads, hgs = a.Hkv / B;
+  const int G = a.H / a.Hkv, B = a.dec_heads;
   const int n = max(n_dev, 1), S = max(s_dev, n);                   // as the split pass keeps them
   const int tiles = (S - 1) / kTile + 1;
   const int cbs = static_cast<int>(min64((static_cast<int64_t>(G) * n + 15) / 16, a.col_blocks));
@@ -740,15 +729,16 @@ __global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(Attn
   // head group) and the column
   const bool all = a.dec_allcols != 0;
   const int c = tok * G + h % G, cb = all ? 0 : c / 16, col = all ? c : c % 16;
-  const int segs = all ? 1 : cbs;                                   // segments per head group
-  if (cb >= segs || col >= a.dec_cols || U <= 0 || W <= 0) return;
-  const int64_t s0 = P + (static_cast<int64_t>(hg) * segs + cb) * tiles, s1 = s0 + tiles;
-  const int64_t f = ((s0 + 1) * W - 1) / U, l = (s1 * W - 1) / U;  // first and last range
-  const int lwf = static_cast<int>(min64(max64(f, 0), W - 1));
-  const int np = static_cast<int>(min64(max64(l, lwf), W - 1)) - lwf + 1;
-  const int64_t seg = (static_cast<int64_t>(rg) * hgs + hg) * (all ? 1 : a.col_blocks) + cb;
-  const int64_t stride = static_cast<int64_t>(B) * a.dec_cols;      // entries between pieces
-  const int64_t e0 = ((seg + lwf) * B + wv) * a.dec_cols + col;    // entry of the first piece
+  const int ncb = max(a.dec_lane_cbs, 1), NL = max(a.dec_lanes, 1);
+  const int pl = hg * ncb + (ncb > 1 ? cb : 0);                     // the split-pass lane that computed it
+  const int Wr = max(W / NL, 1);
+  if ((!all && cb >= cbs) || col >= a.dec_cols || U <= 0 || W <= 0) return;
+  // the ranges that meet the request's tiles [P, P + tiles): its pieces, range k in slot (rg + k) * NL + pl
+  const int64_t f = ((P + 1) * Wr - 1) / U, l = ((P + tiles) * Wr - 1) / U;
+  const int kf = static_cast<int>(min64(max64(f, 0), Wr - 1));
+  const int np = static_cast<int>(min64(max64(l, kf), Wr - 1)) - kf + 1;
+  const int64_t stride = static_cast<int64_t>(NL) * B * a.dec_cols;          // entries between pieces
+  const int64_t e0 = ((static_cast<int64_t>(rg + kf) * NL + pl) * B + wv) * a.dec_cols + col;   // first piece
   const float2* op = reinterpret_cast<const float2*>(a.ws_o + e0 * kD) + lane;
   const int64_t ps = stride * (kD / 2);                             // float2 steps between pieces
   const float* mlp = a.ws_ml + e0 * 2;

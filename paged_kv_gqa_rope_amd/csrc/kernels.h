@@ -67,11 +67,14 @@ struct AttnArgs {
   int32_t dec_heads;             // KV heads per segment (1, 2 or 4)
   int32_t dec_cbw;               // waves per head, one column block each (1, 2 or 4)
   int32_t dec_allcols;           // 1: segments (request, head group) carry all column blocks
+  int32_t dec_lanes;             // workgroups per range of tiles (head groups x dec_lane_cbs)
+  int32_t dec_lane_cbs;          // column blocks with a lane of their own (1 unless one-head segments
+                                 // hold one column block each)
   int32_t dec_cols;              // columns stored per (piece, KV head): min(16, G * max_n), or G * max_n (dec_allcols)
-  int32_t dec_wgs;               // workgroups of the split pass
-  int64_t* ws_pre;               // [generation requests + 1] first unit of each request, total last
+  int32_t dec_wgs;               // workgroups of the split pass (ranges x dec_lanes)
+  int64_t* ws_pre;               // [generation requests + 1] first tile of each request, total last
   int64_t* ws_row;               // [generation requests + 1] first packed row of each request
-  float* ws_ml;                  // [slots][dec_heads][dec_cols][2]  (m, l) per piece
+  float* ws_ml;                  // [slots][dec_heads][dec_cols][2]  (m, l) per piece; slot (r + range) * lanes + lane
   float* ws_o;                   // [slots][dec_heads][dec_cols][D]  o per piece
   int32_t num_cus;               // compute units of the device
 };

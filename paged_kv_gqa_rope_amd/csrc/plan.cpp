@@ -170,11 +170,13 @@ void plan_decode(const pkv_attn_desc& d, const pkv_batch_desc& b, BatchPlan* p) 
   for (int32_t r = p->num_ctx; r < p->B; ++r) {
     const int64_t n = b.host_context_lengths[r];
     const int64_t S = std::max<int64_t>(b.host_sequence_lengths[r], n);
-    units += hgs * (p->dec_allcols ? 1 : (G * n + 15) / 16) * ((S - 1) / kDecodeTile + 1);
+    units += (S - 1) / kDecodeTile + 1;
   }
   p->dec_units = units;
-  p->dec_segments = static_cast<int64_t>(p->num_gen) * hgs * (p->dec_allcols ? 1 : p->col_blocks);
-  p->dec_max_wgs = std::min<int64_t>(kDecodeMaxWGs, units);
+  p->dec_lane_cbs = p->dec_allcols ? 1 : p->col_blocks;
+  p->dec_lanes = static_cast<int32_t>(hgs * p->dec_lane_cbs);
+  p->dec_segments = static_cast<int64_t>(p->num_gen) * p->dec_lanes;
+  p->dec_max_wgs = p->dec_lanes * std::min<int64_t>(std::max<int64_t>(1, kDecodeMaxWGs / p->dec_lanes), units);
   p->dec_cols = p->dec_allcols ? G * p->max_gen_n : std::min(16, G * p->max_gen_n);
   const int64_t entries = (p->dec_segments + p->dec_max_wgs) * p->dec_heads * p->dec_cols;
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
@@ -195,7 +197,7 @@ size_t workspace_upper_bound(const pkv_attn_desc& d, int32_t max_num_requests, i
   const int64_t R = max_num_requests;
   const int64_t cbmax = (std::min<int64_t>(G * kMaxGenTokens, kMaxDecodeCols) + 15) / 16;
   const int64_t tiles = (static_cast<int64_t>(max_seq_len) - 1) / kDecodeTile + 1;
-  const int64_t W = std::min<int64_t>(kDecodeMaxWGs, R * d.num_kv_heads * cbmax * tiles);
+  const int64_t W = std::max<int64_t>(kDecodeMaxWGs, d.num_kv_heads * cbmax);   // workgroups, at most
   // segments carrying all column blocks: at most Hkv segments per request, at most 4 heads
   // x G * kMaxGenTokens columns per slot
   const int64_t all_cols = std::min<int64_t>(G * kMaxGenTokens, kMaxDecodeCols);

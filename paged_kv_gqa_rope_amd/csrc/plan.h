@@ -32,9 +32,12 @@ struct BatchPlan {
   bool dec_allcols = false;   // segments (request, head group) carry all column blocks
   int32_t dec_cols = 0;       // columns stored per (piece, KV head): min(16, G * max_gen_n), or G * max_gen_n
                               // when segments carry all column blocks
-  int64_t dec_units = 0;      // 32-key tiles summed over all segments
-  int64_t dec_segments = 0;   // generation requests x head groups (x col_blocks unless dec_allcols)
-  int64_t dec_max_wgs = 0;    // split-pass workgroups the workspace has room for: min(kDecodeMaxWGs, units)
+  int64_t dec_units = 0;      // 32-key tiles summed over the generation requests
+  int32_t dec_lane_cbs = 1;   // column blocks with a lane of their own (one-head segments with drafts)
+  int32_t dec_lanes = 0;      // lanes: head groups x dec_lane_cbs; each range of tiles runs on one per lane
+  int64_t dec_segments = 0;   // generation requests x lanes
+  int64_t dec_max_wgs = 0;    // split-pass workgroups the workspace has room for: a multiple of the lanes,
+                              // at most max(kDecodeMaxWGs, lanes), at most units x lanes
   // workspace layout (bytes)
   size_t ws_pre_off = 0, ws_ml_off = 0, ws_o_off = 0, ws_bytes = 0;
 };

@@ -209,15 +209,16 @@ int main(int argc, char** argv) {
       const int64_t Gq = x.num_heads / x.num_kv_heads, hgs = x.num_kv_heads / p.dec_heads;
       const bool all = p.dec_allcols;
       int64_t units = 0;
-      for (size_t r = p.num_ctx; r < b.S.size(); ++r)
-        units += hgs * (all ? 1 : (Gq * b.n[r] + 15) / 16) * ((b.S[r] + 31) / 32);
+      for (size_t r = p.num_ctx; r < b.S.size(); ++r) units += (b.S[r] + 31) / 32;
+      const int64_t lanes = hgs * (all ? 1 : p.col_blocks);
       // heads x column waves fill the 4 waves (or one head whose waves share the tiles)
       const bool heads_ok = (p.dec_heads == 1 && p.dec_cbw == 1) || p.dec_heads * p.dec_cbw == 4;
       const bool waves_ok = p.dec_cbw == 1 || (x.num_kv_heads % 4 == 0 && p.dec_cbw >= p.col_blocks && all);
       const int64_t cols = all ? Gq * p.max_gen_n : std::min<int64_t>(16, Gq * p.max_gen_n);
+      const int64_t max_wgs = lanes * std::min<int64_t>(std::max<int64_t>(1, pkv::kDecodeMaxWGs / lanes), units);
       if (!waves_ok || x.num_kv_heads % p.dec_heads != 0 || units != p.dec_units || !heads_ok ||
-          p.dec_max_wgs != std::min<int64_t>(pkv::kDecodeMaxWGs, units) || p.dec_cols != cols ||
-          p.dec_segments != static_cast<int64_t>(p.num_gen) * hgs * (all ? 1 : p.col_blocks)) {
+          p.dec_lanes != lanes || p.dec_max_wgs != max_wgs || p.dec_cols != cols ||
+          p.dec_segments != static_cast<int64_t>(p.num_gen) * lanes) {
         std::printf("FAIL split plan (iteration %d)\n", it);
         return 1;
       }
