@@ -701,15 +701,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // One wave per (generation token, query head), kCombHeads query heads per workgroup, two
-// dimensions per lane.  The pieces of the token's segment are the workgroups whose unit
-// ranges meet the segment's units (found from the recorded first units and the same range
+// dimensions per lane.  The pieces of the token's (request, lane) are the ranges that meet
+// the request's tiles (found from the recorded first tiles and the same range
 // arithmetic).  M = max m_p and L = sum 2^(m_p-M) l_p over them, then lane d sums
 // 2^(m_p-M) o_p[2d, 2d+1] over the pieces in order.  64 pieces at a time: lane p holds
-// piece p's (m, l), butterfly reductions give M and L in a fixed order, and the first
-// eight o_p are loaded before the weights are known.  Every metadata load is issued
-// before the first use.  Pieces past a draft token's position hold m = -inf and weigh
-// nothing; the piece holding key 0 makes M finite.
-__global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(AttnArgs a) {
+// piece p's (m, l), butterfly reductions give M and L in a fixed order, and the o_p are
+// loaded eight at a time.  Every metadata load is issued before the first use; at most
+// 64 VGPRs keep 8 waves per SIMD resident (one round of waves for most batches).  Pieces
+// past a draft token's position hold m = -inf and weigh nothing; the piece holding key 0
+// makes M finite.
+__global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_combine_kernel(AttnArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int h = blockIdx.x * kCombHeads + wave, rg = blockIdx.y, tok = blockIdx.z;
   const int r = a.req_begin + rg;
@@ -742,9 +743,6 @@ __global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(Attn
   const float2* op = reinterpret_cast<const float2*>(a.ws_o + e0 * kD) + lane;
   const int64_t ps = stride * (kD / 2);                             // float2 steps between pieces
   const float* mlp = a.ws_ml + e0 * 2;
-  float2 v[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = k < np ? op[k * ps] : make_float2(0.f, 0.f);
   float M = -INFINITY;
   for (int pb = 0; pb < np; pb += kWave) {
     const int p = pb + lane;
@@ -762,14 +760,6 @@ __global__ __launch_bounds__(kCombHeads * kWave) void decode_combine_kernel(Attn
     L += wave_sum(wt * lp);
     const int cnt = min(kWave, np - pb);
     int k = 0;
-    if (pb == 0) {
-#pragma unroll
-      for (; k < 8; ++k) {
-        const float w = __shfl(wt, k, kWave);                      // 0 past the last piece
-        ox += w * v[k].x;
-        oy += w * v[k].y;
-      }
-    }
     for (; k < cnt; k += 8) {                                      // eight loads in flight
       float2 u[8];
 #pragma unroll
