@@ -7,15 +7,21 @@
 // (get_buffers).  RoPE is the GPT-NeoX variant named in "TensorRT-LLM source analysis
 // report", 1.1; rotation of pairs (j, j + R/2) is the reading documented in pkv.h.
 //
-// Memory-bound: each workgroup owns a few consecutive packed rows (tokens) and spreads
-// the (head, 8-element group) tasks of those tokens over its 256 threads, so every
-// load and store is a 16-byte access and neighbouring lanes touch neighbouring bytes.
-// Arithmetic is fp64 with contraction off and one rounding per stored element, so the
-// stored bits depend only on the inputs and the table.  With a per-head q/k norm
-// ("TensorRT-LLM source analysis report", 1.1, QK LayerNorm; the teardown's kernel
-// directory lists a fused QK-norm + RoPE kernel), a pre-pass computes each head's mean
-// and inverse deviation into LDS and the tasks normalise their elements before rotating.
+// Memory-bound: each wave takes one token at a time and streams its q, k and v rows in
+// 1 KB instructions (64 lanes x one 8-element chunk), so every load and store is
+// coalesced and a lane's chunk sits at the same place in every head it visits.  A
+// rotate-half pair's partner chunk is in the same instruction, R/16 lanes away, and comes
+// over a lane shuffle; interleaved pairs sit inside one chunk.  A wave issues the loads
+// of a whole batch of instructions before any of their arithmetic.  Arithmetic is fp64
+// with contraction off and one rounding per stored element, so the stored bits depend
+// only on the inputs and the table.  With a per-head q/k norm ("TensorRT-LLM source
+// analysis report", 1.1, QK LayerNorm; the teardown's kernel directory lists a fused
+// QK-norm + RoPE kernel), the wave copies the batch's q and k rows into LDS, one lane
+// per head sums its row in index order, and each lane normalises its chunk and its
+// partner's before rotating.
+#include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -23,50 +29,41 @@
 namespace pkv {
 namespace {
 
-constexpr int kAppendThreads = 256;
-constexpr int kMaxTokensPerWg = 8;
+constexpr int kAppendWaves = 4;
+constexpr int kAppendThreads = kAppendWaves * kWave;
+constexpr int kMaxTokensPerWg = 64;
 constexpr int kFlatMaxRequests = 4096;
+constexpr int kAppendWGs = 2048;         // about eight workgroups per CU: many tokens in flight
+constexpr size_t kMaxDynamicLds = 64 * 1024;
+
+// chunk instructions whose loads a wave holds at once (bf16 chunks are 16 bytes, fp32 32)
+template <int IO, bool NORM>
+__host__ __device__ constexpr int append_batch() {
+  return IO == F_BF16 ? 6 : (NORM ? 5 : 4);
+}
+// per-wave LDS of the norm: the batch's q/k rows (padded by 16 bytes) and their statistics
+template <int IO, bool NORM>
+__host__ __device__ constexpr int norm_rows(int D) {
+  return NORM ? append_batch<IO, NORM>() * (kWave * 8 / D) : 0;
+}
+template <int IO>
+__host__ __device__ constexpr int norm_row_bytes(int D) {
+  return D * (IO == F_BF16 ? 2 : 4) + 16;
+}
+template <int IO, bool NORM>
+__host__ __device__ constexpr int norm_wave_bytes(int D) {
+  return norm_rows<IO, NORM>(D) * (norm_row_bytes<IO>(D) + 16);
+}
 
 // Streaming accesses: every input element is read once and every output element written
-// once per step, so stores, and loads of inputs nothing reads again, carry the
-// nontemporal hint.  (With a q/k norm the statistics pass reads q and k first; their
-// second read then comes from the caches, so those loads stay ordinary.)
+// once per step, so loads and stores of q, k, v and their outputs carry the nontemporal
+// hint; the table and the norm weights stay ordinary (shared by many lanes).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-template <bool NT>
-__device__ __forceinline__ uint4 ld16(const void* p) {
-  if constexpr (NT) {
-    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *static_cast<const uint4*>(p);
-  }
-}
-__device__ __forceinline__ void st16(void* p, uint4 u) {
-  __builtin_nontemporal_store(u32x4_t{u.x, u.y, u.z, u.w}, static_cast<u32x4_t*>(p));
-}
-__device__ __forceinline__ void st8(void* p, uint2 u) {
-  __builtin_nontemporal_store(u32x2_t{u.x, u.y}, static_cast<u32x2_t*>(p));
-}
-
 // 8 raw io elements as loaded (bf16: one 16-byte vector; fp32: two)
 struct Raw8 {
   uint4 a, b;
 };
-
-template <int F, bool NT = false>
-__device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {
-  Raw8 r;
-  if constexpr (F == F_BF16) {
-    r.a = ld16<NT>(static_cast<const uint16_t*>(base) + off);
-    r.b = make_uint4(0, 0, 0, 0);
-  } else {
-    const float* p = static_cast<const float*>(base) + off;
-    r.a = ld16<NT>(p);
-    r.b = ld16<NT>(p + 4);
-  }
-  return r;
-}
 
 template <int F>
 __device__ __forceinline__ void widen8(const Raw8& r, double (&x)[8]) {
@@ -81,51 +78,6 @@ __device__ __forceinline__ void widen8(const Raw8& r, double (&x)[8]) {
     const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = static_cast<double>(__uint_as_float(w[i]));
-  }
-}
-
-template <int F, bool NT = false>
-__device__ __forceinline__ void load8(const void* base, int64_t off, double (&x)[8]) {
-  widen8<F>(load_raw8<F, NT>(base, off), x);
-}
-
-// Round y (times `mul` for fp8 and int8) once to format F and store 8 elements at base+off.
-template <int F>
-__device__ __forceinline__ void store8(void* base, int64_t off, const double (&y)[8], double mul) {
-  if constexpr (F == F_FP32) {
-    float* p = static_cast<float*>(base) + off;
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = __float_as_uint(static_cast<float>(y[i]));
-    st16(p, make_uint4(w[0], w[1], w[2], w[3]));
-    st16(p + 4, make_uint4(w[4], w[5], w[6], w[7]));
-  } else if constexpr (F == F_BF16) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f64x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
-    st16(static_cast<uint16_t*>(base) + off, make_uint4(w[0], w[1], w[2], w[3]));
-  } else {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[i / 4] |= (F == F_INT8 ? f64_to_int8(y[i] * mul) : f64_to_e4m3(y[i] * mul)) << (8 * (i % 4));
-    st8(static_cast<uint8_t*>(base) + off, make_uint2(w[0], w[1]));
-  }
-}
-
-// y1 = x1*c - x2*s, y2 = x2*c + x1*s: two fp64 products and one add/subtract each.
-__device__ __forceinline__ void rotate8(const double (&x1)[8], const double (&x2)[8], const double2 (&cs)[8],
-                                        double (&y1)[8], double (&y2)[8]) {
-#pragma clang fp contract(off)
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const double2 t = cs[i];
-    const double a = x1[i] * t.x;
-    const double b = x2[i] * t.y;
-    const double e = x2[i] * t.x;
-    const double f = x1[i] * t.y;
-    y1[i] = a - b;
-    y2[i] = e + f;
   }
 }
 
@@ -156,189 +108,6 @@ struct TokenSlot {
   int32_t r, m, blk, slot;      // blk < 0: table entry out of range (skip the K/V store)
 };
 
-// One (token, task) unit of work.  Tasks of a token: rotation groups of 8 pairs for
-// every q and k head, pass-through groups of 8 dims past the rotary part, and groups of
-// 8 v dims.  Loads of a task are issued before any of its arithmetic.
-constexpr int kHeadsPerRotTask = 4;
-
-// One (token, task) unit of work.  Tasks of a token, in order: rotation tasks (one
-// group of 8 pairs for up to kHeadsPerRotTask q/k heads, so the table slice is read
-// once for all of them), pass-through groups of 8 dims past the rotary part, and
-// groups of 8 v dims.  A task's loads are all issued before its arithmetic.
-template <int IO, int KV, int RS, bool NORM>
-__device__ __forceinline__ void append_task(const AppendArgs& a, const TokenSlot& tk, int t, int Hq,
-                                            const void* __restrict__ q, const void* __restrict__ k,
-                                            const void* __restrict__ v, const double* __restrict__ cs_base,
-                                            void* __restrict__ q_out, void* __restrict__ pool,
-                                            const double2* __restrict__ stat) {
-  constexpr bool NTQK = !NORM;               // q/k read only here (no norm statistics pass)
-  const int R = RS != kRopeNone ? a.R : 0;
-  const int half = R / 2;
-  const int rg = R / 16, pg = (a.D - R) / 8, vg = a.D / 8;
-  // element offsets of a task's 8 pairs: rotate-half -> first elements at j0, partners
-  // at j0 + R/2; interleaved -> 16 consecutive elements from 2*j0 (pairs (2j, 2j+1))
-  auto off_a = [&](int j0) { return RS == kRopeGptj ? 2 * j0 : j0; };
-  auto off_b = [&](int j0) { return RS == kRopeGptj ? 2 * j0 + 8 : j0 + half; };
-  const int qk = Hq + a.Hkv;
-  const int nhc = (qk + kHeadsPerRotTask - 1) / kHeadsPerRotTask;
-  auto pool_off = [&](int which, int g) {
-    return ((static_cast<int64_t>(tk.blk) * 2 + which) * a.T + tk.slot) * static_cast<int64_t>(a.Hkv) * a.D +
-           static_cast<int64_t>(g) * a.D;
-  };
-  // normalise a widened group of head `head` (NORM only); (mean, inv) come from stat[head]
-  auto normalise = [&](double (&x)[8], int head, int dim0) {
-    if constexpr (NORM) {
-      const bool isq = head < Hq;
-      norm8(x, dim0, stat[head], isq ? a.qn_w : a.kn_w, isq ? a.qn_b : a.kn_b);
-    }
-  };
-  auto head_src = [&](int head, const void*& src, int64_t& off) {
-    const bool isq = head < Hq;
-    src = isq ? q : k;
-    off = isq ? tk.row * a.q_stride + static_cast<int64_t>(head) * a.D
-              : tk.row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
-  };
-  if (t < nhc * rg) {                                       // rotated pair groups
-    if (tk.m >= a.max_pos) return;
-    const int hc = t / max(rg, 1), j0 = (t % max(rg, 1)) * 8;
-    const int h0 = hc * kHeadsPerRotTask;
-    const int nh = min(kHeadsPerRotTask, qk - h0);
-    Raw8 r1[kHeadsPerRotTask], r2[kHeadsPerRotTask];
-#pragma unroll
-    for (int u = 0; u < kHeadsPerRotTask; ++u) {
-      if (u < nh) {
-        const void* src;
-        int64_t off;
-        head_src(h0 + u, src, off);
-        r1[u] = load_raw8<IO, NTQK>(src, off + off_a(j0));
-        r2[u] = load_raw8<IO, NTQK>(src, off + off_b(j0));
-      }
-    }
-    const double2* cs = reinterpret_cast<const double2*>(cs_base) + static_cast<int64_t>(tk.m) * half + j0;
-    double2 c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = cs[i];
-#pragma unroll
-    for (int u = 0; u < kHeadsPerRotTask; ++u) {
-      if (u >= nh) break;
-      const int head = h0 + u;
-      double x1[8], x2[8], y1[8], y2[8];
-      if constexpr (RS == kRopeGptj) {                    // de-interleave the 16 elements
-        double e0[8], e1[8];
-        widen8<IO>(r1[u], e0);
-        widen8<IO>(r2[u], e1);
-        normalise(e0, head, off_a(j0));
-        normalise(e1, head, off_b(j0));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x1[i] = e0[2 * i];
-          x2[i] = e0[2 * i + 1];
-          x1[i + 4] = e1[2 * i];
-          x2[i + 4] = e1[2 * i + 1];
-        }
-      } else {
-        widen8<IO>(r1[u], x1);
-        widen8<IO>(r2[u], x2);
-        normalise(x1, head, off_a(j0));
-        normalise(x2, head, off_b(j0));
-      }
-      rotate8(x1, x2, c, y1, y2);
-      double s1[8], s2[8];                                // the two stored groups of 8
-      if constexpr (RS == kRopeGptj) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s1[2 * i] = y1[i];
-          s1[2 * i + 1] = y2[i];
-          s2[2 * i] = y1[i + 4];
-          s2[2 * i + 1] = y2[i + 4];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          s1[i] = y1[i];
-          s2[i] = y2[i];
-        }
-      }
-      if (head < Hq) {
-        const int64_t o = tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D;
-        store8<IO>(q_out, o + off_a(j0), s1, 1.0);
-        store8<IO>(q_out, o + off_b(j0), s2, 1.0);
-      } else if (tk.blk >= 0) {
-        const int64_t o = pool_off(0, head - Hq);
-        store8<KV>(pool, o + off_a(j0), s1, a.inv_k_scale);
-        store8<KV>(pool, o + off_b(j0), s2, a.inv_k_scale);
-      }
-    }
-  } else if (t < nhc * rg + qk * pg) {                      // dimensions past the rotary part
-    t -= nhc * rg;
-    const int head = t / pg, j = R + (t % pg) * 8;
-    const void* src;
-    int64_t off;
-    head_src(head, src, off);
-    double x[8];
-    load8<IO, NTQK>(src, off + j, x);
-    normalise(x, head, j);
-    if (head < Hq)
-      store8<IO>(q_out, tk.row * a.H * a.D + static_cast<int64_t>(head) * a.D + j, x, 1.0);
-    else if (tk.blk >= 0)
-      store8<KV>(pool, pool_off(0, head - Hq) + j, x, a.inv_k_scale);
-  } else {                                                  // values, not rotated
-    t -= nhc * rg + qk * pg;
-    const int g = t / vg, j = (t % vg) * 8;
-    double x[8];
-    load8<IO, true>(v, tk.row * a.kv_stride + static_cast<int64_t>(g) * a.D + j, x);
-    if (tk.blk >= 0) store8<KV>(pool, pool_off(1, g) + j, x, a.inv_v_scale);
-  }
-}
-
-// (mean, 1/sqrt(var + eps)) of one head's D elements: fp64 sums in index order.  The
-// row's loads are issued together (all of a bf16 row, half of an fp32 row of 128 at a
-// time) so that one memory latency covers them, and a bf16 row loaded for the mean is
-// reused for the variance.
-template <int IO, int D>
-__device__ __forceinline__ void row_stats(const void* src, int64_t off, bool layer, double eps, double& mean,
-                                          double& inv) {
-  constexpr int NG = D / 8;                       // groups of 8 elements
-  constexpr int BATCH = IO == F_BF16 ? NG : 8;    // groups held in registers at once
-  Raw8 r[BATCH];
-  auto fetch = [&](int g0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) r[b] = load_raw8<IO>(src, off + static_cast<int64_t>(g0 + b) * 8);
-  };
-  mean = 0.0;
-  if (layer) {
-    double s = 0.0;
-#pragma unroll
-    for (int g0 = 0; g0 < NG; g0 += BATCH) {
-      fetch(g0);
-#pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        double x[8];
-        widen8<IO>(r[b], x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s += x[i];
-      }
-    }
-    mean = s / static_cast<double>(D);
-  }
-  double ss = 0.0;
-#pragma unroll
-  for (int g0 = 0; g0 < NG; g0 += BATCH) {
-    if (!(layer && BATCH == NG)) fetch(g0);      // a whole bf16 row is still in r
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      double x[8];
-      widen8<IO>(r[b], x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double d = x[i] - mean;
-        ss += d * d;
-      }
-    }
-  }
-  inv = 1.0 / __builtin_sqrt(ss / static_cast<double>(D) + eps);
-}
-
 __device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row, int r, int i) {
   TokenSlot tk;
   tk.row = row;
@@ -351,17 +120,366 @@ __device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row,
   return tk;
 }
 
+// A token read from LDS lands in vector registers; its fields are the same in every
+// lane, and saying so keeps the buffer descriptors built from them in scalar registers.
+__device__ __forceinline__ TokenSlot uniform_slot(const TokenSlot& t) {
+  TokenSlot u;
+  const uint64_t row = static_cast<uint64_t>(t.row);
+  u.row = static_cast<int64_t>((static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row >> 32))) << 32) |
+                               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row))));
+  u.r = __builtin_amdgcn_readfirstlane(t.r);
+  u.m = __builtin_amdgcn_readfirstlane(t.m);
+  u.blk = __builtin_amdgcn_readfirstlane(t.blk);
+  u.slot = __builtin_amdgcn_readfirstlane(t.slot);
+  return u;
+}
+
+// Intra-wave LDS hand-over: the wave's stores are visible to its own later loads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint4 shfl16(uint4 v, int src) {
+  return make_uint4(__shfl(v.x, src), __shfl(v.y, src), __shfl(v.z, src), __shfl(v.w, src));
+}
+
+// A token's q, k and v rows are walked as 8-element chunks, 64 per instruction:
+// instructions [0, nq) cover q, then nk of k, then nk of v.  D / 8 chunks make a head and
+// divide 64, so lane l always holds chunk l % (D/8) of some head.
+struct RowGeom {
+  int cph, nqc, nkc, nq, nk, nqk, ntot;
+  __device__ RowGeom(const AppendArgs& a, int Hq) {
+    cph = a.D / 8;
+    nqc = Hq * cph;
+    nkc = a.Hkv * cph;
+    nq = (nqc + kWave - 1) / kWave;
+    nk = (nkc + kWave - 1) / kWave;
+    nqk = nq + nk;
+    ntot = nqk + nk;
+  }
+};
+
+// Raw buffer accesses (gfx9-family descriptor: stride 0, 32-bit data format, range
+// checked per access).  A lane whose chunk is not stored or loaded gets an offset past
+// every range: its load returns zeros and its store is dropped.  Every chunk instruction
+// thus issues the same memory operations whatever its lanes' roles, so the compiler's
+// wait counts stay exact instead of falling back to draining all outstanding accesses.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNT = 2;                        // nontemporal cache policy (loads of inputs read once)
+constexpr uint32_t kOff = 0x80000000u;           // past every range
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufWord3);
+}
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kBufNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void bstore16(Rsrc r, uint32_t off, uint4 u) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{u.x, u.y, u.z, u.w}, r, static_cast<int>(off), 0, 0);
+}
+__device__ __forceinline__ void bstore8(Rsrc r, uint32_t off, uint2 u) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{u.x, u.y}, r, static_cast<int>(off), 0, 0);
+}
+template <int F>
+__host__ __device__ constexpr int fmt_bytes() {
+  return F == F_FP32 ? 4 : F == F_BF16 ? 2 : 1;
+}
+
+// y (times `mul` for fp8 and int8) rounded once to format F: 8 elements as stored
+// (bf16 in .a, fp32 in .a and .b, fp8 and int8 in .a.x and .a.y).
+template <int F>
+__device__ __forceinline__ Raw8 pack8(const double (&y)[8], double mul) {
+  Raw8 o;
+  o.b = make_uint4(0, 0, 0, 0);
+  if constexpr (F == F_FP32) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = __float_as_uint(static_cast<float>(y[i]));
+    o.a = make_uint4(w[0], w[1], w[2], w[3]);
+    o.b = make_uint4(w[4], w[5], w[6], w[7]);
+  } else if constexpr (F == F_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f64x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
+    o.a = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i / 4] |= (F == F_INT8 ? f64_to_int8(y[i] * mul) : f64_to_e4m3(y[i] * mul)) << (8 * (i % 4));
+    o.a = make_uint4(w[0], w[1], 0, 0);
+  }
+  return o;
+}
+// One chunk of format F at off: exactly one or two buffer stores whatever the lane.
+template <int F>
+__device__ __forceinline__ void store8(Rsrc r, uint32_t off, const Raw8& o) {
+  if constexpr (F == F_FP32) {
+    bstore16(r, off, o.a);
+    bstore16(r, off + 16, o.b);
+  } else if constexpr (F == F_BF16) {
+    bstore16(r, off, o.a);
+  } else {
+    bstore8(r, off, make_uint2(o.a.x, o.a.y));
+  }
+}
+__device__ __forceinline__ Raw8 select8(bool c, const Raw8& p, const Raw8& q) {
+  Raw8 o;
+  o.a = make_uint4(c ? p.a.x : q.a.x, c ? p.a.y : q.a.y, c ? p.a.z : q.a.z, c ? p.a.w : q.a.w);
+  o.b = make_uint4(c ? p.b.x : q.b.x, c ? p.b.y : q.b.y, c ? p.b.z : q.b.z, c ? p.b.w : q.b.w);
+  return o;
+}
+
+// Loads of instructions [b0, b0 + NB) of one token (lanes past a row's end get zeros).
+template <int IO, int NB>
+__device__ __forceinline__ void append_load(const AppendArgs& a, const RowGeom& g, const TokenSlot& tk, int lane,
+                                            int b0, bool live, Raw8 (&r)[NB]) {
+  constexpr int CB = 8 * fmt_bytes<IO>();        // bytes of one chunk
+  const unsigned char* qb = static_cast<const unsigned char*>(a.q) + tk.row * a.q_stride * fmt_bytes<IO>();
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k) + tk.row * a.kv_stride * fmt_bytes<IO>();
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v) + tk.row * a.kv_stride * fmt_bytes<IO>();
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int i = b0 + u;
+    const bool isq = i < g.nq, isk = i < g.nqk;
+    const Rsrc rs = rsrc(isq ? qb : isk ? kb : vb, static_cast<int64_t>(isq ? g.nqc : g.nkc) * CB);
+    const int ch = (isq ? i : isk ? i - g.nq : i - g.nqk) * kWave + lane;
+    const uint32_t off = live && i < g.ntot ? static_cast<uint32_t>(ch) * CB : kOff;
+    r[u].a = bload16(rs, off);
+    r[u].b = IO == F_FP32 ? bload16(rs, off + 16) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Rotation role of a lane's chunk (dims e0 .. e0+7), the same in every instruction:
+// 1 rotate-half first half (partner R/16 lanes up), 2 second half (partner R/16 lanes
+// down), 3 interleaved pairs inside the chunk, 0 none (dims past the rotary part).
+struct Role {
+  int role, jt, poff;
+};
+// Rotate-half over whole 128-dim bf16 heads: a head is one 16-lane DPP row and partner
+// chunks are 8 lanes apart, so the exchange is a row rotation (no LDS traffic).
+constexpr int kRopeNeoxRow = 3;
+template <int RS>
+__host__ __device__ constexpr bool neox() {
+  return RS == kRopeNeox || RS == kRopeNeoxRow;
+}
+__device__ __forceinline__ uint4 row_ror8(uint4 v) {
+  return make_uint4(__builtin_amdgcn_mov_dpp(v.x, 0x128, 0xF, 0xF, false),
+                    __builtin_amdgcn_mov_dpp(v.y, 0x128, 0xF, 0xF, false),
+                    __builtin_amdgcn_mov_dpp(v.z, 0x128, 0xF, 0xF, false),
+                    __builtin_amdgcn_mov_dpp(v.w, 0x128, 0xF, 0xF, false));
+}
+template <int RS>
+__device__ __forceinline__ Role chunk_role(int e0, int R) {
+  const int half = R / 2;
+  Role r{0, 0, 0};
+  if constexpr (neox<RS>()) {
+    if (e0 < half) r = Role{1, e0, half / 8};
+    else if (e0 < R) r = Role{2, e0 - half, -(half / 8)};
+  } else if constexpr (RS == kRopeGptj) {
+    if (e0 < R) r = Role{3, e0 / 2, 0};
+  }
+  return r;
+}
+// (cos, sin) of the lane's pairs at the token's position (row 0 where nothing rotates)
+template <int RS>
+__device__ __forceinline__ void load_table(const AppendArgs& a, const TokenSlot& tk, const Role& rl,
+                                           double2 (&cs)[8]) {
+  if constexpr (RS != kRopeNone) {
+    const double2* t = reinterpret_cast<const double2*>(a.cos_sin) +
+                       (rl.role != 0 && tk.m < a.max_pos ? static_cast<int64_t>(tk.m) * (a.R / 2) + rl.jt : 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cs[k] = t[RS == kRopeGptj ? k % 4 : k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cs[k] = make_double2(0.0, 0.0);
+  }
+}
+
+// Arithmetic and stores of instructions [b0, b0 + NB) of one token.  Rotation roles of a
+// lane's chunk (dims e0 .. e0+7): rotate-half first half (partner R/16 lanes up), second
+// half (partner R/16 lanes down), interleaved (pairs inside the chunk), or none (dims
+// past the rotary part).
+template <int IO, int KV, int RS, bool NORM, int NB>
+__device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeom& g, const TokenSlot& tk,
+                                               const Role& rl, const double2 (&cs)[8], int lane, int b0,
+                                               const Raw8 (&r)[NB], unsigned char* __restrict__ stage,
+                                               const float* __restrict__ wts) {
+#pragma clang fp contract(off)
+  constexpr int kRaw = IO == F_BF16 ? 0 : 1;     // fp32 chunks are two 16-byte halves
+  constexpr int CB = 8 * fmt_bytes<IO>(), KB = 8 * fmt_bytes<KV>();
+  const int D = a.D;
+  const int cph = g.cph, hpi = kWave / cph;
+  const int c = lane % cph, e0 = c * 8;
+  const int role = rl.role, poff = rl.poff;
+  // positions past the table (rejected by the host) leave the rotated dims unwritten
+  const bool rot_ok = tk.m < a.max_pos;
+  const bool kv_ok = tk.blk >= 0;
+  const int64_t kdst = ((static_cast<int64_t>(tk.blk) * 2) * a.T + tk.slot) * static_cast<int64_t>(a.Hkv) * D;
+  // descriptors are built where they are used (from scalar bases and sizes), so they stay
+  // in scalar registers
+  unsigned char* const qo = static_cast<unsigned char*>(a.q_out) + tk.row * static_cast<int64_t>(a.H) * D * fmt_bytes<IO>();
+  unsigned char* const ko = static_cast<unsigned char*>(a.pool) + (kv_ok ? kdst * fmt_bytes<KV>() : 0);
+  unsigned char* const vo = ko + (kv_ok ? static_cast<int64_t>(a.T) * a.Hkv * D * fmt_bytes<KV>() : 0);
+  const int64_t qo_bytes = static_cast<int64_t>(g.nqc) * CB, kv_bytes = kv_ok ? static_cast<int64_t>(g.nkc) * KB : 0;
+  const int rowb = norm_row_bytes<IO>(D);
+  double2* stat = reinterpret_cast<double2*>(stage + norm_rows<IO, NORM>(D) * rowb);
+  const int poff_lane = lane + poff;
+  const int nq = g.nq, nqk = g.nqk, ntot = g.ntot;
+
+  if constexpr (NORM) {
+    // this batch's q/k rows into LDS, then one lane per row: (mean, 1/sqrt(var + eps)),
+    // fp64 sums in index order (as the oracle and pkv.h state)
+    const int nqk_b = min(NB, max(nqk - b0, 0));
+    wave_sync();                                  // earlier readers of the staging rows are done
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (u < nqk_b) {
+        unsigned char* dst = stage + (u * hpi + lane / cph) * rowb + c * CB;
+        *reinterpret_cast<uint4*>(dst) = r[u].a;
+        if constexpr (kRaw) *reinterpret_cast<uint4*>(dst + 16) = r[u].b;
+      }
+    }
+    wave_sync();
+    const bool layer = a.norm == kNormLayer;
+    for (int h = lane; h < nqk_b * hpi; h += kWave) {
+      const unsigned char* row = stage + h * rowb;
+      double s = 0.0;
+      if (layer) {
+        for (int q = 0; q < cph; ++q) {
+          Raw8 q8;
+          q8.a = *reinterpret_cast<const uint4*>(row + q * CB);
+          q8.b = kRaw ? *reinterpret_cast<const uint4*>(row + q * CB + 16) : make_uint4(0, 0, 0, 0);
+          double x[8];
+          widen8<IO>(q8, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += x[e];
+        }
+      }
+      const double mean = layer ? s / static_cast<double>(D) : 0.0;
+      double ss = 0.0;
+      for (int q = 0; q < cph; ++q) {
+        Raw8 q8;
+        q8.a = *reinterpret_cast<const uint4*>(row + q * CB);
+        q8.b = kRaw ? *reinterpret_cast<const uint4*>(row + q * CB + 16) : make_uint4(0, 0, 0, 0);
+        double x[8];
+        widen8<IO>(q8, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double d = x[e] - mean;
+          ss += d * d;
+        }
+      }
+      stat[h] = make_double2(mean, 1.0 / __builtin_sqrt(ss / static_cast<double>(D) + a.norm_eps));
+    }
+    wave_sync();
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int i = b0 + u;
+    const bool isq = i < nq, isk = i < nqk;
+    const int kind = isq ? 0 : isk ? 1 : 2;
+    const int ch = (isq ? i : isk ? i - nq : i - nqk) * kWave + lane;
+    const bool live = i < ntot;
+    if (kind == 2) {                                 // values: not rotated
+      const uint32_t off = live ? static_cast<uint32_t>(ch) * KB : kOff;
+      if constexpr (KV == IO) {
+        store8<KV>(rsrc(vo, kv_bytes), off, r[u]);
+      } else {
+        double x[8];
+        widen8<IO>(r[u], x);
+        store8<KV>(rsrc(vo, kv_bytes), off, pack8<KV>(x, a.inv_v_scale));
+      }
+      continue;
+    }
+    Raw8 pr = r[u];
+    if constexpr (RS == kRopeNeoxRow && !NORM) {
+      pr.a = row_ror8(r[u].a);
+    } else if constexpr (RS == kRopeNeox) {          // every lane takes part in the shuffle
+      pr.a = shfl16(r[u].a, poff_lane);
+      if constexpr (kRaw) pr.b = shfl16(r[u].b, poff_lane);
+    }
+    double x[8], y[8];
+    widen8<IO>(r[u], x);
+    if constexpr (NORM) {
+      const bool isq = kind == 0;
+      norm8(x, e0, stat[u * hpi + lane / cph], wts + (isq ? 0 : D), a.qn_b ? wts + (isq ? 2 : 3) * D : nullptr);
+    }
+    // every lane computes its rotation; the role then selects (no divergent branches)
+    if constexpr (RS == kRopeGptj) {                 // pairs (2k, 2k+1) inside the chunk
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double2 t = cs[k];
+        const double x1 = x[2 * k], x2 = x[2 * k + 1];
+        const double p = x1 * t.x, q = x2 * t.y, e = x2 * t.x, f = x1 * t.y;
+        const double y1 = p - q, y2 = e + f;
+        y[2 * k] = role == 3 ? y1 : x1;
+        y[2 * k + 1] = role == 3 ? y2 : x2;
+      }
+    } else if constexpr (neox<RS>()) {
+      double pv[8];
+      if constexpr (NORM && RS == kRopeNeoxRow) {
+        // the partner's normalised values over the row rotation (the same fp64 values
+        // its own lane computed)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint64_t bits = __builtin_bit_cast(uint64_t, x[k]);
+          const uint32_t lo = __builtin_amdgcn_mov_dpp(static_cast<int>(bits), 0x128, 0xF, 0xF, false);
+          const uint32_t hi = __builtin_amdgcn_mov_dpp(static_cast<int>(bits >> 32), 0x128, 0xF, 0xF, false);
+          pv[k] = __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+        }
+      } else {
+        widen8<IO>(pr, pv);
+        if constexpr (NORM) {
+          const bool isq = kind == 0;
+          norm8(pv, e0 + poff * 8, stat[u * hpi + lane / cph], wts + (isq ? 0 : D), a.qn_b ? wts + (isq ? 2 : 3) * D : nullptr);
+        }
+      }
+      const bool first = role == 1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const double2 t = cs[k];
+        // first half: y = x1*cos - x2*sin with x1 own; second half: y = x2*cos + x1*sin with
+        // x2 own (a - b and a + (-b) round alike)
+        const double own = x[k] * t.x, other = pv[k] * t.y;
+        const double sum = own + (first ? -other : other);
+        y[k] = RS == kRopeNeoxRow || role != 0 ? sum : x[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = x[k];
+    }
+    const bool skip = !live || (role != 0 && !rot_ok);
+    // dims past the rotary part keep their input bits when nothing changes them
+    const bool raw = !NORM && RS != kRopeNeoxRow && role == 0;
+    if (kind == 0) {
+      const uint32_t off = skip ? kOff : static_cast<uint32_t>(ch) * CB;
+      store8<IO>(rsrc(qo, qo_bytes), off, select8(raw, r[u], pack8<IO>(y, 1.0)));
+    } else {
+      const uint32_t off = skip ? kOff : static_cast<uint32_t>(ch) * KB;
+      if constexpr (KV == IO) store8<KV>(rsrc(ko, kv_bytes), off, select8(raw, r[u], pack8<KV>(y, a.inv_k_scale)));
+      else store8<KV>(rsrc(ko, kv_bytes), off, pack8<KV>(y, a.inv_k_scale));
+    }
+  }
+}
+
 // FLAT: the grid walks the packed rows, tokens_per_wg consecutive rows per workgroup,
 // and each workgroup finds the rows' requests through an LDS prefix scan of the
 // context lengths (batches of at most kFlatMaxRequests requests).  Otherwise the grid
-// is (row tile, request), for any batch size.
+// is (row tile, request), for any batch size.  Each wave then takes every fourth token
+// of the workgroup.
 template <int IO, int KV, int RS, bool FLAT, bool NORM>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, int tokens_per_wg) {
-  __shared__ int32_t s_cu[kFlatMaxRequests + 1];
+  extern __shared__ __align__(16) unsigned char smem[];
   __shared__ TokenSlot s_tok[kMaxTokensPerWg];
   const int Hq = a.q ? a.H : 0;
+  const int cu_bytes = FLAT ? ((a.B + 1) * 4 + 15) / 16 * 16 : 0;
   int ntok;
   if constexpr (FLAT) {
+    int32_t* s_cu = reinterpret_cast<int32_t*>(smem);
     const int64_t row0 = static_cast<int64_t>(blockIdx.x) * tokens_per_wg;
     if (row0 >= a.N) return;                               // uniform
     ntok = static_cast<int>(min<int64_t>(tokens_per_wg, a.N - row0));
@@ -380,7 +498,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
       const int32_t y = __shfl_up(incl, d, kWave);
       if (lane >= d) incl += y;
     }
-    __shared__ int32_t s_wave[kAppendThreads / kWave];
+    __shared__ int32_t s_wave[kAppendWaves];
     if (lane == kWave - 1) s_wave[wv] = incl;
     if (threadIdx.x == 0) s_cu[0] = 0;
     __syncthreads();
@@ -410,47 +528,56 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
     if (threadIdx.x < ntok)
       s_tok[threadIdx.x] = make_slot(a, rowr + tok0 + threadIdx.x, r, tok0 + threadIdx.x);
   }
-  __syncthreads();
-  // NORM: (mean, 1/sqrt(var + eps)) of every q and k head of the workgroup's tokens, one
-  // thread per (token, head), fp64 sums in index order (as the oracle and pkv.h state)
-  const double2* stat = nullptr;
+  // the norm's weights and biases in LDS: q weights, k weights, q biases, k biases
+  float* wts = reinterpret_cast<float*>(smem + cu_bytes);
   if constexpr (NORM) {
-    __shared__ double2 s_stat[kMaxTokensPerWg * kMaxNormHeads];
-    const int nh = Hq + a.Hkv;
-    const bool layer = a.norm == kNormLayer;
-    for (int u = threadIdx.x; u < ntok * nh; u += kAppendThreads) {
-      const int it = u / nh, head = u - it * nh;
-      const TokenSlot tk = s_tok[it];
-      double mean = 0.0, inv = 0.0;
-      if (tk.row < a.N && tk.m >= 0) {
-        const bool isq = head < Hq;
-        const void* src = isq ? a.q : a.k;
-        const int64_t off = isq ? tk.row * a.q_stride + static_cast<int64_t>(head) * a.D
-                                : tk.row * a.kv_stride + static_cast<int64_t>(head - Hq) * a.D;
-        if (a.D == 128) row_stats<IO, 128>(src, off, layer, a.norm_eps, mean, inv);
-        else row_stats<IO, 64>(src, off, layer, a.norm_eps, mean, inv);
-      }
-      s_stat[u] = make_double2(mean, inv);
+    for (int d = threadIdx.x; d < a.D; d += kAppendThreads) {
+      wts[d] = a.qn_w ? a.qn_w[d] : 0.f;
+      wts[a.D + d] = a.kn_w[d];
+      wts[2 * a.D + d] = a.qn_b ? a.qn_b[d] : 0.f;
+      wts[3 * a.D + d] = a.kn_b ? a.kn_b[d] : 0.f;
     }
-    __syncthreads();
-    stat = s_stat;
   }
-  const int R = RS != kRopeNone ? a.R : 0;
-  const int per_tok = ((Hq + a.Hkv + kHeadsPerRotTask - 1) / kHeadsPerRotTask) * (R / 16) +
-                      (Hq + a.Hkv) * ((a.D - R) / 8) + a.Hkv * (a.D / 8);
-  const int total = ntok * per_tok;
-  const void* __restrict__ q = a.q;
-  const void* __restrict__ k = a.k;
-  const void* __restrict__ v = a.v;
-  const double* __restrict__ cs = a.cos_sin;
-  void* __restrict__ q_out = a.q_out;
-  void* __restrict__ pool = a.pool;
-  for (int task = threadIdx.x; task < total; task += kAppendThreads) {
-    const int it = task / per_tok;
-    const TokenSlot tk = s_tok[it];
-    if (tk.row >= a.N || tk.m < 0) continue;
-    append_task<IO, KV, RS, NORM>(a, tk, task - it * per_tok, Hq, q, k, v, cs, q_out, pool,
-                                  NORM ? stat + it * (Hq + a.Hkv) : nullptr);
+  __syncthreads();
+  // the wave index is the same in every lane; saying so keeps the token walk scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  unsigned char* stage = smem + cu_bytes + (NORM ? 16 * a.D : 0) + wave * norm_wave_bytes<IO, NORM>(a.D);
+  // The workgroup's (token, batch) items, token-major; wave w takes items w, w + 4, ...
+  // The table and the loads of a wave's next item are issued before the arithmetic of
+  // its current one.
+  constexpr int NB = append_batch<IO, NORM>();
+  const RowGeom g(a, Hq);
+  const int nb = (g.ntot + NB - 1) / NB;
+  const int nitems = ntok * nb;
+  const Role rl = chunk_role<RS>((lane % g.cph) * 8, RS != kRopeNone ? a.R : 0);
+  auto next_item = [&](int j) {
+    while (j < nitems) {
+      const TokenSlot tk = uniform_slot(s_tok[j / nb]);
+      if (tk.row < a.N && tk.m >= 0) break;
+      j += kAppendWaves;
+    }
+    return j;
+  };
+  int j = next_item(wave);
+  if (j >= nitems) return;
+  Raw8 cur[NB];
+  append_load<IO, NB>(a, g, uniform_slot(s_tok[j / nb]), lane, (j % nb) * NB, true, cur);
+  for (;;) {
+    const int jn = next_item(j + kAppendWaves);
+    const bool more = jn < nitems;
+    const TokenSlot tk = uniform_slot(s_tok[j / nb]);
+    double2 cs[8];
+    load_table<RS>(a, tk, rl, cs);
+    Raw8 nxt[NB];
+    // issued on every pass (all lanes out of range on the last) so that the loads and
+    // stores of an item do not depend on a branch
+    const int jl = more ? jn : j;
+    append_load<IO, NB>(a, g, uniform_slot(s_tok[jl / nb]), lane, (jl % nb) * NB, more, nxt);
+    append_compute<IO, KV, RS, NORM, NB>(a, g, tk, rl, cs, lane, (j % nb) * NB, cur, stage, wts);
+    if (!more) break;
+    j = jn;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) cur[u] = nxt[u];
   }
 }
 
@@ -471,25 +598,32 @@ __global__ void rope_table_kernel(double base, int R, int max_pos, double* __res
 
 template <int IO, int KV>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
-  // enough workgroups to fill the chip: about N / 512 tokens each, at most 8
-  int64_t want = a.N / 512;
-  const int tpw = static_cast<int>(want < 1 ? 1 : want > kMaxTokensPerWg ? kMaxTokensPerWg : want);
   auto go2 = [&](auto rs, auto nrm) {
     constexpr int RS = decltype(rs)::value;
     constexpr bool NORM = decltype(nrm)::value;
-    if (a.B <= kFlatMaxRequests) {
+    // items of a token (batches of NB chunk instructions), as the kernel counts them
+    const int64_t cph = a.D / 8, Hq = a.q ? a.H : 0;
+    const int64_t ntot = (Hq * cph + kWave - 1) / kWave + 2 * ((a.Hkv * cph + kWave - 1) / kWave);
+    const int64_t nb = (ntot + append_batch<IO, NORM>() - 1) / append_batch<IO, NORM>();
+    // about kAppendWGs workgroups: items per wave, then whole tokens per workgroup
+    const int64_t ipw = (a.N * nb + kAppendWGs * kAppendWaves - 1) / (kAppendWGs * kAppendWaves);
+    const int tpw = static_cast<int>(std::min<int64_t>(kMaxTokensPerWg, std::max<int64_t>(1, (ipw * kAppendWaves + nb - 1) / nb)));
+    const size_t stage = (NORM ? 16 * static_cast<size_t>(a.D) : 0) + static_cast<size_t>(kAppendWaves) * norm_wave_bytes<IO, NORM>(a.D);
+    const size_t lds = (static_cast<size_t>(a.B + 1) * 4 + 15) / 16 * 16 + stage;
+    if (a.B <= kFlatMaxRequests && lds <= kMaxDynamicLds) {
       const dim3 grid(static_cast<unsigned>((a.N + tpw - 1) / tpw));
-      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true, NORM>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true, NORM>), grid, dim3(kAppendThreads), lds, s, a, tpw);
     } else {
       const dim3 grid((a.max_n + tpw - 1) / tpw, a.B);
-      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false, NORM>), grid, dim3(kAppendThreads), 0, s, a, tpw);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false, NORM>), grid, dim3(kAppendThreads), stage, s, a, tpw);
     }
   };
   auto go = [&](auto rs) {
     if (a.norm != kNormNone) go2(rs, std::true_type());
     else go2(rs, std::false_type());
   };
-  if (a.rope == kRopeNeox) go(std::integral_constant<int, kRopeNeox>());
+  if (a.rope == kRopeNeox && IO == F_BF16 && a.D == 128 && a.R == 128) go(std::integral_constant<int, kRopeNeoxRow>());
+  else if (a.rope == kRopeNeox) go(std::integral_constant<int, kRopeNeox>());
   else if (a.rope == kRopeGptj) go(std::integral_constant<int, kRopeGptj>());
   else go(std::integral_constant<int, kRopeNone>());
   return hipGetLastError();
