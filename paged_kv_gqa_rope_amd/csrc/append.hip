@@ -82,23 +82,17 @@ __device__ __forceinline__ void widen8(const Raw8& r, double (&x)[8]) {
 }
 
 // Per-head normalisation of 8 elements at dims dim0 .. dim0+7 of one q or k head:
-// y = ((x - mean) * inv) * w (+ b), fp64, with (mean, inv) of the head from the pre-pass.
-__device__ __forceinline__ void norm8(double (&x)[8], int dim0, double2 st, const float* __restrict__ w,
-                                      const float* __restrict__ b) {
+// y = ((x - mean) * inv) * w (+ b), fp64, with (mean, inv) of the head.  The RMS form has
+// mean 0 and no bias (x - 0 is x, so the subtraction is left out).  w and b are the
+// weights and biases widened to fp64 (exactly) in LDS.
+template <bool LAYER>
+__device__ __forceinline__ void norm8(double (&x)[8], int dim0, double2 st, const double* w, const double* b) {
 #pragma clang fp contract(off)
-  const float4 w0 = *reinterpret_cast<const float4*>(w + dim0), w1 = *reinterpret_cast<const float4*>(w + dim0 + 4);
-  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (b) {
-    const float4 b0 = *reinterpret_cast<const float4*>(b + dim0), b1 = *reinterpret_cast<const float4*>(b + dim0 + 4);
-    bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
-    bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
-  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const double d = x[i] - st.x;
-    const double y = (d * st.y) * static_cast<double>(wv[i]);
-    x[i] = b ? y + static_cast<double>(bv[i]) : y;
+    const double d = LAYER ? x[i] - st.x : x[i];
+    const double y = (d * st.y) * w[dim0 + i];
+    x[i] = LAYER ? y + b[dim0 + i] : y;
   }
 }
 
@@ -292,7 +286,11 @@ __device__ __forceinline__ void load_table(const AppendArgs& a, const TokenSlot&
     const double2* t = reinterpret_cast<const double2*>(a.cos_sin) +
                        (rl.role != 0 && tk.m < a.max_pos ? static_cast<int64_t>(tk.m) * (a.R / 2) + rl.jt : 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) cs[k] = t[RS == kRopeGptj ? k % 4 : k];
+    for (int k = 0; k < 8; ++k) {
+      cs[k] = t[RS == kRopeGptj ? k % 4 : k];
+      // rotate-half first half: y = x1*cos + x2*(-sin), which rounds as x1*cos - x2*sin
+      if (rl.role == 1) cs[k].y = -cs[k].y;
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) cs[k] = make_double2(0.0, 0.0);
@@ -303,12 +301,13 @@ __device__ __forceinline__ void load_table(const AppendArgs& a, const TokenSlot&
 // lane's chunk (dims e0 .. e0+7): rotate-half first half (partner R/16 lanes up), second
 // half (partner R/16 lanes down), interleaved (pairs inside the chunk), or none (dims
 // past the rotary part).
-template <int IO, int KV, int RS, bool NORM, int NB>
+template <int IO, int KV, int RS, int NK, int NB>
 __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeom& g, const TokenSlot& tk,
                                                const Role& rl, const double2 (&cs)[8], int lane, int b0,
                                                const Raw8 (&r)[NB], unsigned char* __restrict__ stage,
-                                               const float* __restrict__ wts) {
+                                               const double* __restrict__ wts) {
 #pragma clang fp contract(off)
+  constexpr bool NORM = NK != kNormNone, LAYER = NK == kNormLayer;
   constexpr int kRaw = IO == F_BF16 ? 0 : 1;     // fp32 chunks are two 16-byte halves
   constexpr int CB = 8 * fmt_bytes<IO>(), KB = 8 * fmt_bytes<KV>();
   const int D = a.D;
@@ -344,7 +343,7 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
       }
     }
     wave_sync();
-    const bool layer = a.norm == kNormLayer;
+    constexpr bool layer = LAYER;
     for (int h = lane; h < nqk_b * hpi; h += kWave) {
       const unsigned char* row = stage + h * rowb;
       double s = 0.0;
@@ -406,7 +405,7 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
     widen8<IO>(r[u], x);
     if constexpr (NORM) {
       const bool isq = kind == 0;
-      norm8(x, e0, stat[u * hpi + lane / cph], wts + (isq ? 0 : D), a.qn_b ? wts + (isq ? 2 : 3) * D : nullptr);
+      norm8<LAYER>(x, e0, stat[u * hpi + lane / cph], wts + (isq ? 0 : D), wts + (isq ? 2 : 3) * D);
     }
     // every lane computes its rotation; the role then selects (no divergent branches)
     if constexpr (RS == kRopeGptj) {                 // pairs (2k, 2k+1) inside the chunk
@@ -435,17 +434,16 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
         widen8<IO>(pr, pv);
         if constexpr (NORM) {
           const bool isq = kind == 0;
-          norm8(pv, e0 + poff * 8, stat[u * hpi + lane / cph], wts + (isq ? 0 : D), a.qn_b ? wts + (isq ? 2 : 3) * D : nullptr);
+          norm8<LAYER>(pv, e0 + poff * 8, stat[u * hpi + lane / cph], wts + (isq ? 0 : D), wts + (isq ? 2 : 3) * D);
         }
       }
-      const bool first = role == 1;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const double2 t = cs[k];
-        // first half: y = x1*cos - x2*sin with x1 own; second half: y = x2*cos + x1*sin with
-        // x2 own (a - b and a + (-b) round alike)
+        // first half: y = x1*cos - x2*sin with x1 own (the sine arrives negated: a + (-b)
+        // rounds as a - b); second half: y = x2*cos + x1*sin with x2 own
         const double own = x[k] * t.x, other = pv[k] * t.y;
-        const double sum = own + (first ? -other : other);
+        const double sum = own + other;
         y[k] = RS == kRopeNeoxRow || role != 0 ? sum : x[k];
       }
     } else {
@@ -471,8 +469,9 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
 // context lengths (batches of at most kFlatMaxRequests requests).  Otherwise the grid
 // is (row tile, request), for any batch size.  Each wave then takes every fourth token
 // of the workgroup.
-template <int IO, int KV, int RS, bool FLAT, bool NORM>
+template <int IO, int KV, int RS, bool FLAT, int NK>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, int tokens_per_wg) {
+  constexpr bool NORM = NK != kNormNone;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ TokenSlot s_tok[kMaxTokensPerWg];
   const int Hq = a.q ? a.H : 0;
@@ -528,20 +527,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
     if (threadIdx.x < ntok)
       s_tok[threadIdx.x] = make_slot(a, rowr + tok0 + threadIdx.x, r, tok0 + threadIdx.x);
   }
-  // the norm's weights and biases in LDS: q weights, k weights, q biases, k biases
-  float* wts = reinterpret_cast<float*>(smem + cu_bytes);
+  // the norm's weights and biases in LDS, widened to fp64: q weights, k weights, q
+  // biases, k biases
+  double* wts = reinterpret_cast<double*>(smem + cu_bytes);
   if constexpr (NORM) {
     for (int d = threadIdx.x; d < a.D; d += kAppendThreads) {
-      wts[d] = a.qn_w ? a.qn_w[d] : 0.f;
-      wts[a.D + d] = a.kn_w[d];
-      wts[2 * a.D + d] = a.qn_b ? a.qn_b[d] : 0.f;
-      wts[3 * a.D + d] = a.kn_b ? a.kn_b[d] : 0.f;
+      wts[d] = a.qn_w ? static_cast<double>(a.qn_w[d]) : 0.0;
+      wts[a.D + d] = static_cast<double>(a.kn_w[d]);
+      wts[2 * a.D + d] = a.qn_b ? static_cast<double>(a.qn_b[d]) : 0.0;
+      wts[3 * a.D + d] = a.kn_b ? static_cast<double>(a.kn_b[d]) : 0.0;
     }
   }
   __syncthreads();
   // the wave index is the same in every lane; saying so keeps the token walk scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  unsigned char* stage = smem + cu_bytes + (NORM ? 16 * a.D : 0) + wave * norm_wave_bytes<IO, NORM>(a.D);
+  unsigned char* stage = smem + cu_bytes + (NORM ? 32 * a.D : 0) + wave * norm_wave_bytes<IO, NORM>(a.D);
   // The workgroup's (token, batch) items, token-major; wave w takes items w, w + 4, ...
   // The table and the loads of a wave's next item are issued before the arithmetic of
   // its current one.
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, in
     // stores of an item do not depend on a branch
     const int jl = more ? jn : j;
     append_load<IO, NB>(a, g, uniform_slot(s_tok[jl / nb]), lane, (jl % nb) * NB, more, nxt);
-    append_compute<IO, KV, RS, NORM, NB>(a, g, tk, rl, cs, lane, (j % nb) * NB, cur, stage, wts);
+    append_compute<IO, KV, RS, NK, NB>(a, g, tk, rl, cs, lane, (j % nb) * NB, cur, stage, wts);
     if (!more) break;
     j = jn;
 #pragma unroll
@@ -600,7 +600,8 @@ template <int IO, int KV>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
   auto go2 = [&](auto rs, auto nrm) {
     constexpr int RS = decltype(rs)::value;
-    constexpr bool NORM = decltype(nrm)::value;
+    constexpr int NK = decltype(nrm)::value;
+    constexpr bool NORM = NK != kNormNone;
     // items of a token (batches of NB chunk instructions), as the kernel counts them
     const int64_t cph = a.D / 8, Hq = a.q ? a.H : 0;
     const int64_t ntot = (Hq * cph + kWave - 1) / kWave + 2 * ((a.Hkv * cph + kWave - 1) / kWave);
@@ -608,19 +609,20 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
     // about kAppendWGs workgroups: items per wave, then whole tokens per workgroup
     const int64_t ipw = (a.N * nb + kAppendWGs * kAppendWaves - 1) / (kAppendWGs * kAppendWaves);
     const int tpw = static_cast<int>(std::min<int64_t>(kMaxTokensPerWg, std::max<int64_t>(1, (ipw * kAppendWaves + nb - 1) / nb)));
-    const size_t stage = (NORM ? 16 * static_cast<size_t>(a.D) : 0) + static_cast<size_t>(kAppendWaves) * norm_wave_bytes<IO, NORM>(a.D);
+    const size_t stage = (NORM ? 32 * static_cast<size_t>(a.D) : 0) + static_cast<size_t>(kAppendWaves) * norm_wave_bytes<IO, NORM>(a.D);
     const size_t lds = (static_cast<size_t>(a.B + 1) * 4 + 15) / 16 * 16 + stage;
     if (a.B <= kFlatMaxRequests && lds <= kMaxDynamicLds) {
       const dim3 grid(static_cast<unsigned>((a.N + tpw - 1) / tpw));
-      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true, NORM>), grid, dim3(kAppendThreads), lds, s, a, tpw);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, true, NK>), grid, dim3(kAppendThreads), lds, s, a, tpw);
     } else {
       const dim3 grid((a.max_n + tpw - 1) / tpw, a.B);
-      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false, NORM>), grid, dim3(kAppendThreads), stage, s, a, tpw);
+      hipLaunchKernelGGL((append_kernel<IO, KV, RS, false, NK>), grid, dim3(kAppendThreads), stage, s, a, tpw);
     }
   };
   auto go = [&](auto rs) {
-    if (a.norm != kNormNone) go2(rs, std::true_type());
-    else go2(rs, std::false_type());
+    if (a.norm == kNormRms) go2(rs, std::integral_constant<int, kNormRms>());
+    else if (a.norm == kNormLayer) go2(rs, std::integral_constant<int, kNormLayer>());
+    else go2(rs, std::integral_constant<int, kNormNone>());
   };
   if (a.rope == kRopeNeox && IO == F_BF16 && a.D == 128 && a.R == 128) go(std::integral_constant<int, kRopeNeoxRow>());
   else if (a.rope == kRopeNeox) go(std::integral_constant<int, kRopeNeox>());
