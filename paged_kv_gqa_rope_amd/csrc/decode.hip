@@ -743,32 +743,62 @@ __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per
   const float2* op = reinterpret_cast<const float2*>(a.ws_o + e0 * kD) + lane;
   const int64_t ps = stride * (kD / 2);                             // float2 steps between pieces
   const float* mlp = a.ws_ml + e0 * 2;
-  float M = -INFINITY;
-  for (int pb = 0; pb < np; pb += kWave) {
-    const int p = pb + lane;
-    M = fmaxf(M, wave_max(p < np ? mlp[p * stride * 2] : -INFINITY));
-  }
   float L = 0.f, ox = 0.f, oy = 0.f;
-  for (int pb = 0; pb < np; pb += kWave) {
-    const int p = pb + lane;
-    float wt = 0.f, lp = 0.f;
-    if (p < np) {
-      const float2 mlv = *reinterpret_cast<const float2*>(mlp + p * stride * 2);
-      wt = mlv.x == -INFINITY ? 0.f : exp2f(mlv.x - M);
-      lp = mlv.y;
+  if (np <= kWave) {
+    // One memory round trip: every lane loads one piece's (m, l) while the first kPre
+    // pieces' o are loaded (issued after the (m, l) loads, so waiting for those does not
+    // wait for these); the weights follow from the maximum.
+    constexpr int kPre = 8;
+    const float2 mlv = *reinterpret_cast<const float2*>(mlp + min(lane, np - 1) * stride * 2);
+    float2 u0[kPre];
+#pragma unroll
+    for (int e = 0; e < kPre; ++e) u0[e] = op[min(e, np - 1) * ps];   // weight 0 past the last piece
+    const float M = wave_max(lane < np ? mlv.x : -INFINITY);
+    const float wt = lane < np && mlv.x != -INFINITY ? exp2f(mlv.x - M) : 0.f;
+    L = wave_sum(wt * (lane < np ? mlv.y : 0.f));
+#pragma unroll
+    for (int e = 0; e < kPre; ++e) {
+      const float w = __shfl(wt, e, kWave);
+      ox += w * u0[e].x;
+      oy += w * u0[e].y;
     }
-    L += wave_sum(wt * lp);
-    const int cnt = min(kWave, np - pb);
-    int k = 0;
-    for (; k < cnt; k += 8) {                                      // eight loads in flight
+    for (int k = kPre; k < np; k += 8) {                           // eight loads in flight
       float2 u[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = k + e < cnt ? op[(pb + k + e) * ps] : make_float2(0.f, 0.f);
+      for (int e = 0; e < 8; ++e) u[e] = op[min(k + e, np - 1) * ps];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float w = __shfl(wt, k + e, kWave);                  // u[e] = 0 past the last piece
+        const float w = __shfl(wt, k + e, kWave);                  // 0 past the last piece
         ox += w * u[e].x;
         oy += w * u[e].y;
+      }
+    }
+  } else {
+    float M = -INFINITY;
+    for (int pb = 0; pb < np; pb += kWave) {
+      const int p = pb + lane;
+      M = fmaxf(M, wave_max(p < np ? mlp[p * stride * 2] : -INFINITY));
+    }
+    for (int pb = 0; pb < np; pb += kWave) {
+      const int p = pb + lane;
+      float wt = 0.f, lp = 0.f;
+      if (p < np) {
+        const float2 v = *reinterpret_cast<const float2*>(mlp + p * stride * 2);
+        wt = v.x == -INFINITY ? 0.f : exp2f(v.x - M);
+        lp = v.y;
+      }
+      L += wave_sum(wt * lp);
+      const int cnt = min(kWave, np - pb);
+      for (int k = 0; k < cnt; k += 8) {                           // eight loads in flight
+        float2 u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = k + e < cnt ? op[(pb + k + e) * ps] : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float w = __shfl(wt, k + e, kWave);                // u[e] = 0 past the last piece
+          ox += w * u[e].x;
+          oy += w * u[e].y;
+        }
       }
     }
   }

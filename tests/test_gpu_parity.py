@@ -122,6 +122,46 @@ def test_qk_norm_append_and_attention(H, case_i):
     print(b.label, kind, style, rot, stats)
 
 
+class _SpanBatch(W.Batch):
+    """Queries and new keys with heads whose squares span many binades, where the
+    index-order sums round differently from other orders: on even tokens every fourth
+    head holds one value 2^24 times smaller than the rest (or a subnormal); on odd tokens
+    heads are all zero, hold one nonzero value, or are drawn as usual."""
+
+    def _draw(self, tag, r, rows, heads):
+        x = super()._draw(tag, r, rows, heads)
+        if tag not in ("q", "k"):
+            return x
+        f = (x.astype(np.uint32) << 16).view(np.float32).copy()
+        for t in range(rows):
+            for h in range(heads):
+                if t % 2 == 0 and h % 4 == 0:
+                    f[t, h, (t + h) % f.shape[2]] *= np.float32(2.0 ** -24)
+                elif t % 2 == 0 and h % 4 == 1:
+                    f[t, h, 3] = np.float32(2.0 ** -130)          # a bf16 subnormal
+                elif t % 2 == 1 and h % 4 == 0:
+                    f[t, h, :] = 0
+                elif t % 2 == 1 and h % 4 == 1:
+                    f[t, h, :] = 0
+                    f[t, h, h % f.shape[2]] = np.float32(-3.0)
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_qk_norm_wide_binade_spans(H, kind):
+    """The norm statistics follow the index-order sums bit for bit on heads where the
+    order matters (tiny and subnormal values among large ones, zero heads)."""
+    sh = dataclasses.replace(W.SHAPES[3], qk_norm=kind, norm_eps=1e-5)
+    b0 = W.small_workload(3, shape=sh)
+    b = _SpanBatch(**{f.name: getattr(b0, f.name) for f in dataclasses.fields(W.Batch)})
+    case("qk norm spans", kind, b.label)
+    st = run_step(H, b)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(sh.kv_dtype)), "pool")
+
+
 FP8_OUT_CASES = [
     # (workload shape, output scale, no saturation): scales that fit the outputs (decode
     # outputs stay below ~0.2, early prompt rows reach ~4); mostly subnormal codes; a scale
