@@ -129,10 +129,26 @@ def _timed_pass(L, st, steps: int, level: int) -> dict:
     return {n: dict(avg_us=1e3 * sum(v) / len(v), launches=len(v)) for n, v in per.items()}
 
 
+def _step_ms(st, steps: int) -> float:
+    """Average ms of K steps, one event pair around all of them (library timing off)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    beg, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    beg.record(stream)
+    for _ in range(steps):
+        st.step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return beg.elapsed_time(end) / steps
+
+
 def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:
     """Warm-up, then K timed steps with the library's timing off (ms_per_step), then K
     steps with an event pair around every launch (per-kernel durations) and K with one
-    around every phase (the decode span: split pass and combine with nothing between)."""
+    around every phase (the decode span: split pass and combine with nothing between).
+    A mixed batch runs by default as one launch for its context and split-pass parts; its
+    per-kernel durations (for the rooflines) come from the same passes repeated with the
+    two parts launched one after the other, and `coscheduled` keeps the one-launch figures."""
     import torch
 
     from paged_kv_gqa_rope_amd import _lib as L
@@ -148,20 +164,28 @@ def run_workload(k: int, steps: int, warmup: int, batch=None) -> dict:
     for _ in range(warmup):
         st.step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    beg, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    beg.record(stream)
-    for _ in range(steps):
-        st.step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = beg.elapsed_time(end) / steps
+    ms_per_step = _step_ms(st, steps)
     kern = _timed_pass(L, st, steps, 1)
     phases = _timed_pass(L, st, steps, 2)
+    co = None
+    if "mixed" in kern:
+        co = dict(ms_per_step=ms_per_step, kernels=kern, phases=phases)
+        old = L.pkv_set_coschedule(0)
+        try:
+            for _ in range(warmup):
+                st.step()
+            ms_serial = _step_ms(st, steps)
+            kern = _timed_pass(L, st, steps, 1)
+            phases = _timed_pass(L, st, steps, 2)
+        finally:
+            L.pkv_set_coschedule(old)
+        co["ms_per_step_serial"] = ms_serial
     w = algorithmic(batch)
     step_bytes = w["append_bytes"] + w["decode_bytes"]
     res = dict(workload=describe(batch), setup_s=round(setup_s, 2), ms_per_step=ms_per_step,
                tok_per_s=w["tokens"] / (ms_per_step * 1e-3), kernels=kern, phases=phases, work=w)
+    if co is not None:
+        res["coscheduled"] = co
     if "decode_split" in kern:
         span = decode_us(res) * 1e-6
         res["decode_GBps"] = w["decode_bytes"] / span / 1e9
@@ -364,6 +388,12 @@ def main() -> int:
         print(f"[bench] workload {k}: {results[k]['ms_per_step']:.3f} ms/step "
               f"{ {n: round(v['avg_us'], 1) for n, v in results[k]['kernels'].items()} } phases "
               f"{ {n: round(v['avg_us'], 1) for n, v in results[k]['phases'].items()} }", file=sys.stderr, flush=True)
+        co = results[k].get("coscheduled")
+        if co:
+            print(f"[bench] workload {k} one launch for context + split pass: {co['ms_per_step']:.3f} ms/step "
+                  f"(serial {co['ms_per_step_serial']:.3f}) "
+                  f"{ {n: round(v['avg_us'], 1) for n, v in co['kernels'].items()} } phases "
+                  f"{ {n: round(v['avg_us'], 1) for n, v in co['phases'].items()} }", file=sys.stderr, flush=True)
     head_k = HEADLINE if HEADLINE in results else ks[0]
     head = results[head_k]
     line = {
@@ -400,6 +430,13 @@ def main() -> int:
         if "prefill_TFLOPs" in r:
             o["prefill_pct_bf16_peak"] = 100 * r["prefill_TFLOPs"] / BF16_DENSE_PEAK_TFLOPS
         o["roofline"] = roofline_for(r, k)
+        co = r.get("coscheduled")
+        if co:
+            # the step above is one launch for the context and split-pass parts; the
+            # per-kernel figures and rooflines come from the same batch launched serially
+            o["ms_per_step_serial"] = co["ms_per_step_serial"]
+            o["coscheduled_us"] = {n: round(v["avg_us"], 2) for n, v in co["kernels"].items()}
+            o["coscheduled_phases_us"] = {n: round(v["avg_us"], 2) for n, v in co["phases"].items()}
         others[f"workload_{k}"] = o
     line["workloads"] = others
     variants = {}

@@ -339,6 +339,20 @@ int32_t pkv_kernel_timings(const char** names, float* milliseconds, int32_t max_
  */
 int32_t pkv_set_decode_workgroups(int32_t n);
 
+/*
+ * Mixed batches (context and generation requests in one call; "TensorRT-LLM source
+ * analysis report", 1.3, mixed-phase processing): by default, when both parts take the
+ * fast kernels (at most 256 context requests, generation requests of one token over KV
+ * heads in fours, tokens_per_block >= 16), one launch runs the context attention on some
+ * compute units and the generation split pass on the others, sized by estimated time;
+ * the combine follows.  With the decode workgroup cap above set (n > 0), the split pass
+ * gets that many workgroups (one per compute unit) and the context part the rest.
+ * on = 0 runs the two parts one after the other, on = 1 restores the default, on < 0 only
+ * queries.  Returns the setting in force before the call (process-wide).  Results stay
+ * within the documented accuracy either way.
+ */
+int32_t pkv_set_coschedule(int32_t on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -118,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_kernel_timing_enable.restype = i32
         L.pkv_set_decode_workgroups.argtypes = [i32]
         L.pkv_set_decode_workgroups.restype = i32
+        L.pkv_set_coschedule.argtypes = [i32]
+        L.pkv_set_coschedule.restype = i32
         L.pkv_kernel_timings.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i32]
         L.pkv_kernel_timings.restype = i32
         _lib = L
@@ -183,6 +185,12 @@ def pkv_attention_forward_noalloc(desc, batch, q, q_row_stride, kv_pool, out, st
 def pkv_set_decode_workgroups(n: int) -> int:
     """Cap the decode split pass's workgroups at n (0: default, < 0: query); returns the old cap."""
     return lib().pkv_set_decode_workgroups(int(n))
+
+
+def pkv_set_coschedule(on: int) -> int:
+    """Mixed batches in one launch (1, default) or context then generation (0); < 0 queries.
+    Returns the previous setting."""
+    return lib().pkv_set_coschedule(int(on))
 
 
 def pkv_kernel_timing_enable(on) -> int:

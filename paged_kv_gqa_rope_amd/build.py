@@ -30,6 +30,7 @@ PER_FILE = {
     "append.hip": ["-ffp-contract=off"],
     # scores are finite or -inf, never NaN: max needs no NaN canonicalisation
     "prefill.hip": ["-fno-honor-nans"],
+    "mixed.hip": ["-fno-honor-nans"],
 }
 
 

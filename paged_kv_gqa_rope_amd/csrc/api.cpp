@@ -56,6 +56,12 @@ hipError_t device_info(DeviceInfo* out) {
 // not timed (pkv_kernel_timings reports how many were dropped through pkv_last_error).
 // Cap on the decode split pass's workgroups (0: the default, kDecodeWGsPerCU per CU).
 std::atomic<int32_t> g_decode_wgs{0};
+// Mixed batches: context and generation parts in one launch (1) or one after the other (0).
+std::atomic<int32_t> g_cosched{1};
+// Per-CU rates that size the two parts of a mixed launch: the context kernel's matrix
+// throughput and the split pass's streaming rate on a CU when few CUs stream.
+constexpr double kCtxFlopsPerCU = 3.6e12;
+constexpr double kGenBytesPerCU = 40e9;
 
 constexpr size_t kTimingEvents = 8192;
 struct TimingRec {
@@ -334,11 +340,72 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
   a.num_cus = dev.cus;
+  // generation part's arguments (the context part's are set below)
+  pkv::AttnArgs ad = a;
+  if (plan.num_gen > 0) {
+    ad.req_begin = plan.num_ctx;
+    ad.req_end = plan.B;
+    ad.row_begin = plan.ctx_tokens;
+    ad.max_n = plan.max_gen_n;
+    ad.col_blocks = plan.col_blocks;
+    if (plan.fast_decode) {
+      ad.dec_heads = plan.dec_heads;
+      ad.dec_cbw = plan.dec_cbw;
+      ad.dec_allcols = plan.dec_allcols ? 1 : 0;
+      ad.dec_cols = plan.dec_cols;
+      ad.dec_lanes = plan.dec_lanes;
+      ad.dec_lane_cbs = plan.dec_lane_cbs;
+      ad.ws_pre = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan.ws_pre_off);
+      ad.ws_row = ad.ws_pre + (plan.num_gen + 1);
+      ad.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_off);
+      ad.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_off);
+    }
+  }
+  // ranges of tiles of the split pass, each on one workgroup per lane, for a target count
+  auto set_ranges = [&](int64_t target) {
+    const int64_t lanes = std::max(plan.dec_lanes, 1);
+    const int64_t ranges = std::max<int64_t>(1, std::min(target, plan.dec_max_wgs) / lanes);
+    ad.dec_wgs = static_cast<int32_t>(ranges * lanes);
+  };
+  const int32_t cap = g_decode_wgs.load(std::memory_order_relaxed);
+  a.req_begin = 0;
+  a.req_end = plan.num_ctx;
+  a.row_begin = 0;
+  a.max_n = plan.max_ctx_n;
+  const int G = H / desc->num_kv_heads;
+  const bool mixed = g_cosched.load(std::memory_order_relaxed) != 0 && plan.num_ctx > 0 && plan.num_gen > 0 &&
+                     plan.fast_prefill && plan.fast_decode && dev.cus >= 16 && pkv::mixed_supported(ad, plan.num_ctx, G);
+  if (mixed) {
+    // CUs for the generation part in proportion to its estimated time: context flops at
+    // the context kernel's per-CU rate against generation bytes at a per-CU streaming rate
+    double flops = 0.0, bytes = 0.0;
+    for (int32_t r = 0; r < plan.B; ++r) {
+      const double n = batch->host_context_lengths[r], S = batch->host_sequence_lengths[r];
+      if (r < plan.num_ctx) flops += 4.0 * H * D * (n * (S - n) + n * (n + 1) / 2);
+      else bytes += 2.0 * S * desc->num_kv_heads * D * (desc->kv_dtype == PKV_FP32 ? 4 : desc->kv_dtype == PKV_BF16 ? 2 : 1);
+    }
+    const double tc = flops / kCtxFlopsPerCU, tg = bytes / kGenBytesPerCU;
+    int64_t gen_cus = cap > 0 ? cap : static_cast<int64_t>(std::llround(dev.cus * tg / std::max(tc + tg, 1e-30)));
+    gen_cus = std::min<int64_t>(std::max<int64_t>(gen_cus / 8 * 8, 8), dev.cus - 8);
+    set_ranges(gen_cus);
+    const int ctx_wgs = std::max(8, (dev.cus - ad.dec_wgs) / 8 * 8);
+    const char* failed = nullptr;
+    e = timed_at(kPhase, "mixed", s, [&] {
+      hipError_t le = timed_at(kLaunch, "mixed", s, [&] {
+        return pkv::launch_mixed(a, batch->host_context_lengths, batch->host_sequence_lengths, ad, ctx_wgs, s);
+      });
+      if (le != hipSuccess) {
+        failed = "mixed launch";
+        return le;
+      }
+      le = timed_at(kLaunch, "decode_combine", s, [&] { return pkv::launch_decode_combine(ad, s); });
+      if (le != hipSuccess) failed = "decode combine launch";
+      return le;
+    });
+    if (e != hipSuccess) return hip_fail(e, failed ? failed : "mixed launch");
+    return PKV_OK;
+  }
   if (plan.num_ctx > 0) {
-    a.req_begin = 0;
-    a.req_end = plan.num_ctx;
-    a.row_begin = 0;
-    a.max_n = plan.max_ctx_n;
     if (plan.fast_prefill)
       e = timed("prefill_mfma", s, [&] { return pkv::launch_prefill(a, batch->host_context_lengths, batch->host_sequence_lengths, s); });
     else
@@ -346,42 +413,22 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
     if (e != hipSuccess) return hip_fail(e, "context attention launch");
   }
   if (plan.num_gen > 0) {
-    a.req_begin = plan.num_ctx;
-    a.req_end = plan.B;
-    a.row_begin = plan.ctx_tokens;
-    a.max_n = plan.max_gen_n;
-    a.col_blocks = plan.col_blocks;
     if (plan.fast_decode) {
-      a.dec_heads = plan.dec_heads;
-      a.dec_cbw = plan.dec_cbw;
-      a.dec_allcols = plan.dec_allcols ? 1 : 0;
-      a.dec_cols = plan.dec_cols;
-      // ranges of tiles, each on one workgroup per lane
-      const int32_t cap = g_decode_wgs.load(std::memory_order_relaxed);
-      const int64_t target = cap > 0 ? cap : static_cast<int64_t>(pkv::kDecodeWGsPerCU) * std::max(dev.cus, 1);
-      const int64_t lanes = std::max(plan.dec_lanes, 1);
-      const int64_t ranges = std::max<int64_t>(1, std::min(target, plan.dec_max_wgs) / lanes);
-      a.dec_wgs = static_cast<int32_t>(ranges * lanes);
-      a.dec_lanes = plan.dec_lanes;
-      a.dec_lane_cbs = plan.dec_lane_cbs;
-      a.ws_pre = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan.ws_pre_off);
-      a.ws_row = a.ws_pre + (plan.num_gen + 1);
-      a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_off);
-      a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_off);
+      set_ranges(cap > 0 ? cap : static_cast<int64_t>(pkv::kDecodeWGsPerCU) * std::max(dev.cus, 1));
       const char* failed = nullptr;
       e = timed_at(kPhase, "decode", s, [&] {
-        hipError_t le = timed_at(kLaunch, "decode_split", s, [&] { return pkv::launch_decode_split(a, s); });
+        hipError_t le = timed_at(kLaunch, "decode_split", s, [&] { return pkv::launch_decode_split(ad, s); });
         if (le != hipSuccess) {
           failed = "decode launch";
           return le;
         }
-        le = timed_at(kLaunch, "decode_combine", s, [&] { return pkv::launch_decode_combine(a, s); });
+        le = timed_at(kLaunch, "decode_combine", s, [&] { return pkv::launch_decode_combine(ad, s); });
         if (le != hipSuccess) failed = "decode combine launch";
         return le;
       });
       if (e != hipSuccess) return hip_fail(e, failed ? failed : "decode launch");
     } else {
-      e = timed("attn_generic_gen", s, [&] { return pkv::launch_attn_generic(a, s); });
+      e = timed("attn_generic_gen", s, [&] { return pkv::launch_attn_generic(ad, s); });
       if (e != hipSuccess) return hip_fail(e, "generation attention launch");
     }
   }
@@ -404,6 +451,11 @@ int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch
 int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
                                       int64_t q_row_stride, const void* kv_pool, void* out, void* stream) {
   return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, false, 1.f, nullptr, 0, stream, true);
+}
+
+int32_t pkv_set_coschedule(int32_t on) {
+  if (on < 0) return g_cosched.load();
+  return g_cosched.exchange(on ? 1 : 0);
 }
 
 int32_t pkv_set_decode_workgroups(int32_t n) {

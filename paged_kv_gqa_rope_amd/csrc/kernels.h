@@ -90,6 +90,12 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s);
+// Mixed batch in one launch: the context requests of ac on ctx_wgs workgroups' worth of
+// the persistent context schedule, and the generation split pass of ad (its dec_wgs
+// ranges) on the rest of the grid; the combine follows separately.
+bool mixed_supported(const AttnArgs& ad, int num_ctx, int G);
+hipError_t launch_mixed(const AttnArgs& ac, const int32_t* host_ctx_len, const int32_t* host_seq_len,
+                        const AttnArgs& ad, int ctx_wgs, hipStream_t s);
 // Persistent context kernel: one launch per kPrefillMaxReqs context requests.
 struct PrefillSched {
   int32_t nreq;        // requests of this launch

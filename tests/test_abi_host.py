@@ -239,6 +239,14 @@ def test_decode_workgroup_cap_set_and_query():
     assert L.pkv_set_decode_workgroups(-1) == 0
 
 
+def test_coschedule_switch_set_and_query():
+    assert L.pkv_set_coschedule(-1) == 1                 # default: mixed batches in one launch
+    assert L.pkv_set_coschedule(0) == 1
+    assert L.pkv_set_coschedule(-1) == 0
+    assert L.pkv_set_coschedule(5) == 0                  # any nonzero value turns it on
+    assert L.pkv_set_coschedule(-1) == 1
+
+
 def test_timed_launch_wrappers_return(tmp_path):
     """Every launch goes through the timing wrappers (a phase span around per-kernel
     records); with timing off, at either level or without a device they must return:

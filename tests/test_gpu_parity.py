@@ -122,6 +122,45 @@ def test_qk_norm_append_and_attention(H, case_i):
     print(b.label, kind, style, rot, stats)
 
 
+# Mixed batches (context chunks and generation requests) run as one launch that splits the
+# CUs between the context schedule and the split pass.  Same decode workgroup count in
+# both modes, so the split pass covers the same ranges: outputs must be bitwise equal to
+# the serial launches and within the bars against the oracle.
+MIXED_CASES = [
+    # (shape, kv dtype, decode workgroups, context chunks (n, cached: a multiple of the block),
+    #  cached lengths of generation requests)
+    (4, None, 16, [(128, 0), (192, 128), (100, 384)], [20, 77, 140, 333, 500, 9]),        # GQA-8 bf16
+    (3, None, 8, [(300, 0), (65, 640)], [1, 64, 65, 900]),                                 # GQA-4 bf16
+    (2, None, 32, [(70, 0)], [0, 63, 64, 700, 1000]),                                      # MHA bf16
+    (5, "fp8", 24, [(200, 128)], [1000, 2500, 3000]),                                      # GQA-4 fp8
+    (4, "int8", 8, [(64, 64), (33, 0)], [5, 511, 512]),                                    # GQA-8 int8
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(MIXED_CASES)))
+def test_mixed_launch_matches_serial(H, case_i):
+    from paged_kv_gqa_rope_amd import _lib as L
+    k, kv, wgs, ctx, past = MIXED_CASES[case_i]
+    sh = W.SHAPES[k]
+    if kv == "fp8":
+        sh = dataclasses.replace(sh, kv_dtype=W.FP8_E4M3, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    elif kv == "int8":
+        sh = dataclasses.replace(sh, kv_dtype=W.INT8, k_scale=2.0 ** -5, v_scale=2.0 ** -5)
+    b = W.make_batch(sh, ctx=ctx, gen_past=past, seed=6100 + case_i, pool_blocks_min=4, label=f"mixed-{case_i}")
+    case("mixed", b.label, sh.name, sh.kv_dtype, wgs)
+    old_w = L.pkv_set_decode_workgroups(wgs)
+    old_c = L.pkv_set_coschedule(1)
+    try:
+        mixed = run_step(H, b).out_host()
+        L.pkv_set_coschedule(0)
+        serial = run_step(H, b).out_host()
+    finally:
+        L.pkv_set_coschedule(old_c)
+        L.pkv_set_decode_workgroups(old_w)
+    assert_bits_equal(bits_of(mixed), bits_of(serial), "mixed vs serial output")
+    compare_attention(mixed, O.run(b)["out"], sh, b.label)
+
+
 class _SpanBatch(W.Batch):
     """Queries and new keys with heads whose squares span many binades, where the
     index-order sums round differently from other orders: on even tokens every fourth

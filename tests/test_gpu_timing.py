@@ -8,18 +8,29 @@ from workloads import synth as W
 pytestmark = pytest.mark.gpu
 
 
-def test_timing_levels_record_launches_and_phases():
+@pytest.mark.parametrize("cosched", [0, 1])
+def test_timing_levels_record_launches_and_phases(cosched):
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a GPU")
     from paged_kv_gqa_rope_amd import _lib as L
     from paged_kv_gqa_rope_amd.harness import PagedStep
     b = W.small_workload(4)                  # context chunks, then generation requests
-    print("CASE timing levels", b.label, flush=True)
-    st = PagedStep(b)
+    print("CASE timing levels", b.label, "co-scheduled" if cosched else "serial", flush=True)
+    old = L.pkv_set_coschedule(cosched)
+    try:
+        _check_levels(L, PagedStep(b), cosched)
+    finally:
+        L.pkv_set_coschedule(old)
+
+
+def _check_levels(L, st, cosched):
     st.step()
     torch.cuda.synchronize()
-    expect = {1: {"append_rope", "prefill_mfma", "decode_split", "decode_combine"},
-              2: {"append_rope", "prefill_mfma", "decode"}}
+    if cosched:      # context and split pass in one launch, then the combine
+        expect = {1: {"append_rope", "mixed", "decode_combine"}, 2: {"append_rope", "mixed"}}
+    else:
+        expect = {1: {"append_rope", "prefill_mfma", "decode_split", "decode_combine"},
+                  2: {"append_rope", "prefill_mfma", "decode"}}
     spans = {}
     for level, names in expect.items():
         L.check(L.pkv_kernel_timing_enable(level))
