@@ -17,8 +17,9 @@
 // waves read the neighbouring heads' pieces of the same cache rows at about the same time,
 // which HBM serves faster than one head's pieces alone; with 2 (or 3-4) column blocks
 // (draft tokens) a segment is (request, 2 (or 1) KV heads) with all column blocks, and the
-// waves of one head load the same tiles at about the same time, so HBM serves each tile
-// once and L2 the repeats.  Otherwise a segment is (request, one KV head, column block),
+// 2 (or 4) waves of one head each load a share of every tile (K or V, or half of either),
+// stage it in one LDS tile of the head and meet at a barrier, so each tile leaves HBM
+// once.  Otherwise a segment is (request, one KV head, column block),
 // its waves sharing the tiles and merging their states in LDS at the end of each piece.
 // Per wave and tile:
 //   * S^T = K Q^T on MFMA 16x16x32 bf16: A = 16 keys x 32 dims of K, read in operand
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per
 template <int KV>
 void launch_split_t(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.dec_wgs), block(kThreads);
-  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, false>), grid, block, 0, s, a);
-  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, false>), grid, block, 0, s, a);
+  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, true>), grid, block, 0, s, a);
+  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, true>), grid, block, 0, s, a);
   else if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<KV, 4, 1, true>), grid, block, 0, s, a);
   else if (a.col_blocks == 1) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, false>), grid, block, 0, s, a);

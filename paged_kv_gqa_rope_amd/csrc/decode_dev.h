@@ -3,6 +3,8 @@
 #pragma once
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,10 +31,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// 16 bytes of the cache.  With one column block every K/V byte is read once per step and
-// every load instruction covers whole rows (whole 128-byte lines), so the loads carry the
-// nontemporal hint (NT): lines are not kept for reuse that will not come.  With several
-// column blocks (draft tokens) the other blocks read the same lines soon after: plain loads.
+// 16 bytes of the cache.  Every K/V byte is read once per step (several column blocks of a
+// head share one staged tile) and every load instruction covers whole rows (whole 128-byte
+// lines), so the loads can carry the nontemporal hint (NT): lines are not kept for reuse
+// that will not come.
 template <bool NT>
 __device__ __forceinline__ uint4 load_kv(const void* p) {
   if constexpr (NT) {
@@ -81,6 +83,16 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// Workgroup barrier for LDS data: this wave's LDS writes complete (lgkmcnt(0)), then
+// s_barrier; global loads in flight stay in flight (no vmcnt wait).  The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);   // vmcnt and expcnt unconstrained
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Registers of one 32-key tile in flight: K and V rows as loaded (16 lanes per bf16
@@ -162,7 +174,7 @@ __device__ __forceinline__ Piece read_piece(const int4* pa, const int4* pb, int 
 // across piece boundaries: a new piece starts with its first tiles already in flight, and
 // only the softmax state and Q are reset.  Each piece leaves one partial state in its slot.
 // NT: stream the cache with the nontemporal hint (every byte read once) or keep its lines
-// in L2 (several column blocks read the same keys).
+// in L2 (segments of one column block each read the same keys).
 template <int KV, int HPS, int CBW, bool NT>
 __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int k, const int plane, const int4* pla,
                                               const int4* plb, uint16_t (*vtile)[kTile * kVStride],
@@ -199,6 +211,21 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   // (scalar) base, so one register serves every load
   const uint32_t lane_off = static_cast<uint32_t>(lane / kLanes) * row_bytes + (lane % kLanes) * 16u;
   const float xscale = a.scale_log2 * a.k_scale;
+  // SHARE (several column blocks per head): the CBW waves of one head split each tile's
+  // loads (K for one half of them, V for the other; with four, 16 rows each), stage them
+  // in one LDS tile of the head and meet at a workgroup barrier before the math, so every
+  // cache byte leaves HBM once.  Two LDS tiles per head alternate between items: a wave
+  // writes tile s of item i + 2 only after the barrier of item i + 1, which every wave
+  // passes after its reads of item i are complete.
+  constexpr bool SHARE = CBW > 1;
+  constexpr int kPart = SHARE ? 2 * kLoads / CBW : 1;          // loads of a wave's share
+  const int s_kind = SHARE ? wcb / (CBW / 2 > 0 ? CBW / 2 : 1) : 0;   // 0: K rows, 1: V rows
+  const int s_it0 = SHARE ? (wcb % (CBW / 2 > 0 ? CBW / 2 : 1)) * kPart : 0;   // first load
+  struct Share {
+    uint4 r[kPart];
+  };
+  using Regs = typename std::conditional<SHARE, Share, TileRegs<KV>>::type;
+  int stg = 0;                                                  // LDS tile of the next item
 
   // ---- fetch cursor (wave-uniform): item f_k of piece f_p, with the piece's facts kept in
   // scalars (the LDS list is read only when the cursor moves to another piece)
@@ -244,7 +271,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   // at the tile's first slot) or B1 (the block of rows 16..31; the same block unless
   // T = 16).  Rows past the piece end are still slots of an allocated block (in bounds);
   // their scores are masked and their V rows zeroed in compute.
-  auto issue = [&](const Ticket& t, TileRegs<KV>& R) {
+  auto issue = [&](const Ticket& t, Regs& R) {
     int32_t id0 = __builtin_amdgcn_readfirstlane(t.id0);
     int32_t id1 = __builtin_amdgcn_readfirstlane(t.id1);
     id0 = (id0 >= 0 && id0 < a.num_blocks) ? id0 : 0;
@@ -253,12 +280,22 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     const char* b0 = head + static_cast<int64_t>(id0) * blk_bytes + static_cast<int64_t>(t.tb & tmask) * row_bytes;
     const char* b1 = a.T >= kTile ? b0 : head + static_cast<int64_t>(id1) * blk_bytes - 16 * static_cast<int64_t>(row_bytes);
     const int64_t vofs = static_cast<int64_t>(a.T) * row_bytes;
+    if constexpr (SHARE) {
+      const char* bk = s_kind ? b0 + vofs : b0;
+      const char* bh = s_kind ? b1 + vofs : b1;
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it)
-      R.k[it] = load_kv<NT>((it < kLoads / 2 ? b0 : b1) + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
+      for (int j = 0; j < kPart; ++j) {
+        const int it = s_it0 + j;
+        R.r[j] = load_kv<NT>((it < kLoads / 2 ? bk : bh) + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
+      }
+    } else {
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it)
-      R.v[it] = load_kv<NT>((it < kLoads / 2 ? b0 : b1) + vofs + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
+      for (int it = 0; it < kLoads; ++it)
+        R.k[it] = load_kv<NT>((it < kLoads / 2 ? b0 : b1) + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+        R.v[it] = load_kv<NT>((it < kLoads / 2 ? b0 : b1) + vofs + static_cast<int64_t>(it * kRows) * row_bytes + lane_off);
+    }
   };
 
   // ---- state of the piece being computed
@@ -365,43 +402,8 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
       __syncthreads();                                          // LDS free for the next tiles
     }
   };
-  auto compute = [&](const int tb, const int kend, const int lim_all, const TileRegs<KV>& R) {
-    // K and V rows into this wave's LDS tiles (bf16; an fp8 / int8 cache is dequantised here)
-    wave_lds_fence();
-    if constexpr (KV == F_BF16) {
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = it * 4 + lg;
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, li) * 8) = R.k[it];
-        *reinterpret_cast<uint4*>(vt + row * kVStride + li * 8) = R.v[it];
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = it * 8 + lane / 8, c0 = (lane % 8) * 2;
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) =
-            codes8_to_bf16x8<KV>(make_uint2(R.k[it].x, R.k[it].y));
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) =
-            codes8_to_bf16x8<KV>(make_uint2(R.k[it].z, R.k[it].w));
-        uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
-        *reinterpret_cast<uint4*>(d) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].x, R.v[it].y));
-        *reinterpret_cast<uint4*>(d + 8) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].z, R.v[it].w));
-      }
-    }
-    if (tb + kTile > kend) {
-      // wave-uniform, last tile of a piece only: rows at or past the piece end were read
-      // from unwritten slots; zero their V so that P = 0 times them stays 0
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it) {
-        const int row = it * kRows + lane / kLanes;
-        if (tb + row >= kend) {
-          uint16_t* d = vt + row * kVStride + (lane % kLanes) * (kD / kLanes);
-#pragma unroll
-          for (int j = 0; j < kD / kLanes; j += 8) *reinterpret_cast<uint4*>(d + j) = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-    wave_lds_fence();
+  // The tile's math from LDS tiles kt (K) and vt (V): scores, online softmax, O += P V.
+  auto tile_math = [&](const uint16_t* kt, const uint16_t* vt, const int tb, const int kend, const int lim_all) {
     // A operand K: lane (li, lg) of step ks holds key kb*16 + li, dims ks*32 + lg*8 .. +7
     bf16x8 kf[2][4];
 #pragma unroll
@@ -487,16 +489,107 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     }
   };
 
-  // Compute item k of the current piece from R (nothing for an item past its tiles).
-  auto compute_item = [&](int k, const TileRegs<KV>& R) {
+  // This wave's share of a tile into the head's LDS tile (SHARE); V rows at or past the
+  // piece end are written as zeros (P = 0 times them stays 0).
+  auto stage_share = [&](uint16_t* kt, uint16_t* vt, const int tb, const int kend, const Regs& R) {
+    if constexpr (SHARE) {
+      // the row and byte column of load `it` as in `issue`
+      auto row_of = [&](int it) { return it * kRows + lane / kLanes; };
+      if (s_kind == 0) {                                        // K rows (wave-uniform)
+#pragma unroll
+        for (int j = 0; j < kPart; ++j) {
+          const int row = row_of(s_it0 + j);
+          if constexpr (KV == F_BF16) {
+            *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, li) * 8) = R.r[j];
+          } else {
+            const int c0 = (lane % 8) * 2;
+            *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) = codes8_to_bf16x8<KV>(make_uint2(R.r[j].x, R.r[j].y));
+            *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) = codes8_to_bf16x8<KV>(make_uint2(R.r[j].z, R.r[j].w));
+          }
+        }
+      } else {                                                  // V rows
+        const int lim = tb + kTile > kend ? kend - tb : kTile;  // rows from lim on are zeroed
+#pragma unroll
+        for (int j = 0; j < kPart; ++j) {
+          const int row = row_of(s_it0 + j);
+          const bool keep = row < lim;
+          if constexpr (KV == F_BF16) {
+            const uint4 u = R.r[j];
+            *reinterpret_cast<uint4*>(vt + row * kVStride + li * 8) =
+                make_uint4(keep ? u.x : 0u, keep ? u.y : 0u, keep ? u.z : 0u, keep ? u.w : 0u);
+          } else {
+            const uint4 lo = codes8_to_bf16x8<KV>(make_uint2(R.r[j].x, R.r[j].y));
+            const uint4 hi = codes8_to_bf16x8<KV>(make_uint2(R.r[j].z, R.r[j].w));
+            uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
+            *reinterpret_cast<uint4*>(d) = make_uint4(keep ? lo.x : 0u, keep ? lo.y : 0u, keep ? lo.z : 0u, keep ? lo.w : 0u);
+            *reinterpret_cast<uint4*>(d + 8) = make_uint4(keep ? hi.x : 0u, keep ? hi.y : 0u, keep ? hi.z : 0u, keep ? hi.w : 0u);
+          }
+        }
+      }
+    }
+  };
+  // K and V rows of a whole tile into this wave's LDS tiles (bf16; an fp8 / int8 cache is
+  // dequantised here), then the tile's math.
+  auto compute = [&](const int tb, const int kend, const int lim_all, const TileRegs<KV>& R) {
+    wave_lds_fence();
+    if constexpr (KV == F_BF16) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + lg;
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, li) * 8) = R.k[it];
+        *reinterpret_cast<uint4*>(vt + row * kVStride + li * 8) = R.v[it];
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = it * 8 + lane / 8, c0 = (lane % 8) * 2;
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) =
+            codes8_to_bf16x8<KV>(make_uint2(R.k[it].x, R.k[it].y));
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) =
+            codes8_to_bf16x8<KV>(make_uint2(R.k[it].z, R.k[it].w));
+        uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
+        *reinterpret_cast<uint4*>(d) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].x, R.v[it].y));
+        *reinterpret_cast<uint4*>(d + 8) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].z, R.v[it].w));
+      }
+    }
+    if (tb + kTile > kend) {
+      // wave-uniform, last tile of a piece only: rows at or past the piece end were read
+      // from unwritten slots; zero their V so that P = 0 times them stays 0
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it) {
+        const int row = it * kRows + lane / kLanes;
+        if (tb + row >= kend) {
+          uint16_t* d = vt + row * kVStride + (lane % kLanes) * (kD / kLanes);
+#pragma unroll
+          for (int j = 0; j < kD / kLanes; j += 8) *reinterpret_cast<uint4*>(d + j) = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    wave_lds_fence();
+    tile_math(kt, vt, tb, kend, lim_all);
+  };
+  // Compute item k of the current piece from R (nothing for an item past its tiles).  With
+  // SHARE every wave stages its share and meets the others at the barrier, whether or not
+  // the piece has its column block.
+  auto compute_item = [&](int k, const Regs& R) {
     const int tile = base + k * TS;
-    if (tile < c_nt && c_valid) compute((c_t0 + tile) * kTile, c_kend, c_lim, R);
+    if constexpr (SHARE) {
+      uint16_t* skt = ktile[wh * 2 + stg];
+      uint16_t* svt = vtile[wh * 2 + stg];
+      stg ^= 1;
+      const int tb = (c_t0 + tile) * kTile;
+      stage_share(skt, svt, tb, c_kend, R);
+      lds_barrier();
+      if (tile < c_nt && c_valid) tile_math(skt, svt, tb, c_kend, c_lim);
+    } else {
+      if (tile < c_nt && c_valid) compute((c_t0 + tile) * kTile, c_kend, c_lim, R);
+    }
   };
 
   // Software pipeline over the stream: the next item's loads are in flight while an item
   // is computed and its block IDs are read one item further ahead; every path has the same
   // loads in flight, so the compiler's wait before an item's compute covers that item only.
-  TileRegs<KV> ra, rb;
+  Regs ra, rb;
   Ticket ta, tb;
   fetch_piece(0);
   fetch(ta);
@@ -656,8 +749,8 @@ __host__ __device__ constexpr int decode_lds_bytes() {
 
 
 // Split pass with register-staged tiles (any KV head count, any cache format).  With
-// CBW > 1 a segment carries all column blocks of its heads (the waves of one head load
-// the same tiles at about the same time; HBM serves them once, L2 the repeats).
+// CBW > 1 a segment carries all column blocks of its heads, and the waves of one head
+// share each staged tile (every tile leaves HBM once).
 template <int KV, int HPS, int CBW, bool NT>
 __device__ __forceinline__ void decode_split_body(const AttnArgs& a, int bid, int nbid, unsigned char* lds) {
   auto& vtile = *reinterpret_cast<uint16_t (*)[kWaves][kTile * kVStride]>(lds);
