@@ -49,116 +49,149 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   decode_split_body<KV, HPS, CBW, NT>(a, blockIdx.x, gridDim.x, lds);
 }
 
-// One wave per (generation token, query head), kCombHeads query heads per workgroup, two
+// One wave per (generation token, query head) -- or per TPW tokens of one request and query
+// head, when requests carry draft tokens -- kCombHeads query heads per workgroup, two
 // dimensions per lane.  The pieces of the token's (request, lane) are the ranges that meet
 // the request's tiles (found from the recorded first tiles and the same range
 // arithmetic).  M = max m_p and L = sum 2^(m_p-M) l_p over them, then lane d sums
 // 2^(m_p-M) o_p[2d, 2d+1] over the pieces in order.  64 pieces at a time: lane p holds
 // piece p's (m, l), butterfly reductions give M and L in a fixed order, and the o_p are
-// loaded eight at a time.  Every metadata load is issued before the first use; at most
-// 64 VGPRs keep 8 waves per SIMD resident (one round of waves for most batches).  Pieces
-// past a draft token's position hold m = -inf and weigh nothing; the piece holding key 0
-// makes M finite.
+// loaded kPre (then eight) at a time.  Every metadata load is issued before the first use,
+// and the loads of a wave's TPW tokens are all in flight together; at most 64 VGPRs keep
+// 8 waves per SIMD resident (one round of waves for most batches).  Pieces past a draft
+// token's position hold m = -inf and weigh nothing; the piece holding key 0 makes M finite.
+// The sums run in the same order for every TPW (bitwise the same output).
+template <int TPW>
 __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_combine_kernel(AttnArgs a) {
+  constexpr int kPre = TPW == 1 ? 8 : 4;                             // o_p loads issued with the (m, l) loads
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int h = blockIdx.x * kCombHeads + wave, rg = blockIdx.y, tok = blockIdx.z;
+  const int h = blockIdx.x * kCombHeads + wave, rg = blockIdx.y, tok0 = blockIdx.z * TPW;
   const int r = a.req_begin + rg;
   const int R = a.req_end - a.req_begin, W = a.dec_wgs;
   const int n_dev = a.ctx_len[r], s_dev = a.seq_len[r];
   const int64_t P = a.ws_pre[rg], U = a.ws_pre[R], row0 = a.ws_row[rg];
-  if (h >= a.H || tok >= n_dev) return;                             // wave-uniform
+  if (h >= a.H || tok0 >= n_dev || U <= 0 || W <= 0) return;      // wave-uniform
   const int G = a.H / a.Hkv, B = a.dec_heads;
   const int n = max(n_dev, 1), S = max(s_dev, n);                   // as the split pass keeps them
   const int tiles = (S - 1) / kTile + 1;
   const int cbs = static_cast<int>(min64((static_cast<int64_t>(G) * n + 15) / 16, a.col_blocks));
-  const int64_t row = row0 + tok;
-  if (row < a.row_begin || row >= a.N) return;                      // outside the generation rows
   const int g = h / G, hg = g / B, wv = g % B;
-  // segment and stored column of (token, head): (request, head group, column block) and
-  // the column within its block, or, when segments carry all column blocks, (request,
-  // head group) and the column
   const bool all = a.dec_allcols != 0;
-  const int c = tok * G + h % G, cb = all ? 0 : c / 16, col = all ? c : c % 16;
   const int ncb = max(a.dec_lane_cbs, 1), NL = max(a.dec_lanes, 1);
-  const int pl = hg * ncb + (ncb > 1 ? cb : 0);                     // the split-pass lane that computed it
   const int Wr = max(W / NL, 1);
-  if ((!all && cb >= cbs) || col >= a.dec_cols || U <= 0 || W <= 0) return;
   // the ranges that meet the request's tiles [P, P + tiles): its pieces, range k in slot (rg + k) * NL + pl
   const int64_t f = ((P + 1) * Wr - 1) / U, l = ((P + tiles) * Wr - 1) / U;
   const int kf = static_cast<int>(min64(max64(f, 0), Wr - 1));
   const int np = static_cast<int>(min64(max64(l, kf), Wr - 1)) - kf + 1;
   const int64_t stride = static_cast<int64_t>(NL) * B * a.dec_cols;          // entries between pieces
-  const int64_t e0 = ((static_cast<int64_t>(rg + kf) * NL + pl) * B + wv) * a.dec_cols + col;   // first piece
-  const float2* op = reinterpret_cast<const float2*>(a.ws_o + e0 * kD) + lane;
-  const int64_t ps = stride * (kD / 2);                             // float2 steps between pieces
-  const float* mlp = a.ws_ml + e0 * 2;
-  float L = 0.f, ox = 0.f, oy = 0.f;
+  // Per token: its output row and the first piece's entry.  A token outside the
+  // generation rows, or whose column the split pass did not compute, gets no output.
+  bool ok[TPW];
+  int64_t row[TPW];
+  const float* ob[TPW];                                             // the first piece's o (wave-uniform)
+  const float* mlp[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tok = tok0 + t;
+    row[t] = row0 + tok;
+    // segment and stored column of (token, head): (request, head group, column block) and
+    // the column within its block, or, when segments carry all column blocks, (request,
+    // head group) and the column
+    const int c = tok * G + h % G, cb = all ? 0 : c / 16, col = all ? c : c % 16;
+    const int pl = hg * ncb + (ncb > 1 ? cb : 0);                   // the split-pass lane that computed it
+    ok[t] = tok < n_dev && row[t] >= a.row_begin && row[t] < a.N && !(!all && cb >= cbs) && col < a.dec_cols;
+    const int64_t e0 = ok[t] ? ((static_cast<int64_t>(rg + kf) * NL + pl) * B + wv) * a.dec_cols + col : 0;
+    ob[t] = a.ws_o + e0 * kD;
+    mlp[t] = a.ws_ml + e0 * 2;
+  }
+  // o_p of piece p for this lane
+  const int64_t ps = stride * kD;                                   // floats between pieces
+  auto o_at = [&](int t, int p) { return *reinterpret_cast<const float2*>(ob[t] + p * ps + 2 * lane); };
+  float L[TPW], ox[TPW], oy[TPW];
   if (np <= kWave) {
     // One memory round trip: every lane loads one piece's (m, l) while the first kPre
     // pieces' o are loaded (issued after the (m, l) loads, so waiting for those does not
     // wait for these); the weights follow from the maximum.
-    constexpr int kPre = 8;
-    const float2 mlv = *reinterpret_cast<const float2*>(mlp + min(lane, np - 1) * stride * 2);
-    float2 u0[kPre];
+    float2 mlv[TPW], u0[TPW][kPre];
 #pragma unroll
-    for (int e = 0; e < kPre; ++e) u0[e] = op[min(e, np - 1) * ps];   // weight 0 past the last piece
-    const float M = wave_max(lane < np ? mlv.x : -INFINITY);
-    const float wt = lane < np && mlv.x != -INFINITY ? exp2f(mlv.x - M) : 0.f;
-    L = wave_sum(wt * (lane < np ? mlv.y : 0.f));
+    for (int t = 0; t < TPW; ++t)
+      mlv[t] = ok[t] ? *reinterpret_cast<const float2*>(mlp[t] + min(lane, np - 1) * stride * 2) : make_float2(0.f, 0.f);
 #pragma unroll
-    for (int e = 0; e < kPre; ++e) {
-      const float w = __shfl(wt, e, kWave);
-      ox += w * u0[e].x;
-      oy += w * u0[e].y;
-    }
-    for (int k = kPre; k < np; k += 8) {                           // eight loads in flight
-      float2 u[8];
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = op[min(k + e, np - 1) * ps];
+      for (int e = 0; e < kPre; ++e)                                // weight 0 past the last piece
+        u0[t][e] = ok[t] ? o_at(t, min(e, np - 1)) : make_float2(0.f, 0.f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = __shfl(wt, k + e, kWave);                  // 0 past the last piece
-        ox += w * u[e].x;
-        oy += w * u[e].y;
+    for (int t = 0; t < TPW; ++t) {
+      const float M = wave_max(lane < np ? mlv[t].x : -INFINITY);
+      const float wt = lane < np && mlv[t].x != -INFINITY ? exp2f(mlv[t].x - M) : 0.f;
+      L[t] = wave_sum(wt * (lane < np ? mlv[t].y : 0.f));
+      ox[t] = oy[t] = 0.f;
+#pragma unroll
+      for (int e = 0; e < kPre; ++e) {
+        const float w = __shfl(wt, e, kWave);
+        ox[t] += w * u0[t][e].x;
+        oy[t] += w * u0[t][e].y;
+      }
+      for (int k = kPre; k < np && ok[t]; k += 8) {               // eight loads in flight
+        float2 u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = o_at(t, min(k + e, np - 1));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // 0 past the last piece (lanes >= np hold weight 0; pieces past lane 63 do not exist)
+          const float w = k + e < kWave ? __shfl(wt, k + e, kWave) : 0.f;
+          ox[t] += w * u[e].x;
+          oy[t] += w * u[e].y;
+        }
       }
     }
   } else {
-    float M = -INFINITY;
-    for (int pb = 0; pb < np; pb += kWave) {
-      const int p = pb + lane;
-      M = fmaxf(M, wave_max(p < np ? mlp[p * stride * 2] : -INFINITY));
-    }
-    for (int pb = 0; pb < np; pb += kWave) {
-      const int p = pb + lane;
-      float wt = 0.f, lp = 0.f;
-      if (p < np) {
-        const float2 v = *reinterpret_cast<const float2*>(mlp + p * stride * 2);
-        wt = v.x == -INFINITY ? 0.f : exp2f(v.x - M);
-        lp = v.y;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      L[t] = ox[t] = oy[t] = 0.f;
+      if (!ok[t]) continue;
+      float M = -INFINITY;
+      for (int pb = 0; pb < np; pb += kWave) {
+        const int p = pb + lane;
+        M = fmaxf(M, wave_max(p < np ? mlp[t][p * stride * 2] : -INFINITY));
       }
-      L += wave_sum(wt * lp);
-      const int cnt = min(kWave, np - pb);
-      for (int k = 0; k < cnt; k += 8) {                           // eight loads in flight
-        float2 u[8];
+      for (int pb = 0; pb < np; pb += kWave) {
+        const int p = pb + lane;
+        float wt = 0.f, lp = 0.f;
+        if (p < np) {
+          const float2 v = *reinterpret_cast<const float2*>(mlp[t] + p * stride * 2);
+          wt = v.x == -INFINITY ? 0.f : exp2f(v.x - M);
+          lp = v.y;
+        }
+        L[t] += wave_sum(wt * lp);
+        const int cnt = min(kWave, np - pb);
+        for (int k = 0; k < cnt; k += 8) {                         // eight loads in flight
+          float2 u[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = k + e < cnt ? op[(pb + k + e) * ps] : make_float2(0.f, 0.f);
+          for (int e = 0; e < 8; ++e) u[e] = k + e < cnt ? o_at(t, pb + k + e) : make_float2(0.f, 0.f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float w = __shfl(wt, k + e, kWave);                // u[e] = 0 past the last piece
-          ox += w * u[e].x;
-          oy += w * u[e].y;
+          for (int e = 0; e < 8; ++e) {
+            const float w = __shfl(wt, k + e, kWave);              // u[e] = 0 past the last piece
+            ox[t] += w * u[e].x;
+            oy[t] += w * u[e].y;
+          }
         }
       }
     }
   }
-  const float sc = a.v_scale / L;
-  const int64_t oi = (row * a.H + h) * kD + 2 * lane;
-  if (a.out_fmt == F_FP8) {
-    const uint32_t lo = f32_to_e4m3(ox * sc * a.out_mul), hi = f32_to_e4m3(oy * sc * a.out_mul);
-    *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + oi) = static_cast<uint16_t>(lo | (hi << 8));
-  } else {
-    const uint32_t lo = f32_to_bf16(ox * sc), hi = f32_to_bf16(oy * sc);
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) = lo | (hi << 16);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (!ok[t]) continue;
+    const float sc = a.v_scale / L[t];
+    const int64_t oi = (row[t] * a.H + h) * kD + 2 * lane;
+    if (a.out_fmt == F_FP8) {
+      const uint32_t lo = f32_to_e4m3(ox[t] * sc * a.out_mul), hi = f32_to_e4m3(oy[t] * sc * a.out_mul);
+      *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.out) + oi) = static_cast<uint16_t>(lo | (hi << 8));
+    } else {
+      const uint32_t lo = f32_to_bf16(ox[t] * sc), hi = f32_to_bf16(oy[t] * sc);
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) = lo | (hi << 16);
+    }
   }
 }
 
@@ -182,8 +215,12 @@ hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((a.H + kCombHeads - 1) / kCombHeads, a.req_end - a.req_begin, a.max_n);
-  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(kCombHeads * kWave), 0, s, a);
+  constexpr int kTpw = 2;                                            // tokens per wave with draft tokens
+  const int hb = (a.H + kCombHeads - 1) / kCombHeads, R = a.req_end - a.req_begin;
+  if (a.max_n > 1)
+    hipLaunchKernelGGL(decode_combine_kernel<kTpw>, dim3(hb, R, (a.max_n + kTpw - 1) / kTpw), dim3(kCombHeads * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<1>, dim3(hb, R, a.max_n), dim3(kCombHeads * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -466,6 +466,23 @@ def test_decode_split_workgroup_counts(H, case_i, wgs):
     compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
 
 
+@pytest.mark.parametrize("wgs", [116, 120, 122, 124, 126, 128, 132, 140])
+def test_combine_piece_counts_around_one_wave(H, wgs):
+    """One long request with draft tokens next to two short ones, cut into about 58 to 70
+    pieces (W / 2 ranges over 128 tiles): the combine's single-round-trip path up to 64
+    pieces, its remainder loads past the first pieces, and the general path above 64."""
+    from paged_kv_gqa_rope_amd import _lib as L
+    sh = W.Shape("combine-pieces", 32, 8, 128, 64, W.BF16, W.BF16, 1e4, max_num_tokens=1 << 14)
+    b = W.make_batch(sh, gen_past=[3996, 2, 40], gen_new=[4, 2, 3], seed=5300 + wgs, pool_blocks_min=3)
+    case("combine piece counts", sh.name, "W", wgs)
+    old = L.pkv_set_decode_workgroups(wgs)
+    try:
+        st = run_step(H, b)
+    finally:
+        L.pkv_set_decode_workgroups(old)
+    compare_attention(st.out_host(), O.run(b)["out"], sh, sh.name)
+
+
 def test_decode_fp8_saturating_values(H):
     # values beyond 448 * scale saturate on write; the oracle reads the same codes
     sh = W.Shape("fp8-sat", 8, 2, 128, 64, W.BF16, W.FP8_E4M3, 1e4, k_scale=2.0 ** -9, v_scale=2.0 ** -9)
