@@ -368,8 +368,14 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
         widen8<IO>(q8, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const double d = x[e] - mean;
-          ss += d * d;
+          if (layer) {
+            const double d = x[e] - mean;
+            ss += d * d;
+          } else {
+            // x widens a bf16 or fp32 value (at most 24 significant bits), so x * x is
+            // exact in fp64 and the fused form rounds once, as ss + x * x does
+            ss = __builtin_fma(x[e], x[e], ss);
+          }
         }
       }
       stat[h] = make_double2(mean, 1.0 / __builtin_sqrt(ss / static_cast<double>(D) + a.norm_eps));
