@@ -31,6 +31,21 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray,
     ``heads`` optionally restricts the computed query heads (output keeps only
     those, in the given order).
     """
+    L = np.asarray(K).shape[0]
+    positions = np.asarray(positions, dtype=np.int64)
+    visible = np.arange(L)[None, :] <= positions[:, None]        # [n, L]
+    return attend_visible(q, K, V, visible, scale=scale, heads=heads)
+
+
+def attend_visible(q: np.ndarray, K: np.ndarray, V: np.ndarray, visible: np.ndarray,
+                   scale: float | None = None, heads=None) -> np.ndarray:
+    """O[i, h] = sum over visible t of softmax_t(scale * <q[i,h], K[t,g]>) V[t,g].
+
+    The general mask: ``visible`` [n, L] says which cache positions row i attends to
+    (every row sees at least one).  Draft tokens verified as a tree ("TensorRT-LLM
+    source analysis report", section 1.4: position offsets and a packed mask) see the
+    cached tokens and, among the new ones, what their mask row names.
+    """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -40,8 +55,7 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray,
     if scale is None:
         scale = 1.0 / np.sqrt(np.float64(D))
     heads = list(range(H)) if heads is None else list(heads)
-    positions = np.asarray(positions, dtype=np.int64)
-    masked = np.arange(L)[None, :] > positions[:, None]          # [n, L]
+    masked = ~np.asarray(visible, dtype=bool)                    # [n, L]
     out = np.empty((n, len(heads), D), dtype=np.float64)
     for oi, h in enumerate(heads):
         g = h // G

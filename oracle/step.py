@@ -8,8 +8,12 @@ The step (from the pages' description of the problem):
    section); packed rows carry no padding and context requests come before
    generation requests (report, section 1.3).  A generation request brings 1
    token, or 1 + k draft tokens to verify (report, section 1.4: generation
-   lengths and position offsets); read as one chain, token i at position
-   p_r + i, so the drafts are causal among themselves like a chunk;
+   lengths, position offsets, packed mask); by default read as one chain, token i
+   at position p_r + i, so the drafts are causal among themselves like a chunk.
+   Read as a tree (``tree``), token i sits at position p_r + offset_i and sees
+   the cached tokens and the new tokens j whose bit j its mask row sets, while
+   its K/V still go to cache position p_r + i (the offsets move the rotation,
+   not the slot);
 2. append -- optionally normalise each head of the new q and k (see
    ``qknorm``), rotate them at their absolute positions p_r + i
    (RoPE, see ``rope``), round q to the io format (q_out), store the rotated k
@@ -35,7 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .attention import attend
+from .attention import attend, attend_visible
 from .qknorm import qk_norm
 from .rope import neox_tables, rope_apply
 
@@ -51,16 +55,41 @@ def tables(batch, max_pos: int | None = None):
     return neox_tables(sh.rope_theta, sh.rot_dim, max(max_pos, 1))
 
 
-def append_request(batch, r: int, tabs, rope: bool = True):
-    """Return (q_out, k_store, v_store) of request r's new tokens.
+def _as_tree(batch, r: int, tree) -> bool:
+    """Whether request r's new tokens are read as a draft tree (generation requests of a
+    tree batch, or of any batch when ``tree`` is True)."""
+    use = batch.tree if tree is None else tree
+    return bool(use) and int(batch.request_types[r]) == 1          # a generation request
+
+
+def spec_rows(batch, r: int):
+    """(offsets [n], masks [n] as Python ints) of request r's rows, from the batch's
+    draft-tree inputs."""
+    off, mask = batch.spec_inputs()
+    a = int(batch.token_offsets[r])
+    n = int(batch.context_lengths[r])
+    rows = mask[a:a + n].astype(np.uint64)
+    return off[a:a + n].astype(np.int64), [int(m[0]) | (int(m[1]) << 32) for m in rows]
+
+
+def positions_of(batch, r: int, tree=None) -> np.ndarray:
+    """Rotation positions of request r's new tokens: p_r + i, or p_r + offset_i."""
+    n = int(batch.context_lengths[r])
+    p = int(batch.past_lengths[r])
+    if _as_tree(batch, r, tree):
+        return p + spec_rows(batch, r)[0]
+    return np.arange(p, p + n)
+
+
+def append_request(batch, r: int, tabs, rope: bool = True, tree=None):
+    """Return (q_out, k_store, v_store) of request r's new tokens, in token order (cache
+    positions p_r .. S_r - 1).
 
     q_out is in the io representation; k_store/v_store in the cache
     representation.  ``rope=False`` stores k unrotated and skips q.
     """
     sh = batch.shape
-    n = int(batch.context_lengths[r])
-    p = int(batch.past_lengths[r])
-    pos = np.arange(p, p + n)
+    pos = positions_of(batch, r, tree)
     k = io_decode(batch, batch.new_k(r))
     v = io_decode(batch, batch.new_v(r))
     q_out = None
@@ -87,22 +116,35 @@ def history_request(batch, r: int):
     return k, v
 
 
-def cache_request(batch, r: int, tabs):
+def cache_request(batch, r: int, tabs, tree=None):
     """(q_out, K, V): request r's rotated q (io repr) and its whole cache after
     the append, decoded to fp64, contiguous by position [S_r, Hkv, D]."""
     sh = batch.shape
-    q_out, k_new, v_new = append_request(batch, r, tabs)
+    q_out, k_new, v_new = append_request(batch, r, tabs, tree=tree)
     k_hist, v_hist = history_request(batch, r)
     K = codecs.decode(np.concatenate([k_hist, k_new], axis=0), sh.kv_dtype, sh.k_scale)
     V = codecs.decode(np.concatenate([v_hist, v_new], axis=0), sh.kv_dtype, sh.v_scale)
     return q_out, K, V
 
 
-def attention_request(batch, r: int, tabs, heads=None, rows=None) -> np.ndarray:
+def attention_request(batch, r: int, tabs, heads=None, rows=None, tree=None) -> np.ndarray:
     """fp64 attention output of request r's new rows: [n_r (or len(rows)), H (or len(heads)), D]."""
-    q_out, K, V = cache_request(batch, r, tabs)
+    q_out, K, V = cache_request(batch, r, tabs, tree=tree)
     p = int(batch.past_lengths[r])
     q = io_decode(batch, q_out)
+    if _as_tree(batch, r, tree):
+        # row i sees cache positions 0 .. p-1 and p + j for every bit j of its mask
+        masks = spec_rows(batch, r)[1]
+        L = K.shape[0]
+        visible = np.zeros((q.shape[0], L), dtype=bool)
+        visible[:, :p] = True
+        for i, m in enumerate(masks):
+            for j in range(L - p):
+                visible[i, p + j] = bool((m >> j) & 1)
+        if rows is not None:
+            rows = np.asarray(rows)
+            q, visible = q[rows], visible[rows]
+        return attend_visible(q, K, V, visible, heads=heads)
     positions = p + np.arange(q.shape[0])
     if rows is not None:
         rows = np.asarray(rows)
@@ -110,17 +152,17 @@ def attention_request(batch, r: int, tabs, heads=None, rows=None) -> np.ndarray:
     return attend(q, K, V, positions, heads=heads)
 
 
-def run(batch):
+def run(batch, tree=None):
     """Whole step: dict with packed q_out (io repr), out (fp64 [N, H, D]) and the
-    per-request stored new K/V."""
+    per-request stored new K/V.  ``tree`` overrides the batch's reading of draft tokens."""
     tabs = tables(batch)
     q_outs, outs, k_new, v_new = [], [], [], []
     for r in range(batch.num_requests):
-        q_out, kn, vn = append_request(batch, r, tabs)
+        q_out, kn, vn = append_request(batch, r, tabs, tree=tree)
         q_outs.append(q_out)
         k_new.append(kn)
         v_new.append(vn)
-        outs.append(attention_request(batch, r, tabs))
+        outs.append(attention_request(batch, r, tabs, tree=tree))
     return {
         "q_out": np.concatenate(q_outs, axis=0),
         "out": np.concatenate(outs, axis=0),

@@ -184,6 +184,57 @@ def test_draft_tokens_equal_single_token_steps_with_the_earlier_drafts_cached():
         assert np.allclose(outA[i], outB[0], rtol=0, atol=1e-12), i
 
 
+def test_chain_shaped_tree_inputs_give_the_chain_step():
+    """Position offsets 0..n-1 with lower-triangular masks (the inputs a chain of drafts
+    hands over) read through the tree path give the chain step bit for bit."""
+    for sh in (W.SHAPES[1], W.SHAPES[4]):
+        b = W.make_batch(sh, ctx=[(20, 40)], gen_past=[29, 0, 70], gen_new=[5, 3, 1], seed=81)
+        off, mask = b.spec_inputs()
+        assert list(off[20:25]) == [0, 1, 2, 3, 4] and [int(m) for m in mask[20:25, 0]] == [1, 3, 7, 15, 31]
+        a, t = S.run(b, tree=False), S.run(b, tree=True)
+        assert np.array_equal(a["q_out"], t["q_out"]) and np.array_equal(a["out"], t["out"])
+        for x, y in zip(a["k_new"], t["k_new"]):
+            assert np.array_equal(x, y)
+
+
+def test_tree_token_equals_one_token_step_over_its_path():
+    """A draft token of a tree at depth d (position offset d, mask = itself and its
+    ancestors; source analysis report 1.4) attends like a one-token generation request
+    at position p + d whose cache holds the history and its ancestors' stored K/V in
+    path order: the same keys, rotated at the same positions.  Its stored key is the one
+    that request stores.  Built as separate batches; fp32 io and cache, so storing is
+    exact."""
+    from batch_util import Crafted
+    sh = W.SHAPES[1]
+    p, n = 29, 9
+    A = W.make_batch(sh, gen_past=[p], gen_new=[n], seed=79, tree=True)
+    par = A.draft_parents(0)
+    assert any(par[i] != i - 1 for i in range(1, n)), "the seed must give a branching tree"
+    tabs = S.tables(A)
+    outA = S.attention_request(A, 0, tabs)
+    _, k_new, v_new = S.append_request(A, 0, tabs)
+    hk, hv = A.hist_k(0), A.hist_v(0)
+    for i in range(n):
+        path = []
+        j = i
+        while j >= 0:
+            path.append(j)
+            j = int(par[j])
+        path = path[::-1]                       # root .. i
+        d = len(path) - 1
+        anc = path[:-1]
+        Bi = W.make_batch(sh, gen_past=[p + d], seed=80)
+        Ci = Crafted(sh, Bi.seed, Bi.request_types, Bi.context_lengths, Bi.sequence_lengths,
+                     Bi.block_table, Bi.num_pool_blocks, "tree-path")
+        Ci.set_values([A.new_q(0)[i:i + 1]], [A.new_k(0)[i:i + 1]], [A.new_v(0)[i:i + 1]],
+                      [np.concatenate([hk, k_new[anc].view(np.float32)])],
+                      [np.concatenate([hv, v_new[anc].view(np.float32)])])
+        outB = S.attention_request(Ci, 0, S.tables(Ci))
+        assert np.allclose(outA[i], outB[0], rtol=0, atol=1e-12), i
+        _, kB, _ = S.append_request(Ci, 0, S.tables(Ci))
+        assert np.array_equal(k_new[i], kB[0]), i
+
+
 # ------------------------------------------------------------------ softmax / attention
 def test_softmax_printed_temperature_example():
     rows = [l.split() for l in open(os.path.join(HERE, "golden", "softmax_temperature.txt"))

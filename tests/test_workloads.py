@@ -74,3 +74,26 @@ def test_small_fitted_scales():
     assert 5.0 < ak < 7.0 and 5.0 < av < 7.0
     i8 = W.fitted(W.small_workload(2), W.INT8)
     assert i8.shape.kv_dtype == W.INT8 and i8.shape.k_scale == W.fit_kv_scales(i8, W.INT8)[0]
+
+
+def test_draft_tree_inputs_are_consistent():
+    """The generator's tree inputs: a row's mask holds itself and its ancestors (bit i
+    set, no bit at or past n), its offset is its depth (popcount - 1), a parent's mask is
+    inside its child's, and context rows carry zeros."""
+    b = W.make_batch(W.SHAPES[4], ctx=[(16, 0)], gen_past=[10, 300, 5], gen_new=[7, 1, 33], seed=5, tree=True)
+    off, mask = b.spec_inputs()
+    assert off.shape == (b.num_tokens,) and mask.shape == (b.num_tokens, 2)
+    assert not off[:16].any() and not mask[:16].any()
+    row = 16
+    for r in range(1, b.num_requests):
+        n = int(b.context_lengths[r])
+        par = b.draft_parents(r)
+        for i in range(n):
+            m = int(mask[row + i, 0]) | (int(mask[row + i, 1]) << 32)
+            assert (m >> i) & 1 and m >> n == 0
+            assert int(off[row + i]) == bin(m).count("1") - 1
+            if par[i] >= 0:
+                pm = int(mask[row + par[i], 0]) | (int(mask[row + par[i], 1]) << 32)
+                assert pm & m == pm and par[i] < i
+        row += n
+    assert any(b.draft_parents(3)[i] != i - 1 for i in range(1, 33))

@@ -38,7 +38,7 @@ import numpy as np
 FP32, BF16, FP8_E4M3, INT8 = "fp32", "bf16", "fp8_e4m3", "int8"
 CONTEXT, GENERATION = 0, 1
 
-_TAGS = {"lengths": 1, "blocks": 2, "q": 3, "k": 4, "v": 5, "hist_k": 6, "hist_v": 7, "norm": 8}
+_TAGS = {"lengths": 1, "blocks": 2, "q": 3, "k": 4, "v": 5, "hist_k": 6, "hist_v": 7, "norm": 8, "tree": 9}
 
 
 def _rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
@@ -85,6 +85,7 @@ class Batch:
     block_table: np.ndarray        # int32 [B, max_blocks_per_seq]; -1 where unused
     num_pool_blocks: int
     label: str = ""
+    tree: bool = False             # generation requests' draft tokens form random trees
 
     # ---- lengths -------------------------------------------------------
     @property
@@ -159,6 +160,43 @@ class Batch:
             return (x.astype(np.uint32) << 16).view(np.float32)
         return x
 
+    # ---- draft tokens ----------------------------------------------------
+    def draft_parents(self, r: int) -> np.ndarray:
+        """Parent of each new token of request r in its draft tree (-1 for token 0).  A
+        chain (token i - 1) unless the batch has ``tree`` and r is a generation request:
+        then token i's parent is drawn uniformly from tokens 0 .. i-1 (a tree whose
+        tokens are listed parents first, as verification batches list them)."""
+        n = int(self.context_lengths[r])
+        par = np.arange(-1, n - 1, dtype=np.int64)
+        if self.tree and int(self.request_types[r]) == GENERATION and n > 1:
+            g = _rng(self.seed, "tree", r)
+            par[1:] = [int(g.integers(0, i)) for i in range(1, n)]
+        return par
+
+    def spec_inputs(self) -> tuple[np.ndarray, np.ndarray]:
+        """The draft-tree inputs in packed row order: int32 [N] position offsets (a
+        generation row's depth in its request's tree; context rows 0) and uint32 [N, 2]
+        packed masks (bit j of word j // 32 at bit j % 32 set when the row's token attends
+        to new token j of its request: itself and its ancestors; context rows 0)."""
+        off = np.zeros(self.num_tokens, np.int32)
+        mask = np.zeros((self.num_tokens, 2), np.uint32)
+        row = 0
+        for r in range(self.num_requests):
+            n = int(self.context_lengths[r])
+            if int(self.request_types[r]) == GENERATION:
+                par = self.draft_parents(r)
+                depth = np.zeros(n, np.int64)
+                anc = [0] * n
+                for i in range(n):
+                    depth[i] = 0 if par[i] < 0 else depth[par[i]] + 1
+                    anc[i] = (1 << i) | (0 if par[i] < 0 else anc[par[i]])
+                off[row:row + n] = depth
+                for i in range(n):
+                    mask[row + i, 0] = anc[i] & 0xFFFFFFFF
+                    mask[row + i, 1] = anc[i] >> 32
+            row += n
+        return off, mask
+
     def packed(self, which: str) -> np.ndarray:
         """Concatenate new_q / new_k / new_v over requests in packed row order."""
         parts = [getattr(self, which)(r) for r in range(self.num_requests)]
@@ -166,13 +204,14 @@ class Batch:
 
 
 def make_batch(shape: Shape, ctx=(), gen_past=(), seed: int = 0, pool_blocks_min: int = 0,
-               label: str = "", gen_new=None) -> Batch:
+               label: str = "", gen_new=None, tree: bool = False) -> Batch:
     """Build a batch from explicit lengths.
 
     ``ctx`` is a sequence of (n_r, past_r) for context requests (their chunk
     and the tokens already cached before it); ``gen_past`` lists the cached
     length of each generation request.  A generation request brings one new
-    token, or ``gen_new[j]`` tokens (the token plus draft tokens to verify).
+    token, or ``gen_new[j]`` tokens (the token plus draft tokens to verify),
+    which form a chain, or random trees with ``tree``.
     """
     T = shape.tokens_per_block
     types, n, s = [], [], []
@@ -194,7 +233,7 @@ def make_batch(shape: Shape, ctx=(), gen_past=(), seed: int = 0, pool_blocks_min
     for r, k in enumerate(need):
         table[r, :k] = ids[pos:pos + k]
         pos += k
-    return Batch(shape, seed, types, n, s, table, pool, label)
+    return Batch(shape, seed, types, n, s, table, pool, label, tree)
 
 
 CODE_MAX = {FP8_E4M3: 448.0, INT8: 127.0}
