@@ -310,6 +310,44 @@ int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch
                                       const void* q, int64_t q_row_stride, const void* kv_pool,
                                       void* out, void* stream);
 
+/*
+ * Draft tokens verified as a tree ([REPORT] 1.4: spec_decoding_position_offsets and
+ * spec_decoding_packed_mask; a Medusa-style candidate tree checked in one forward pass,
+ * [TEARDOWN] speculative decoding).  For every packed row of a generation request with
+ * n tokens (the row of its token i):
+ *   position offset o_i : 0 <= o_i < n.  The row's q and k are rotated at position
+ *              S_r - n + o_i; its K/V still go to cache position S_r - n + i (the offsets
+ *              move the rotation, not the slot).
+ *   packed mask M_i    : two 32-bit words, bit j of word j / 32 at bit j % 32 set when the
+ *              row attends to new token j's key (cache position S_r - n + j).  Bit i must
+ *              be set and no bit j >= n.  Every row also attends to all S_r - n cached
+ *              positions.
+ * Offsets 0 .. n-1 with M_i = bits 0 .. i give the chain that the entry points without
+ * a tree compute.  Context rows' entries are ignored.
+ *   host_position_offsets, position_offsets : host and device int32 [N], packed row order.
+ *   host_packed_mask, packed_mask           : host and device uint32 [N][2].
+ * The host copies are validated (PKV_ERR_INVALID_ARG names the first bad row); the
+ * kernels read the device copies, which must hold the same values.
+ */
+typedef struct pkv_spec_tree {
+  const int32_t* host_position_offsets;
+  const int32_t* position_offsets;
+  const uint32_t* host_packed_mask;
+  const uint32_t* packed_mask;
+} pkv_spec_tree;
+
+/* pkv_append_rope with generation rows rotated at S_r - n_r + o_i (pkv_spec_tree). */
+int32_t pkv_append_rope_tree(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_spec_tree* tree,
+                             const void* q, int64_t q_row_stride,
+                             const void* k, const void* v, int64_t kv_row_stride,
+                             const double* rope_cos_sin, int32_t rope_max_pos,
+                             void* q_out, void* kv_pool, void* stream);
+
+/* pkv_attention_forward with generation rows attending to the cached positions and the
+ * new tokens their packed masks name (pkv_spec_tree). */
+int32_t pkv_attention_forward_tree(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_spec_tree* tree,
+                                   const void* q, int64_t q_row_stride, const void* kv_pool,
+                                   void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Opt-in timing for measurement tools.  pkv_kernel_timing_enable(1) times every kernel

@@ -6,7 +6,8 @@ PyTorch-owned device buffers.
 """
 from . import _lib  # noqa: F401
 from ._lib import (  # noqa: F401
-    PkvError, pkv_abi_version, pkv_append_rope, pkv_attention_forward, pkv_kernel_timing_enable,
+    PkvError, pkv_abi_version, pkv_append_rope, pkv_append_rope_tree, pkv_attention_forward,
+    pkv_attention_forward_tree, pkv_kernel_timing_enable,
     pkv_kernel_timings, pkv_last_error, pkv_rope_cos_sin, pkv_set_coschedule, pkv_set_decode_workgroups, pkv_workspace_size,
     pkv_workspace_size_for_batch,
 )

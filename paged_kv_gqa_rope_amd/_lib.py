@@ -77,6 +77,15 @@ class pkv_qk_norm(ctypes.Structure):
     ]
 
 
+class pkv_spec_tree(ctypes.Structure):
+    _fields_ = [
+        ("host_position_offsets", ctypes.c_void_p),
+        ("position_offsets", ctypes.c_void_p),
+        ("host_packed_mask", ctypes.c_void_p),
+        ("packed_mask", ctypes.c_void_p),
+    ]
+
+
 class PkvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"pkv status {status}: {message}")
@@ -114,6 +123,11 @@ def lib() -> ctypes.CDLL:
         L.pkv_attention_forward.restype = i32
         L.pkv_attention_forward_noalloc.argtypes = [D, Bt, vp, i64, vp, vp, vp]
         L.pkv_attention_forward_noalloc.restype = i32
+        Tr = ctypes.POINTER(pkv_spec_tree)
+        L.pkv_append_rope_tree.argtypes = [D, Bt, Tr, vp, i64, vp, vp, i64, vp, i32, vp, vp, vp]
+        L.pkv_append_rope_tree.restype = i32
+        L.pkv_attention_forward_tree.argtypes = [D, Bt, Tr, vp, i64, vp, vp, vp, sz, vp]
+        L.pkv_attention_forward_tree.restype = i32
         L.pkv_kernel_timing_enable.argtypes = [i32]
         L.pkv_kernel_timing_enable.restype = i32
         L.pkv_set_decode_workgroups.argtypes = [i32]
@@ -179,6 +193,20 @@ def pkv_attention_forward_fp8_out(desc, batch, q, q_row_stride, kv_pool, out_sca
 def pkv_attention_forward_noalloc(desc, batch, q, q_row_stride, kv_pool, out, stream) -> int:
     return lib().pkv_attention_forward_noalloc(ctypes.byref(desc), ctypes.byref(batch), q, q_row_stride, kv_pool,
                                                out, stream)
+
+
+def pkv_append_rope_tree(desc, batch, tree, q, q_row_stride, k, v, kv_row_stride, rope_cos_sin, rope_max_pos,
+                         q_out, kv_pool, stream) -> int:
+    return lib().pkv_append_rope_tree(ctypes.byref(desc), ctypes.byref(batch),
+                                      ctypes.byref(tree) if tree is not None else None, q, q_row_stride, k, v,
+                                      kv_row_stride, rope_cos_sin, rope_max_pos, q_out, kv_pool, stream)
+
+
+def pkv_attention_forward_tree(desc, batch, tree, q, q_row_stride, kv_pool, out, workspace, workspace_bytes,
+                               stream) -> int:
+    return lib().pkv_attention_forward_tree(ctypes.byref(desc), ctypes.byref(batch),
+                                            ctypes.byref(tree) if tree is not None else None, q, q_row_stride,
+                                            kv_pool, out, workspace, workspace_bytes, stream)
 
 
 

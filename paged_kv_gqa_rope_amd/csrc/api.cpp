@@ -172,13 +172,14 @@ int32_t pkv_rope_cos_sin(double base, int32_t rotary_dim, int32_t max_pos, doubl
 static int32_t append_impl(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_qk_norm* norm,
                            const void* q, int64_t q_row_stride, const void* k, const void* v, int64_t kv_row_stride,
                            const double* rope_cos_sin, int32_t rope_max_pos, void* q_out, void* kv_pool,
-                           void* stream) {
+                           void* stream, const pkv_spec_tree* tree = nullptr, bool with_tree = false) {
   std::string err;
   int rc = pkv::validate_desc(desc, err);
   if (rc != PKV_OK) return set_err(rc, err);
   pkv::BatchPlan plan;
   rc = pkv::validate_batch(desc, batch, &plan, err);
   if (rc != PKV_OK) return set_err(rc, err);
+  if (with_tree && (rc = pkv::validate_tree(batch, plan, tree, err)) != PKV_OK) return set_err(rc, err);
   if (plan.N == 0) return PKV_OK;
   const int32_t H = desc->num_heads, Hkv = desc->num_kv_heads, D = desc->head_dim;
   if ((q == nullptr) != (q_out == nullptr)) return set_err(PKV_ERR_INVALID_ARG, "q and q_out must both be given or both NULL");
@@ -241,6 +242,8 @@ static int32_t append_impl(const pkv_attn_desc* desc, const pkv_batch_desc* batc
   a.rope = desc->rope_style == PKV_ROPE_NEOX ? pkv::kRopeNeox
            : desc->rope_style == PKV_ROPE_GPTJ ? pkv::kRopeGptj : pkv::kRopeNone;
   a.max_n = plan.max_n;
+  a.pos_off = with_tree ? tree->position_offsets : nullptr;
+  a.gen_row = plan.ctx_tokens;
   a.norm = nkind == PKV_NORM_RMS ? pkv::kNormRms : nkind == PKV_NORM_LAYER ? pkv::kNormLayer : pkv::kNormNone;
   if (a.norm != pkv::kNormNone) {
     a.norm_eps = static_cast<double>(norm->eps);
@@ -270,17 +273,27 @@ int32_t pkv_append_qknorm_rope(const pkv_attn_desc* desc, const pkv_batch_desc* 
                      kv_pool, stream);
 }
 
+int32_t pkv_append_rope_tree(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_spec_tree* tree,
+                             const void* q, int64_t q_row_stride, const void* k, const void* v,
+                             int64_t kv_row_stride, const double* rope_cos_sin, int32_t rope_max_pos, void* q_out,
+                             void* kv_pool, void* stream) {
+  return append_impl(desc, batch, nullptr, q, q_row_stride, k, v, kv_row_stride, rope_cos_sin, rope_max_pos, q_out,
+                     kv_pool, stream, tree, true);
+}
+
 // use_scratch: the split-KV partials go to the library's scratch array instead of the
 // caller's workspace (workspace and workspace_bytes are then ignored).
 static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,
                               int64_t q_row_stride, const void* kv_pool, void* out, bool fp8_out, float out_scale,
-                              void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
+                              void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false,
+                              const pkv_spec_tree* tree = nullptr, bool with_tree = false) {
   std::string err;
   int rc = pkv::validate_desc(desc, err);
   if (rc != PKV_OK) return set_err(rc, err);
   pkv::BatchPlan plan;
   rc = pkv::validate_batch(desc, batch, &plan, err);
   if (rc != PKV_OK) return set_err(rc, err);
+  if (with_tree && (rc = pkv::validate_tree(batch, plan, tree, err)) != PKV_OK) return set_err(rc, err);
   if (plan.N == 0) return PKV_OK;
   const int32_t H = desc->num_heads, D = desc->head_dim;
   if (!q || !kv_pool || !out) return set_err(PKV_ERR_INVALID_ARG, "q, kv_pool and out must not be NULL");
@@ -342,6 +355,7 @@ static int32_t attention_impl(const pkv_attn_desc* desc, const pkv_batch_desc* b
   a.num_cus = dev.cus;
   // generation part's arguments (the context part's are set below)
   pkv::AttnArgs ad = a;
+  ad.spec_mask = with_tree ? tree->packed_mask : nullptr;
   if (plan.num_gen > 0) {
     ad.req_begin = plan.num_ctx;
     ad.req_end = plan.B;
@@ -446,6 +460,13 @@ int32_t pkv_attention_forward_fp8_out(const pkv_attn_desc* desc, const pkv_batch
                                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, true, out_scale_quant_orig, workspace,
                         workspace_bytes, stream);
+}
+
+int32_t pkv_attention_forward_tree(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const pkv_spec_tree* tree,
+                                   const void* q, int64_t q_row_stride, const void* kv_pool, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(desc, batch, q, q_row_stride, kv_pool, out, false, 1.f, workspace, workspace_bytes, stream,
+                        false, tree, true);
 }
 
 int32_t pkv_attention_forward_noalloc(const pkv_attn_desc* desc, const pkv_batch_desc* batch, const void* q,

@@ -96,17 +96,23 @@ __device__ __forceinline__ void norm8(double (&x)[8], int dim0, double2 st, cons
   }
 }
 
-// Where one token goes: its packed row, request, absolute position and pool slot.
+// Where one token goes: its packed row, request, cache position, rotation position and
+// pool slot.
 struct TokenSlot {
   int64_t row;
-  int32_t r, m, blk, slot;      // blk < 0: table entry out of range (skip the K/V store)
+  int32_t r, m, p, blk, slot;   // blk < 0: table entry out of range (skip the K/V store)
 };
 
 __device__ __forceinline__ TokenSlot make_slot(const AppendArgs& a, int64_t row, int r, int i) {
   TokenSlot tk;
   tk.row = row;
   tk.r = r;
-  tk.m = a.seq_len[r] - a.ctx_len[r] + i;
+  const int n = a.ctx_len[r], base = a.seq_len[r] - n;
+  tk.m = base + i;
+  // a draft tree's token rotates at base + its position offset (checked on the host to
+  // lie in 0 .. n-1; kept there whatever the device copy holds)
+  tk.p = tk.m;
+  if (a.pos_off != nullptr && row >= a.gen_row && row < a.N) tk.p = base + min(max(a.pos_off[row], 0), max(n - 1, 0));
   const int64_t lblk = tk.m / a.T;
   int32_t blk = (tk.m >= 0 && lblk < a.mbps) ? a.table[static_cast<int64_t>(r) * a.mbps + lblk] : -1;
   tk.blk = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
@@ -123,6 +129,7 @@ __device__ __forceinline__ TokenSlot uniform_slot(const TokenSlot& t) {
                                static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row))));
   u.r = __builtin_amdgcn_readfirstlane(t.r);
   u.m = __builtin_amdgcn_readfirstlane(t.m);
+  u.p = __builtin_amdgcn_readfirstlane(t.p);
   u.blk = __builtin_amdgcn_readfirstlane(t.blk);
   u.slot = __builtin_amdgcn_readfirstlane(t.slot);
   return u;
@@ -284,7 +291,7 @@ __device__ __forceinline__ void load_table(const AppendArgs& a, const TokenSlot&
                                            double2 (&cs)[8]) {
   if constexpr (RS != kRopeNone) {
     const double2* t = reinterpret_cast<const double2*>(a.cos_sin) +
-                       (rl.role != 0 && tk.m < a.max_pos ? static_cast<int64_t>(tk.m) * (a.R / 2) + rl.jt : 0);
+                       (rl.role != 0 && tk.p < a.max_pos ? static_cast<int64_t>(tk.p) * (a.R / 2) + rl.jt : 0);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       cs[k] = t[RS == kRopeGptj ? k % 4 : k];
@@ -315,7 +322,7 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
   const int c = lane % cph, e0 = c * 8;
   const int role = rl.role, poff = rl.poff;
   // positions past the table (rejected by the host) leave the rotated dims unwritten
-  const bool rot_ok = tk.m < a.max_pos;
+  const bool rot_ok = tk.p < a.max_pos;
   const bool kv_ok = tk.blk >= 0;
   const int64_t kdst = ((static_cast<int64_t>(tk.blk) * 2) * a.T + tk.slot) * static_cast<int64_t>(a.Hkv) * D;
   // descriptors are built where they are used (from scalar bases and sizes), so they stay

@@ -45,8 +45,17 @@ __global__ __launch_bounds__(kWave) void attn_generic_kernel(AttnArgs a, int hc)
   const int lane = threadIdx.x;
   const int64_t row = wave_prefix(a.ctx_len, r) + i;
   if (row >= a.N) return;
-  const int m = a.seq_len[r] - n + i;                  // this row's position; keys 0..m
+  // keys 0..m: m is this row's position (a chain), or the request's last key when its
+  // draft tokens form a tree (the row's mask then selects among the new keys)
+  const int base = a.seq_len[r] - n;
+  const bool tree = a.spec_mask != nullptr;
+  const int m = tree ? a.seq_len[r] - 1 : base + i;
   const int L = m + 1;
+  uint32_t vm_lo = 0, vm_hi = 0;
+  if (tree) {
+    vm_lo = a.spec_mask[row * 2];
+    vm_hi = a.spec_mask[row * 2 + 1];
+  }
   const int G = a.H / a.Hkv;
   const int h0 = blockIdx.y * hc;
   const int g = h0 / G;
@@ -71,7 +80,9 @@ __global__ __launch_bounds__(kWave) void attn_generic_kernel(AttnArgs a, int hc)
   for (int c0 = 0; c0 < L; c0 += kWave) {
     const int t = c0 + lane;
     int32_t blk = -1;
-    if (t < L) {
+    const int j = t - base;                              // new key j (tree masks)
+    const bool vis = !tree || j < 0 || (((j < 32 ? vm_lo : vm_hi) >> (j & 31)) & 1u);
+    if (t < L && vis) {
       const int64_t lb = t / a.T;
       blk = lb < a.mbps ? a.table[static_cast<int64_t>(r) * a.mbps + lb] : -1;
       if (blk >= a.num_blocks) blk = -1;

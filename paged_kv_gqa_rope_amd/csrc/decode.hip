@@ -43,10 +43,10 @@ namespace {
 using namespace dc;
 
 // The split pass on its own: one workgroup of four waves per range.
-template <int KV, int HPS, int CBW, bool NT>
+template <int KV, int HPS, int CBW, bool NT, bool TREE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[decode_lds_bytes()];
-  decode_split_body<KV, HPS, CBW, NT>(a, blockIdx.x, gridDim.x, lds);
+  decode_split_body<KV, HPS, CBW, NT, TREE>(a, blockIdx.x, gridDim.x, lds);
 }
 
 // One wave per (generation token, query head) -- or per TPW tokens of one request and query
@@ -197,20 +197,26 @@ __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per
 
 }  // namespace
 
-template <int KV>
+template <int KV, bool TREE>
 void launch_split_t(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.dec_wgs), block(kThreads);
-  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, true>), grid, block, 0, s, a);
-  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, true>), grid, block, 0, s, a);
-  else if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<KV, 4, 1, true>), grid, block, 0, s, a);
-  else if (a.col_blocks == 1) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, false>), grid, block, 0, s, a);
+  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, true, TREE>), grid, block, 0, s, a);
+  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, true, TREE>), grid, block, 0, s, a);
+  else if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<KV, 4, 1, true, TREE>), grid, block, 0, s, a);
+  else if (a.col_blocks == 1) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, true, TREE>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, false, TREE>), grid, block, 0, s, a);
+}
+
+template <bool TREE>
+void launch_split_kv(const AttnArgs& a, hipStream_t s) {
+  if (a.kv_fmt == F_FP8) launch_split_t<F_FP8, TREE>(a, s);
+  else if (a.kv_fmt == F_INT8) launch_split_t<F_INT8, TREE>(a, s);
+  else launch_split_t<F_BF16, TREE>(a, s);
 }
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  if (a.kv_fmt == F_FP8) launch_split_t<F_FP8>(a, s);
-  else if (a.kv_fmt == F_INT8) launch_split_t<F_INT8>(a, s);
-  else launch_split_t<F_BF16>(a, s);
+  if (a.spec_mask != nullptr) launch_split_kv<true>(a, s);
+  else launch_split_kv<false>(a, s);
   return hipGetLastError();
 }
 

@@ -174,8 +174,9 @@ __device__ __forceinline__ Piece read_piece(const int4* pa, const int4* pb, int 
 // across piece boundaries: a new piece starts with its first tiles already in flight, and
 // only the softmax state and Q are reset.  Each piece leaves one partial state in its slot.
 // NT: stream the cache with the nontemporal hint (every byte read once) or keep its lines
-// in L2 (segments of one column block each read the same keys).
-template <int KV, int HPS, int CBW, bool NT>
+// in L2 (segments of one column block each read the same keys).  TREE: draft tokens
+// verified as a tree; a column sees the cached keys and the new keys its mask row names.
+template <int KV, int HPS, int CBW, bool NT, bool TREE>
 __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int k, const int plane, const int4* pla,
                                               const int4* plb, uint16_t (*vtile)[kTile * kVStride],
                                               uint16_t (*ktile)[kTile * kD], float (*ml)[16][2]) {
@@ -303,6 +304,8 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   float m_run, l_run;                                           // for column li
   f32x4 o[8];                                                   // O[column lg*4+i][dim nb*16+li]
   int key_lim;                                                  // keys 0 .. key_lim for column li
+  uint32_t vm_lo = 0, vm_hi = 0;                                // TREE: column li's mask over the new keys
+  int c_base = 0;                                               // TREE: first new key of the request
   int c_t0, c_nt, c_cnt, c_kend, c_lim, c_ncol, c_valid, c_g, c_cb;
   int64_t c_slot;
   auto start_piece = [&](int p) {
@@ -315,8 +318,10 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     c_g = q.hg * HPS + wh;                                      // this wave's KV head
     c_kend = tiles_end(q.t0 + q.nt, S);
     // A tile needs no masking when it lies inside the piece and inside the causal range
-    // of every valid column of the block (the lowest of them is token cb*16 / G).
-    c_lim = S - n + (c_cb * 16) / G;
+    // of every valid column of the block (the lowest of them is token cb*16 / G; with a
+    // tree, every column sees the cached keys only for sure).
+    c_lim = TREE ? S - n - 1 : S - n + (c_cb * 16) / G;
+    c_base = S - n;
     c_ncol = min(16, G * n - c_cb * 16);                        // valid columns of the block
     if (CBW == 1) c_ncol = min(c_ncol, a.dec_cols);
     c_slot = static_cast<int64_t>(q.r - a.req_begin + k) * a.dec_lanes + plane;
@@ -325,11 +330,16 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     // up to that position: causal among a request's draft tokens) and head g*G + gc % G.
     const int gc = c_cb * 16 + li, tok = gc / G;
     const bool col_ok = tok < n;
-    key_lim = col_ok ? S - n + tok : -1;
+    key_lim = col_ok ? (TREE ? S - 1 : S - n + tok) : -1;
     const int64_t row0 = q.row0;
     // rows outside the generation rows, or a column block the request does not have: no output
     c_valid = row0 >= a.row_begin && row0 + n <= a.N && c_ncol > 0;
     const int64_t row = c_valid ? row0 + min(tok, n - 1) : a.row_begin;
+    if constexpr (TREE) {
+      const uint2 mw = col_ok && c_valid ? *reinterpret_cast<const uint2*>(a.spec_mask + row * 2) : make_uint2(0, 0);
+      vm_lo = mw.x;
+      vm_hi = mw.y;
+    }
     // B operand Q^T: column li, dims ks*32 + lg*8 + j (the dim order inside a
     // contraction is free as long as K uses the same one).
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
@@ -436,7 +446,13 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = tb + kb * 16 + lg * 4 + i;
-          x[kb * 4 + i] = key < kend && key <= key_lim ? sacc[kb][i] * xscale : -INFINITY;
+          bool vis = key < kend && key <= key_lim;
+          if constexpr (TREE) {
+            // new key j = key - c_base (0 <= j < n <= 64) is seen when bit j of the mask is set
+            const int j = key - c_base;
+            vis = vis && (j < 0 || (((j < 32 ? vm_lo : vm_hi) >> (j & 31)) & 1u));
+          }
+          x[kb * 4 + i] = vis ? sacc[kb][i] * xscale : -INFINITY;
           tmax = fmaxf(tmax, x[kb * 4 + i]);
         }
     }
@@ -751,7 +767,7 @@ __host__ __device__ constexpr int decode_lds_bytes() {
 // Split pass with register-staged tiles (any KV head count, any cache format).  With
 // CBW > 1 a segment carries all column blocks of its heads, and the waves of one head
 // share each staged tile (every tile leaves HBM once).
-template <int KV, int HPS, int CBW, bool NT>
+template <int KV, int HPS, int CBW, bool NT, bool TREE>
 __device__ __forceinline__ void decode_split_body(const AttnArgs& a, int bid, int nbid, unsigned char* lds) {
   auto& vtile = *reinterpret_cast<uint16_t (*)[kWaves][kTile * kVStride]>(lds);
   auto& ktile = *reinterpret_cast<uint16_t (*)[kWaves][kTile * kD]>(lds + kWaves * kTile * kVStride * 2);
@@ -763,7 +779,7 @@ __device__ __forceinline__ void decode_split_body(const AttnArgs& a, int bid, in
   while (true) {
     const int np = list_pieces(a, lane, L);
     if (np == 0) return;                                        // uniform
-    decode_stream<KV, HPS, CBW, NT>(a, np, k, lane, L.pla, L.plb, vtile, ktile, ml);
+    decode_stream<KV, HPS, CBW, NT, TREE>(a, np, k, lane, L.pla, L.plb, vtile, ktile, ml);
     __syncthreads();                                            // the list is read before it is refilled
   }
 }

@@ -41,6 +41,10 @@ struct AppendArgs {
   const float* kn_w;        // [D] weights for key heads
   const float* qn_b;        // [D] biases (layer form; may be null: zero)
   const float* kn_b;
+  // draft tokens as a tree: rows from gen_row on (generation requests) are rotated at
+  // S - n + pos_off[row] instead of S - n + i; null: the chain
+  const int32_t* pos_off;
+  int32_t gen_row;
 };
 
 struct AttnArgs {
@@ -77,6 +81,9 @@ struct AttnArgs {
   float* ws_ml;                  // [slots][dec_heads][dec_cols][2]  (m, l) per piece; slot (r + range) * lanes + lane
   float* ws_o;                   // [slots][dec_heads][dec_cols][D]  o per piece
   int32_t num_cus;               // compute units of the device
+  // draft tokens as a tree (generation launches only): packed row's two mask words, bit j
+  // set when the row sees new token j of its request; null: the chain (token i sees 0..i)
+  const uint32_t* spec_mask;
 };
 
 // Bytes of the library's device scratch array (one per GPU) used by the entry point that

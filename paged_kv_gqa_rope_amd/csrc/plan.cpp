@@ -207,4 +207,29 @@ size_t workspace_upper_bound(const pkv_attn_desc& d, int32_t max_num_requests, i
          static_cast<size_t>(entries) * d.head_dim * sizeof(float);
 }
 
+int validate_tree(const pkv_batch_desc* b, const BatchPlan& plan, const pkv_spec_tree* t, std::string& err) {
+  if (!t) return fail(err, PKV_ERR_INVALID_ARG, "spec tree is NULL");
+  if (!t->host_position_offsets || !t->position_offsets || !t->host_packed_mask || !t->packed_mask)
+    return fail(err, PKV_ERR_INVALID_ARG, "spec tree: host and device position offsets and packed masks are all required");
+  if ((reinterpret_cast<uintptr_t>(t->position_offsets) & 3u) || (reinterpret_cast<uintptr_t>(t->packed_mask) & 7u))
+    return fail(err, PKV_ERR_INVALID_ARG, "spec tree: position offsets must be 4-byte and packed masks 8-byte aligned");
+  int64_t row = plan.ctx_tokens;
+  for (int32_t r = plan.num_ctx; r < plan.B; ++r) {
+    const int32_t n = b->host_context_lengths[r];
+    for (int32_t i = 0; i < n; ++i, ++row) {
+      const int32_t o = t->host_position_offsets[row];
+      if (o < 0 || o >= n)
+        return fail(err, PKV_ERR_INVALID_ARG, "spec tree: row %lld has position offset %lld outside 0 .. n-1 (n = %lld)",
+                    row, o, n);
+      const uint64_t m = static_cast<uint64_t>(t->host_packed_mask[2 * row]) |
+                         (static_cast<uint64_t>(t->host_packed_mask[2 * row + 1]) << 32);
+      if (!((m >> i) & 1u))
+        return fail(err, PKV_ERR_INVALID_ARG, "spec tree: row %lld (token %lld of its request) lacks its own mask bit", row, i);
+      if (n < 64 && (m >> n) != 0)
+        return fail(err, PKV_ERR_INVALID_ARG, "spec tree: row %lld names a token at or past n = %lld in its mask", row, n);
+    }
+  }
+  return PKV_OK;
+}
+
 }  // namespace pkv

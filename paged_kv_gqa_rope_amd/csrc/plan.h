@@ -80,6 +80,10 @@ constexpr bool kHaveFastPrefill = true;
 
 int validate_desc(const pkv_attn_desc* d, std::string& err);
 int validate_batch(const pkv_attn_desc* d, const pkv_batch_desc* b, BatchPlan* plan, std::string& err);
+// Host check of a draft tree for a validated batch: every generation row's position
+// offset in 0 .. n-1, its own mask bit set and no bit at or past n; pointers given and
+// aligned.
+int validate_tree(const pkv_batch_desc* b, const BatchPlan& plan, const pkv_spec_tree* t, std::string& err);
 
 // Kernel selection for a validated desc (pure function of the desc).
 bool desc_fast_decode(const pkv_attn_desc& d);

@@ -146,6 +146,21 @@ class PagedStep:
             nrm.q_bias = self.norm_tensors["q_bias"].data_ptr()
             nrm.k_bias = self.norm_tensors["k_bias"].data_ptr()
             self.norm = nrm
+        self.tree = None
+        if getattr(batch, "tree", False):
+            if self.norm is not None or self.out_fp8_scale > 0:
+                raise ValueError("draft trees go through pkv_append_rope_tree / pkv_attention_forward_tree, "
+                                 "which take no qk norm and write no fp8 output")
+            off, mask = batch.spec_inputs()
+            self.tree_host = (np.ascontiguousarray(off, np.int32), np.ascontiguousarray(mask, np.uint32))
+            self.tree_dev = (torch.from_numpy(self.tree_host[0]).to(self.device),
+                             torch.from_numpy(self.tree_host[1].view(np.int32)).to(self.device))
+            tr = L.pkv_spec_tree()
+            tr.host_position_offsets = self.tree_host[0].ctypes.data
+            tr.position_offsets = self.tree_dev[0].data_ptr()
+            tr.host_packed_mask = self.tree_host[1].ctypes.data
+            tr.packed_mask = self.tree_dev[1].data_ptr()
+            self.tree = tr
         self.ws_bytes = L.pkv_workspace_size_for_batch(self.desc, self.bdesc)
         self.ws = torch.empty((max(self.ws_bytes, 256),), dtype=torch.uint8, device=self.device)
         if fill_history:
@@ -177,6 +192,11 @@ class PagedStep:
             del k, v, lens
 
     def append(self) -> int:
+        if self.tree is not None:
+            return L.pkv_append_rope_tree(self.desc, self.bdesc, self.tree, self.q.data_ptr(), self.q.shape[1],
+                                          self.k.data_ptr(), self.v.data_ptr(), self.k.shape[1],
+                                          self.rope.data_ptr(), self.max_pos, self.q_out.data_ptr(),
+                                          self.pool.data_ptr(), self.stream)
         if self.norm is not None:
             return L.pkv_append_qknorm_rope(self.desc, self.bdesc, self.norm, self.q.data_ptr(), self.q.shape[1],
                                             self.k.data_ptr(), self.v.data_ptr(), self.k.shape[1],
@@ -187,6 +207,10 @@ class PagedStep:
                                  self.q_out.data_ptr(), self.pool.data_ptr(), self.stream)
 
     def forward(self) -> int:
+        if self.tree is not None:
+            return L.pkv_attention_forward_tree(self.desc, self.bdesc, self.tree, self.q_out.data_ptr(),
+                                                self.q_out.shape[1], self.pool.data_ptr(), self.out.data_ptr(),
+                                                self.ws.data_ptr(), self.ws_bytes, self.stream)
         if self.out_fp8_scale > 0:
             return L.pkv_attention_forward_fp8_out(self.desc, self.bdesc, self.q_out.data_ptr(), self.q_out.shape[1],
                                                    self.pool.data_ptr(), self.out_fp8_scale, self.out.data_ptr(),

@@ -264,3 +264,42 @@ def test_timed_launch_wrappers_return(tmp_path):
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
     assert res.returncode == 0 and "returned" in res.stdout, res.stderr[-2000:]
+
+
+def _tree(off, mask_words, dev=True):
+    off = np.ascontiguousarray(off, np.int32)
+    mask = np.ascontiguousarray(np.asarray(mask_words, np.uint32).reshape(-1, 2))
+    t = L.pkv_spec_tree()
+    t.host_position_offsets = off.ctypes.data
+    t.position_offsets = P if dev else None
+    t.host_packed_mask = mask.ctypes.data
+    t.packed_mask = P if dev else None
+    return t, (off, mask)
+
+
+def test_draft_tree_inputs_are_validated_on_the_host():
+    # one context request (5 tokens), then generation requests with 3 and 2 tokens
+    hb = HostBatch([0, 1, 1], [5, 3, 2], [5, 13, 12], [[0], [1], [2]], 4)
+    good_off = [0, 0, 0, 0, 0, 0, 1, 1, 0, 1]
+    good_mask = [0, 0] * 5 + [1, 0, 3, 0, 5, 0, 1, 0, 3, 0]   # token 2 of request 1 is a sibling of token 1
+    bad = [
+        ([0] * 5 + [0, 1, 3, 0, 1], good_mask, "position offset"),      # offset 3 >= n = 3
+        ([0] * 5 + [0, 1, 1, 0, -1], good_mask, "position offset"),     # negative
+        (good_off, [0, 0] * 5 + [1, 0, 1, 0, 5, 0, 1, 0, 3, 0], "own mask bit"),   # token 1 lacks bit 1
+        (good_off, [0, 0] * 5 + [1, 0, 3, 0, 13, 0, 1, 0, 3, 0], "past n"),        # bit 3 with n = 3
+        (good_off, [0, 0] * 5 + [1, 0, 3, 0, 5, 1, 1, 0, 3, 0], "past n"),         # high word
+    ]
+    d = desc_for()
+    for off, mask, what in bad:
+        t, keep = _tree(off, mask)
+        rc = L.pkv_append_rope_tree(d, hb.desc, t, P, d.num_heads * d.head_dim, P, P, d.num_kv_heads * d.head_dim,
+                                    P, 10 ** 6, P, P, None)
+        expect(L.PKV_ERR_INVALID_ARG, rc)
+        assert what in L.pkv_last_error(), (what, L.pkv_last_error())
+        rc = L.pkv_attention_forward_tree(d, hb.desc, t, P, d.num_heads * d.head_dim, P, P, P, 1 << 40, None)
+        expect(L.PKV_ERR_INVALID_ARG, rc)
+    t, keep = _tree(good_off, good_mask, dev=False)                      # device copies missing
+    expect(L.PKV_ERR_INVALID_ARG, L.pkv_attention_forward_tree(d, hb.desc, t, P, d.num_heads * d.head_dim, P, P, P,
+                                                               1 << 40, None))
+    expect(L.PKV_ERR_INVALID_ARG, L.pkv_attention_forward_tree(d, hb.desc, None, P, d.num_heads * d.head_dim, P, P,
+                                                               P, 1 << 40, None))

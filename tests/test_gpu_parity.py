@@ -256,6 +256,47 @@ def test_generation_requests_with_draft_tokens(H, case_i):
     print(b.label, stats)
 
 
+TREE_CASES = [
+    # (shape, cached lengths, new tokens per generation request, context requests, kv override)
+    (2, [70, 300, 5], [2, 4, 7], [], None),                   # MHA: one column block, 4 heads per segment
+    (5, [1500, 700, 64], [4, 1, 3], [], W.FP8_E4M3),          # fp8 cache (fitted scales), G = 4
+    (4, [300, 90, 1000, 63], [8, 2, 5, 1], [], None),         # G = 8: 64 columns, 4 column-block waves per head
+    (4, [300, 0, 640, 31], [4, 3, 2, 4], [], None),           # G = 8: 2 column-block waves per head; an empty cache
+    (4, [200, 1200], [9, 3], [], None),                       # 72 columns: generic kernel
+    (1, [40, 9], [3, 6], [(20, 16)], None),                   # fp32: generic kernel, context rows first
+    (4, [500, 250, 33], [4, 6, 2], [(100, 0), (64, 128)], W.INT8),   # context chunks, then tree drafts (int8)
+    (4, [4000, 77], [33, 64], [], None),                      # trees as wide as the masks (33 and 64 tokens)
+    (2, [100, 2000], [33, 40], [], None),                     # MHA, 33 and 40 tokens: the masks' high word in the split pass
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(TREE_CASES)))
+def test_generation_requests_with_draft_trees(H, case_i):
+    """Draft tokens as random trees (pkv_append_rope_tree, pkv_attention_forward_tree):
+    token i is rotated at p + its depth, stored at cache position p + i, and sees the
+    cache and its ancestors; q_out and the pool bit-exact, attention within the bars."""
+    k, past, new, ctx, kv = TREE_CASES[case_i]
+    sh = dataclasses.replace(W.SHAPES[k], max_num_tokens=1 << 16)
+    b = W.make_batch(sh, ctx=ctx, gen_past=past, gen_new=new, seed=3500 + case_i, pool_blocks_min=8,
+                     label=f"tree{case_i}", tree=True)
+    if kv is not None:
+        b = W.fitted(b, kv)
+    case("draft trees", b.label, b.shape.name, "new", new, "past", past, "ctx", ctx)
+    assert any(b.draft_parents(r)[i] != i - 1 for r in range(b.num_requests) for i in range(1, int(b.context_lengths[r])))
+    st = run_step(H, b)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(b.shape.kv_dtype)), "pool")
+    ref = O.run(b)["out"]
+    stats = compare_attention(st.out_host(), ref, b.shape, b.label)
+    # a tree differs from the chain read of the same inputs wherever a token is not its
+    # predecessor's child: the chain's attention must fail the bars somewhere
+    chain = O.run(b, tree=False)["out"]
+    assert np.max(np.abs(chain - ref)) > 0.05, "the case must tell a tree from a chain"
+    print(b.label, stats)
+
+
 def test_full_tiny_workload(H):
     b = W.workload(1)
     case("full", b.label)
