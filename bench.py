@@ -69,7 +69,8 @@ def describe(batch) -> str:
             + (f" rope={sh.rope_style} rotary_dim={sh.rot_dim}" if sh.rope_style != "neox" or sh.rot_dim != sh.head_dim
                else "")
             + (f" qk_norm={sh.qk_norm}" if sh.qk_norm != "none" else "")
-            + (f" out=fp8(scale {sh.out_fp8_scale:g})" if sh.out_fp8_scale > 0 else ""))
+            + (f" out=fp8(scale {sh.out_fp8_scale:g})" if sh.out_fp8_scale > 0 else "")
+            + (" drafts=random trees" if getattr(batch, "tree", False) else ""))
 
 
 def variant_batch(name: str):
@@ -87,6 +88,10 @@ def variant_batch(name: str):
         sh = dataclasses.replace(W.SHAPES[4])
         past = W._uniform_pasts(1004, 128, 256, 4096)
         return W.make_batch(sh, gen_past=past, gen_new=[4] * 128, seed=1004, label="w4-spec4")
+    if name == "tree4-gqa8":     # the same 128 requests with their 1 + 3 tokens as random draft trees
+        sh = dataclasses.replace(W.SHAPES[4])
+        past = W._uniform_pasts(1004, 128, 256, 4096)
+        return W.make_batch(sh, gen_past=past, gen_new=[4] * 128, seed=1004, label="w4-tree4", tree=True)
     if name == "qknorm3":        # workload 3 with a per-head RMS norm of q and k before RoPE
         sh = dataclasses.replace(W.SHAPES[3], qk_norm="rms")
         return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-qknorm")
@@ -102,7 +107,7 @@ def variant_batch(name: str):
     raise KeyError(name)
 
 
-VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "fp8out3", "spec4-gqa8", "int8kv5")
+VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "fp8out3", "spec4-gqa8", "tree4-gqa8", "int8kv5")
 
 
 def decode_us(res: dict) -> float:
