@@ -42,10 +42,20 @@ def sample_heads(sh, k):
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_full_size_workload_sampled_parity(H, k):
-    b = W.workload(k)
+    _sampled_parity(H, W.workload(k), k, f"workload {k}")
+
+
+@pytest.mark.parametrize("name", ["spec4-gqa8", "tree4-gqa8", "int8kv5"])
+def test_full_size_variant_sampled_parity(H, name):
+    """The bench's draft-token (chain and tree) and int8-cache variants at full size."""
+    import bench
+    _sampled_parity(H, bench.variant_batch(name), 10 + bench.VARIANTS.index(name), f"variant {name}")
+
+
+def _sampled_parity(H, b, k, what):
     sh = b.shape
     t0 = time.time()
-    print(f"CASE full-size workload {k} ({sh.name}): building, history fill", flush=True)
+    print(f"CASE full-size {what} ({sh.name}): building, history fill", flush=True)
     st = H.PagedStep(b, sentinel=False)
     torch.cuda.synchronize()
     print(f"  setup {time.time() - t0:.1f} s; step", flush=True)
