@@ -90,6 +90,54 @@ int run(const char* name, const pkv_attn_desc* d, const pkv_batch_desc* b) {
   return rc;
 }
 
+// A draft tree's host and "device" arrays for a batch (the device pointers alias the
+// host arrays, 8-byte aligned; validation reads only the host copies).
+struct Tree {
+  std::vector<int32_t> off;
+  std::vector<uint64_t> mask64;                      // two 32-bit words per row
+  pkv_spec_tree t{};
+  // a valid tree per generation request: parent of token i drawn from 0 .. i-1
+  void random(const Batch& b, std::mt19937_64& rng) {
+    off.assign(b.desc.num_tokens, 0);
+    mask64.assign(b.desc.num_tokens, 0);
+    int64_t row = 0;
+    for (size_t r = 0; r < b.types.size(); ++r) {
+      const int32_t n = b.n[r];
+      if (b.types[r] == PKV_REQ_GENERATION) {
+        std::vector<int32_t> depth(n, 0);
+        for (int32_t i = 0; i < n; ++i) {
+          uint64_t m = 1ull << i;
+          if (i > 0) {
+            const int32_t par = static_cast<int32_t>(rng() % static_cast<uint64_t>(i));
+            depth[i] = depth[par] + 1;
+            m |= mask64[row + par];
+          }
+          off[row + i] = depth[i];
+          mask64[row + i] = m;
+        }
+      }
+      row += n;
+    }
+    point();
+  }
+  void point() {
+    t.host_position_offsets = off.data();
+    t.position_offsets = off.data();
+    t.host_packed_mask = reinterpret_cast<const uint32_t*>(mask64.data());
+    t.packed_mask = reinterpret_cast<const uint32_t*>(mask64.data());
+  }
+};
+
+int run_tree(const char* name, const pkv_attn_desc* d, const pkv_batch_desc* b, const pkv_spec_tree* t) {
+  std::string err;
+  int rc = pkv::validate_desc(d, err);
+  pkv::BatchPlan p;
+  if (rc == PKV_OK) rc = pkv::validate_batch(d, b, &p, err);
+  if (rc == PKV_OK) rc = pkv::validate_tree(b, p, t, err);
+  std::printf("case %s %d\n", name, rc);
+  return rc;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -155,6 +203,25 @@ int main(int argc, char** argv) {
   run("zero_context_length", &d, &b.desc);
   pkv_batch_desc empty{};
   run("empty", &d, &empty);
+
+  // ---- draft trees (one context request, then two generation requests with 3 and 5 tokens)
+  {
+    std::mt19937_64 trng(7);
+    pool = fill(b, {{C, 64, 64}, {G, 3, 300}, {G, 5, 90}}, 64);
+    b.build(pool);
+    Tree t;
+    t.random(b, trng);
+    run_tree("tree_ok", &d, &b.desc, &t.t);
+    t.off[64 + 2] = 3;                               // offset past n - 1 = 2
+    run_tree("tree_offset_past_n", &d, &b.desc, &t.t);
+    t.random(b, trng);
+    t.mask64[64 + 3 + 4] &= ~(1ull << 4);            // last token lacks its own bit
+    run_tree("tree_own_bit_missing", &d, &b.desc, &t.t);
+    t.random(b, trng);
+    t.mask64[64 + 1] |= 1ull << 40;                  // a bit in the high word, past n = 3
+    run_tree("tree_bit_past_n", &d, &b.desc, &t.t);
+    run_tree("tree_null", &d, &b.desc, nullptr);
+  }
 
   // ---- random batches: accepted ones plan consistently and fit the workspace bound
   std::mt19937_64 rng(12345);
@@ -226,6 +293,25 @@ int main(int argc, char** argv) {
     if (p.num_ctx + p.num_gen != p.B || p.N != b.desc.num_tokens) {
       std::printf("FAIL plan counts (iteration %d)\n", it);
       return 1;
+    }
+    // a random valid tree is accepted; the same tree with one planted fault is not
+    if (p.num_gen > 0 && p.N > 0) {
+      Tree t;
+      t.random(b, rng);
+      if (pkv::validate_tree(&b.desc, p, &t.t, err) != PKV_OK) {
+        std::printf("FAIL valid tree rejected: %s (iteration %d)\n", err.c_str(), it);
+        return 1;
+      }
+      const int32_t r = U(p.num_ctx, p.B - 1);
+      int64_t row = 0;
+      for (int32_t j = 0; j < r; ++j) row += b.n[j];
+      const int32_t i = U(0, b.n[r] - 1);
+      if (U(0, 1)) t.off[row + i] = b.n[r] + U(0, 3);
+      else t.mask64[row + i] &= ~(1ull << i);
+      if (pkv::validate_tree(&b.desc, p, &t.t, err) == PKV_OK) {
+        std::printf("FAIL planted tree fault accepted (iteration %d)\n", it);
+        return 1;
+      }
     }
   }
   std::printf("fuzz %d accepted %d\n", fuzz, accepted);

@@ -1,6 +1,7 @@
 """The HIP-free host part of the library (batch validation, split plan, workspace
-bound) built on its own with AddressSanitizer and UndefinedBehaviorSanitizer, driven
-through every error case and a few thousand random batches."""
+bound, draft-tree checks) built on its own with AddressSanitizer and
+UndefinedBehaviorSanitizer, driven through every error case and a few thousand random
+batches (each with a random valid tree and a planted tree fault)."""
 import os
 import shutil
 import subprocess
@@ -17,6 +18,7 @@ EXPECTED = {
     "block_id_outside_pool": -6, "table_too_narrow": -6, "too_many_draft_tokens": -2,
     "sequence_shorter_than_chunk": -1, "num_tokens_mismatch": -1, "max_context_length_short": -1,
     "host_lengths_null": -1, "bad_request_type": -1, "zero_context_length": -1, "empty": 0,
+    "tree_ok": 0, "tree_offset_past_n": -1, "tree_own_bit_missing": -1, "tree_bit_past_n": -1, "tree_null": -1,
 }
 
 
