@@ -56,7 +56,7 @@ extern "C" {
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = -1,  /* null pointer, inconsistent sizes, misaligned buffer    */
-  PKV_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement            */
+  PKV_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement          */
   PKV_ERR_ORDER = -3,        /* a context request after a generation request ([REPORT] 1.3) */
   PKV_ERR_CHUNK_ALIGN = -4,  /* context request whose cached length is not a multiple of
                                 tokens_per_block: only the last chunk of a prompt may be
