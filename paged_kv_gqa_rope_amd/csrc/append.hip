@@ -351,37 +351,52 @@ __device__ __forceinline__ void append_compute(const AppendArgs& a, const RowGeo
     }
     wave_sync();
     constexpr bool layer = LAYER;
+    // A row's chunks are read kStatAhead at a time (cph = D / 8 is 8 or 16), so one LDS
+    // latency covers several chunks; the sums still run in index order.
+    constexpr int kStatAhead = 8;
     for (int h = lane; h < nqk_b * hpi; h += kWave) {
       const unsigned char* row = stage + h * rowb;
       double s = 0.0;
       if (layer) {
-        for (int q = 0; q < cph; ++q) {
-          Raw8 q8;
-          q8.a = *reinterpret_cast<const uint4*>(row + q * CB);
-          q8.b = kRaw ? *reinterpret_cast<const uint4*>(row + q * CB + 16) : make_uint4(0, 0, 0, 0);
-          double x[8];
-          widen8<IO>(q8, x);
+        for (int q0 = 0; q0 < cph; q0 += kStatAhead) {
+          Raw8 q8[kStatAhead];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += x[e];
+          for (int j = 0; j < kStatAhead; ++j) {
+            q8[j].a = *reinterpret_cast<const uint4*>(row + (q0 + j) * CB);
+            q8[j].b = kRaw ? *reinterpret_cast<const uint4*>(row + (q0 + j) * CB + 16) : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int j = 0; j < kStatAhead; ++j) {
+            double x[8];
+            widen8<IO>(q8[j], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += x[e];
+          }
         }
       }
       const double mean = layer ? s / static_cast<double>(D) : 0.0;
       double ss = 0.0;
-      for (int q = 0; q < cph; ++q) {
-        Raw8 q8;
-        q8.a = *reinterpret_cast<const uint4*>(row + q * CB);
-        q8.b = kRaw ? *reinterpret_cast<const uint4*>(row + q * CB + 16) : make_uint4(0, 0, 0, 0);
-        double x[8];
-        widen8<IO>(q8, x);
+      for (int q0 = 0; q0 < cph; q0 += kStatAhead) {
+        Raw8 q8[kStatAhead];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (layer) {
-            const double d = x[e] - mean;
-            ss += d * d;
-          } else {
-            // x widens a bf16 or fp32 value (at most 24 significant bits), so x * x is
-            // exact in fp64 and the fused form rounds once, as ss + x * x does
-            ss = __builtin_fma(x[e], x[e], ss);
+        for (int j = 0; j < kStatAhead; ++j) {
+          q8[j].a = *reinterpret_cast<const uint4*>(row + (q0 + j) * CB);
+          q8[j].b = kRaw ? *reinterpret_cast<const uint4*>(row + (q0 + j) * CB + 16) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kStatAhead; ++j) {
+          double x[8];
+          widen8<IO>(q8[j], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (layer) {
+              const double d = x[e] - mean;
+              ss += d * d;
+            } else {
+              // x widens a bf16 or fp32 value (at most 24 significant bits), so x * x is
+              // exact in fp64 and the fused form rounds once, as ss + x * x does
+              ss = __builtin_fma(x[e], x[e], ss);
+            }
           }
         }
       }
