@@ -31,9 +31,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// 16 bytes of the cache.  Every K/V byte is read once per step (several column blocks of a
-// head share one staged tile) and every load instruction covers whole rows (whole 128-byte
-// lines), so the loads can carry the nontemporal hint (NT): lines are not kept for reuse
+// 16 bytes of the cache.  Where every K/V byte is read once per step (one column block, or
+// several sharing one staged tile) and every load instruction covers whole rows (whole
+// 128-byte lines), the loads carry the nontemporal hint (NT): lines are not kept for reuse
 // that will not come.
 template <bool NT>
 __device__ __forceinline__ uint4 load_kv(const void* p) {
@@ -213,9 +213,9 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   const uint32_t lane_off = static_cast<uint32_t>(lane / kLanes) * row_bytes + (lane % kLanes) * 16u;
   const float xscale = a.scale_log2 * a.k_scale;
   // SHARE (several column blocks per head): the CBW waves of one head split each tile's
-  // loads (K for one half of them, V for the other; with four, 16 rows each), stage them
-  // in one LDS tile of the head and meet at a workgroup barrier before the math, so every
-  // cache byte leaves HBM once.  Two LDS tiles per head alternate between items: a wave
+  // loads (with two waves one loads the K rows and the other the V rows; with four, each
+  // loads 16 rows of K or of V), stage them in one LDS tile of the head and meet at a
+  // workgroup barrier before the math, so every cache byte leaves HBM once.  Two LDS tiles per head alternate between items: a wave
   // writes tile s of item i + 2 only after the barrier of item i + 1, which every wave
   // passes after its reads of item i are complete.
   constexpr bool SHARE = CBW > 1;
