@@ -43,10 +43,10 @@ namespace {
 using namespace dc;
 
 // The split pass on its own: one workgroup of four waves per range.
-template <int KV, int HPS, int CBW, bool NT, bool TREE>
+template <int KV, int HPS, int CBW, bool NT, bool TREE, int DH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[decode_lds_bytes()];
-  decode_split_body<KV, HPS, CBW, NT, TREE>(a, blockIdx.x, gridDim.x, lds);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[decode_lds_bytes<DH>()];
+  decode_split_body<KV, HPS, CBW, NT, TREE, DH>(a, blockIdx.x, gridDim.x, lds);
 }
 
 // One wave per (generation token, query head) -- or per TPW tokens of one request and query
@@ -60,10 +60,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // and the loads of a wave's TPW tokens are all in flight together; at most 64 VGPRs keep
 // 8 waves per SIMD resident (one round of waves for most batches).  Pieces past a draft
 // token's position hold m = -inf and weigh nothing; the piece holding key 0 makes M finite.
-// The sums run in the same order for every TPW (bitwise the same output).
-template <int TPW>
+// The sums run in the same order for every TPW (bitwise the same output).  Head size DH:
+// lane d holds dimensions 2d and 2d + 1, so with DH = 64 lanes 32 .. 63 hold no
+// dimensions (they still hold pieces' (m, l)).
+template <int TPW, int DH>
 __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_combine_kernel(AttnArgs a) {
   constexpr int kPre = TPW == 1 ? 8 : 4;                             // o_p loads issued with the (m, l) loads
+  constexpr int kD = DH;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int h = blockIdx.x * kCombHeads + wave, rg = blockIdx.y, tok0 = blockIdx.z * TPW;
   const int r = a.req_begin + rg;
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per
   }
   // o_p of piece p for this lane
   const int64_t ps = stride * kD;                                   // floats between pieces
-  auto o_at = [&](int t, int p) { return *reinterpret_cast<const float2*>(ob[t] + p * ps + 2 * lane); };
+  const int dl = DH == 128 ? lane : min(lane, DH / 2 - 1);           // this lane's dimension pair
+  auto o_at = [&](int t, int p) { return *reinterpret_cast<const float2*>(ob[t] + p * ps + 2 * dl); };
   float L[TPW], ox[TPW], oy[TPW];
   if (np <= kWave) {
     // One memory round trip: every lane loads one piece's (m, l) while the first kPre
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per
   }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    if (!ok[t]) continue;
+    if (!ok[t] || 2 * lane >= DH) continue;
     const float sc = a.v_scale / L[t];
     const int64_t oi = (row[t] * a.H + h) * kD + 2 * lane;
     if (a.out_fmt == F_FP8) {
@@ -197,36 +201,49 @@ __global__ __launch_bounds__(kCombHeads * kWave) __attribute__((amdgpu_waves_per
 
 }  // namespace
 
-template <int KV, bool TREE>
+template <int KV, bool TREE, int DH>
 void launch_split_t(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.dec_wgs), block(kThreads);
-  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, true, TREE>), grid, block, 0, s, a);
-  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, true, TREE>), grid, block, 0, s, a);
-  else if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<KV, 4, 1, true, TREE>), grid, block, 0, s, a);
-  else if (a.col_blocks == 1) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, true, TREE>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, false, TREE>), grid, block, 0, s, a);
+  if (a.dec_cbw == 4) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 4, true, TREE, DH>), grid, block, 0, s, a);
+  else if (a.dec_cbw == 2) hipLaunchKernelGGL((decode_split_kernel<KV, 2, 2, true, TREE, DH>), grid, block, 0, s, a);
+  else if (a.dec_heads == kWaves) hipLaunchKernelGGL((decode_split_kernel<KV, 4, 1, true, TREE, DH>), grid, block, 0, s, a);
+  else if (a.col_blocks == 1) hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, true, TREE, DH>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_split_kernel<KV, 1, 1, false, TREE, DH>), grid, block, 0, s, a);
 }
 
-template <bool TREE>
+template <bool TREE, int DH>
 void launch_split_kv(const AttnArgs& a, hipStream_t s) {
-  if (a.kv_fmt == F_FP8) launch_split_t<F_FP8, TREE>(a, s);
-  else if (a.kv_fmt == F_INT8) launch_split_t<F_INT8, TREE>(a, s);
-  else launch_split_t<F_BF16, TREE>(a, s);
+  if (a.kv_fmt == F_FP8) launch_split_t<F_FP8, TREE, DH>(a, s);
+  else if (a.kv_fmt == F_INT8) launch_split_t<F_INT8, TREE, DH>(a, s);
+  else launch_split_t<F_BF16, TREE, DH>(a, s);
 }
 
 hipError_t launch_decode_split(const AttnArgs& a, hipStream_t s) {
-  if (a.spec_mask != nullptr) launch_split_kv<true>(a, s);
-  else launch_split_kv<false>(a, s);
+  if (a.D != 64 && a.D != 128) return hipErrorInvalidValue;
+  if (a.spec_mask != nullptr) {
+    if (a.D == 64) launch_split_kv<true, 64>(a, s);
+    else launch_split_kv<true, 128>(a, s);
+  } else {
+    if (a.D == 64) launch_split_kv<false, 64>(a, s);
+    else launch_split_kv<false, 128>(a, s);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
+template <int DH>
+void launch_combine_t(const AttnArgs& a, hipStream_t s) {
   constexpr int kTpw = 2;                                            // tokens per wave with draft tokens
   const int hb = (a.H + kCombHeads - 1) / kCombHeads, R = a.req_end - a.req_begin;
   if (a.max_n > 1)
-    hipLaunchKernelGGL(decode_combine_kernel<kTpw>, dim3(hb, R, (a.max_n + kTpw - 1) / kTpw), dim3(kCombHeads * kWave), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<kTpw, DH>), dim3(hb, R, (a.max_n + kTpw - 1) / kTpw), dim3(kCombHeads * kWave), 0, s, a);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<1>, dim3(hb, R, a.max_n), dim3(kCombHeads * kWave), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<1, DH>), dim3(hb, R, a.max_n), dim3(kCombHeads * kWave), 0, s, a);
+}
+
+hipError_t launch_decode_combine(const AttnArgs& a, hipStream_t s) {
+  if (a.D == 64) launch_combine_t<64>(a, s);
+  else if (a.D == 128) launch_combine_t<128>(a, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -21,8 +21,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 32;          // keys per wave iteration
-constexpr int kD = 128;            // head_dim handled here
-constexpr int kVStride = 136;      // LDS row stride (bf16 elements) of a staged V tile
+// The split pass handles head_dim DH = 64 or 128 (a template parameter): a staged V row
+// is padded by 8 elements, and a K row holds DH / 8 16-byte chunks.
+template <int DH>
+constexpr int v_stride() { return DH + 8; }        // LDS row stride (bf16 elements) of a staged V tile
 constexpr int kXcds = 8;           // XCDs of the chip, each with its own L2
 constexpr int kPieceBatch = 32;    // pieces listed at a time by the split pass
 constexpr int kCombHeads = 4;      // query heads (one wave each) per combine workgroup
@@ -44,9 +46,10 @@ __device__ __forceinline__ uint4 load_kv(const void* p) {
     return *static_cast<const uint4*>(p);
   }
 }
-// K tile in LDS: 16-byte chunk c of key row r sits at chunk position c ^ (r & 15), so the
-// 16 rows one MFMA operand read touches at one chunk fall on 16 distinct bank groups.
-__device__ __forceinline__ int kpos(int r, int c) { return c ^ (r & 15); }
+// K tile in LDS: 16-byte chunk c of key row r sits at chunk position c ^ (r & (DH/8 - 1)),
+// so the rows one MFMA operand read touches at one chunk fall on distinct bank groups.
+template <int DH>
+__device__ __forceinline__ int kpos(int r, int c) { return c ^ (r & (DH / 8 - 1)); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -95,12 +98,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Registers of one 32-key tile in flight: K and V rows as loaded (16 lanes per bf16
-// row, 8 lanes per fp8 / int8 row), copied to LDS at compute time.
-template <int KV>
+// Registers of one 32-key tile in flight: K and V rows as loaded (DH / 8 lanes per bf16
+// row, DH / 16 per fp8 / int8 row), copied to LDS at compute time.
+template <int KV, int DH>
 struct TileRegs {
-  uint4 k[KV == F_BF16 ? 8 : 4];
-  uint4 v[KV == F_BF16 ? 8 : 4];
+  uint4 k[kTile * DH * (KV == F_BF16 ? 2 : 1) / 1024];
+  uint4 v[kTile * DH * (KV == F_BF16 ? 2 : 1) / 1024];
 };
 
 __device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
@@ -176,10 +179,14 @@ __device__ __forceinline__ Piece read_piece(const int4* pa, const int4* pb, int 
 // NT: stream the cache with the nontemporal hint (every byte read once) or keep its lines
 // in L2 (segments of one column block each read the same keys).  TREE: draft tokens
 // verified as a tree; a column sees the cached keys and the new keys its mask row names.
-template <int KV, int HPS, int CBW, bool NT, bool TREE>
+template <int KV, int HPS, int CBW, bool NT, bool TREE, int DH>
 __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, const int k, const int plane, const int4* pla,
-                                              const int4* plb, uint16_t (*vtile)[kTile * kVStride],
-                                              uint16_t (*ktile)[kTile * kD], float (*ml)[16][2]) {
+                                              const int4* plb, uint16_t (*vtile)[kTile * v_stride<DH>()],
+                                              uint16_t (*ktile)[kTile * DH], float (*ml)[16][2]) {
+  constexpr int kD = DH;
+  constexpr int kVStride = v_stride<DH>();
+  constexpr int kKS = DH / 32;                                 // contraction steps of S^T = K Q^T
+  constexpr int kNB = DH / 16;                                 // 16-dim blocks of O
   // ALT: one KV head per segment, its waves sharing the tiles; otherwise every wave streams
   // all tiles for its own (KV head, column block): HPS heads x CBW column blocks.
   constexpr bool ALT = HPS == 1 && CBW == 1;
@@ -204,7 +211,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   // Load `it` of a tile covers rows it*kRows + lane/kLanes at byte column (lane%kLanes)*16
   // (16 lanes per 256-byte bf16 row, 8 per 128-byte fp8 / int8 row).
   constexpr int kEB = KV == F_BF16 ? 2 : 1;                    // cache element bytes
-  constexpr int kLoads = KV == F_BF16 ? 8 : 4;
+  constexpr int kLoads = kTile * kD * kEB / 1024;              // 1 KB load instructions per K (or V) tile
   constexpr int kRows = kWave * 16 / (kD * kEB);               // rows per load instruction
   constexpr int kLanes = kWave / kRows;                        // lanes per row
   const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * kEB;
@@ -225,7 +232,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   struct Share {
     uint4 r[kPart];
   };
-  using Regs = typename std::conditional<SHARE, Share, TileRegs<KV>>::type;
+  using Regs = typename std::conditional<SHARE, Share, TileRegs<KV, DH>>::type;
   int stg = 0;                                                  // LDS tile of the next item
 
   // ---- fetch cursor (wave-uniform): item f_k of piece f_p, with the piece's facts kept in
@@ -300,9 +307,9 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   };
 
   // ---- state of the piece being computed
-  bf16x8 qf[4];
+  bf16x8 qf[kKS];
   float m_run, l_run;                                           // for column li
-  f32x4 o[8];                                                   // O[column lg*4+i][dim nb*16+li]
+  f32x4 o[kNB];                                                 // O[column lg*4+i][dim nb*16+li]
   int key_lim;                                                  // keys 0 .. key_lim for column li
   uint32_t vm_lo = 0, vm_hi = 0;                                // TREE: column li's mask over the new keys
   int c_base = 0;                                               // TREE: first new key of the request
@@ -345,7 +352,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * a.q_stride +
                          static_cast<int64_t>(c_g * G + gc % G) * kD + lg * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < kKS; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(qp + ks * 32);
       if (!col_ok) u = make_uint4(0, 0, 0, 0);
       qf[ks] = as_bf16x8(u);
@@ -353,7 +360,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     m_run = -INFINITY;
     l_run = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
   // Write the piece's partial state (m, l, o) to its slot.
   auto end_piece = [&]() {
@@ -367,7 +374,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
           const int c = lg * 4 + i;
           if (c < ncol) {
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) a.ws_o[(e0 + c) * kD + nb * 16 + li] = o[nb][i];
+            for (int nb = 0; nb < kNB; ++nb) a.ws_o[(e0 + c) * kD + nb * 16 + li] = o[nb][i];
           }
         }
         if (lg == 0 && li < ncol) {
@@ -380,7 +387,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
       __syncthreads();
       float* red = reinterpret_cast<float*>(&vtile[0][0]);      // [wave][16 columns][kD]
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
+      for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[(wave * 16 + lg * 4 + i) * kD + nb * 16 + li] = o[nb][i];
       if (lg == 0) {
@@ -415,13 +422,13 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   // The tile's math from LDS tiles kt (K) and vt (V): scores, online softmax, O += P V.
   auto tile_math = [&](const uint16_t* kt, const uint16_t* vt, const int tb, const int kend, const int lim_all) {
     // A operand K: lane (li, lg) of step ks holds key kb*16 + li, dims ks*32 + lg*8 .. +7
-    bf16x8 kf[2][4];
+    bf16x8 kf[2][kKS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < kKS; ++ks) {
         const int row = kb * 16 + li;
-        kf[kb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + row * kD + kpos(row, ks * 4 + lg) * 8));
+        kf[kb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + row * kD + kpos<DH>(row, ks * 4 + lg) * 8));
       }
     // scores S^T[key][head]: lane holds head li, keys tb + kb*16 + lg*4 + i
     f32x4 sacc[2];
@@ -429,7 +436,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[ks], sacc[kb], 0, 0, 0);
     }
     float x[8];
@@ -473,7 +480,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
       for (int i = 0; i < 4; ++i) {
         const float ah = __shfl(alpha, lg * 4 + i, kWave);
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ah;
+        for (int nb = 0; nb < kNB; ++nb) o[nb][i] *= ah;
       }
     }
     const float m_off = m_run == -INFINITY ? 0.f : m_run;
@@ -495,7 +502,7 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
     // O += P V: B operand = V[keys][dims nb*16 .. +15] read transposed
     const int krow = lg * 4 + li / 4;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
       const uint16_t* src = vt + krow * kVStride + nb * 16 + 4 * (li % 4);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 16 * kVStride));
@@ -516,11 +523,11 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
         for (int j = 0; j < kPart; ++j) {
           const int row = row_of(s_it0 + j);
           if constexpr (KV == F_BF16) {
-            *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, li) * 8) = R.r[j];
+            *reinterpret_cast<uint4*>(kt + row * kD + kpos<DH>(row, lane % kLanes) * 8) = R.r[j];
           } else {
-            const int c0 = (lane % 8) * 2;
-            *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) = codes8_to_bf16x8<KV>(make_uint2(R.r[j].x, R.r[j].y));
-            *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) = codes8_to_bf16x8<KV>(make_uint2(R.r[j].z, R.r[j].w));
+            const int c0 = (lane % kLanes) * 2;
+            *reinterpret_cast<uint4*>(kt + row * kD + kpos<DH>(row, c0) * 8) = codes8_to_bf16x8<KV>(make_uint2(R.r[j].x, R.r[j].y));
+            *reinterpret_cast<uint4*>(kt + row * kD + kpos<DH>(row, c0 + 1) * 8) = codes8_to_bf16x8<KV>(make_uint2(R.r[j].z, R.r[j].w));
           }
         }
       } else {                                                  // V rows
@@ -531,12 +538,12 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
           const bool keep = row < lim;
           if constexpr (KV == F_BF16) {
             const uint4 u = R.r[j];
-            *reinterpret_cast<uint4*>(vt + row * kVStride + li * 8) =
+            *reinterpret_cast<uint4*>(vt + row * kVStride + (lane % kLanes) * 8) =
                 make_uint4(keep ? u.x : 0u, keep ? u.y : 0u, keep ? u.z : 0u, keep ? u.w : 0u);
           } else {
             const uint4 lo = codes8_to_bf16x8<KV>(make_uint2(R.r[j].x, R.r[j].y));
             const uint4 hi = codes8_to_bf16x8<KV>(make_uint2(R.r[j].z, R.r[j].w));
-            uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
+            uint16_t* d = vt + row * kVStride + (lane % kLanes) * 16;
             *reinterpret_cast<uint4*>(d) = make_uint4(keep ? lo.x : 0u, keep ? lo.y : 0u, keep ? lo.z : 0u, keep ? lo.w : 0u);
             *reinterpret_cast<uint4*>(d + 8) = make_uint4(keep ? hi.x : 0u, keep ? hi.y : 0u, keep ? hi.z : 0u, keep ? hi.w : 0u);
           }
@@ -546,24 +553,24 @@ __device__ __forceinline__ void decode_stream(const AttnArgs& a, const int np, c
   };
   // K and V rows of a whole tile into this wave's LDS tiles (bf16; an fp8 / int8 cache is
   // dequantised here), then the tile's math.
-  auto compute = [&](const int tb, const int kend, const int lim_all, const TileRegs<KV>& R) {
+  auto compute = [&](const int tb, const int kend, const int lim_all, const TileRegs<KV, DH>& R) {
     wave_lds_fence();
     if constexpr (KV == F_BF16) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = it * 4 + lg;
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, li) * 8) = R.k[it];
-        *reinterpret_cast<uint4*>(vt + row * kVStride + li * 8) = R.v[it];
+      for (int it = 0; it < kLoads; ++it) {
+        const int row = it * kRows + lane / kLanes, ch = lane % kLanes;
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos<DH>(row, ch) * 8) = R.k[it];
+        *reinterpret_cast<uint4*>(vt + row * kVStride + ch * 8) = R.v[it];
       }
     } else {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = it * 8 + lane / 8, c0 = (lane % 8) * 2;
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0) * 8) =
+      for (int it = 0; it < kLoads; ++it) {
+        const int row = it * kRows + lane / kLanes, c0 = (lane % kLanes) * 2;
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos<DH>(row, c0) * 8) =
             codes8_to_bf16x8<KV>(make_uint2(R.k[it].x, R.k[it].y));
-        *reinterpret_cast<uint4*>(kt + row * kD + kpos(row, c0 + 1) * 8) =
+        *reinterpret_cast<uint4*>(kt + row * kD + kpos<DH>(row, c0 + 1) * 8) =
             codes8_to_bf16x8<KV>(make_uint2(R.k[it].z, R.k[it].w));
-        uint16_t* d = vt + row * kVStride + (lane % 8) * 16;
+        uint16_t* d = vt + row * kVStride + (lane % kLanes) * 16;
         *reinterpret_cast<uint4*>(d) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].x, R.v[it].y));
         *reinterpret_cast<uint4*>(d + 8) = codes8_to_bf16x8<KV>(make_uint2(R.v[it].z, R.v[it].w));
       }
@@ -759,16 +766,18 @@ __device__ __forceinline__ int list_pieces(const AttnArgs& a, const int lane, Ra
 }
 // LDS bytes of decode_split_body: the staged V and K tiles of the four waves, their
 // softmax states and the range's bookkeeping.
+template <int DH>
 __host__ __device__ constexpr int decode_lds_bytes() {
-  return (kWaves * kTile * kVStride + kWaves * kTile * kD) * 2 + kWaves * 16 * 2 * 4 + static_cast<int>(sizeof(RangeLds));
+  return (kWaves * kTile * v_stride<DH>() + kWaves * kTile * DH) * 2 + kWaves * 16 * 2 * 4 + static_cast<int>(sizeof(RangeLds));
 }
 
 
 // Split pass with register-staged tiles (any KV head count, any cache format).  With
 // CBW > 1 a segment carries all column blocks of its heads, and the waves of one head
 // share each staged tile (every tile leaves HBM once).
-template <int KV, int HPS, int CBW, bool NT, bool TREE>
+template <int KV, int HPS, int CBW, bool NT, bool TREE, int DH>
 __device__ __forceinline__ void decode_split_body(const AttnArgs& a, int bid, int nbid, unsigned char* lds) {
+  constexpr int kVStride = v_stride<DH>(), kD = DH;
   auto& vtile = *reinterpret_cast<uint16_t (*)[kWaves][kTile * kVStride]>(lds);
   auto& ktile = *reinterpret_cast<uint16_t (*)[kWaves][kTile * kD]>(lds + kWaves * kTile * kVStride * 2);
   auto& ml = *reinterpret_cast<float (*)[kWaves][16][2]>(lds + (kWaves * kTile * kVStride + kWaves * kTile * kD) * 2);
@@ -779,7 +788,7 @@ __device__ __forceinline__ void decode_split_body(const AttnArgs& a, int bid, in
   while (true) {
     const int np = list_pieces(a, lane, L);
     if (np == 0) return;                                        // uniform
-    decode_stream<KV, HPS, CBW, NT, TREE>(a, np, k, lane, L.pla, L.plb, vtile, ktile, ml);
+    decode_stream<KV, HPS, CBW, NT, TREE, DH>(a, np, k, lane, L.pla, L.plb, vtile, ktile, ml);
     __syncthreads();                                            // the list is read before it is refilled
   }
 }

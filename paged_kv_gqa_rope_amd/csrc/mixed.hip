@@ -17,8 +17,8 @@ namespace pkv {
 namespace {
 
 constexpr int kMixedWaves = 8;
-constexpr int kMixedLds = pf::prefill_lds_bytes<4>() > dc::decode_lds_bytes() ? pf::prefill_lds_bytes<4>()
-                                                                                  : dc::decode_lds_bytes();
+constexpr int kMixedLds = pf::prefill_lds_bytes<4>() > dc::decode_lds_bytes<128>() ? pf::prefill_lds_bytes<4>()
+                                                                                  : dc::decode_lds_bytes<128>();
 
 template <int G, bool BT, int KV>
 __global__ __launch_bounds__(kMixedWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -31,7 +31,7 @@ void mixed_kernel(AttnArgs ac, PrefillSched sc, AttnArgs ad, int nctx) {
   }
   // waves 4-7 of a split-pass workgroup end here (a wave-uniform test)
   if (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x)) >= dc::kThreads) return;
-  dc::decode_split_body<KV, 4, 1, true, false>(ad, bid - nctx, static_cast<int>(gridDim.x) - nctx, lds);
+  dc::decode_split_body<KV, 4, 1, true, false, 128>(ad, bid - nctx, static_cast<int>(gridDim.x) - nctx, lds);
 }
 
 template <int G, int KV>
@@ -60,7 +60,8 @@ hipError_t launch_mixed_g(const AttnArgs& ac, const int32_t* host_n, const int32
 
 bool mixed_supported(const AttnArgs& ad, int num_ctx, int G) {
   return num_ctx <= kPrefillMaxReqs && ad.dec_heads == 4 && ad.dec_cbw == 1 && ad.col_blocks == 1 &&
-         (G == 1 || G == 2 || G == 4 || G == 8) && ad.T >= 16 && ad.spec_mask == nullptr;   // chains only
+         (G == 1 || G == 2 || G == 4 || G == 8) && ad.T >= 16 && ad.D == 128 &&
+         ad.spec_mask == nullptr;   // chains only
 }
 
 hipError_t launch_mixed(const AttnArgs& ac, const int32_t* host_ctx_len, const int32_t* host_seq_len,

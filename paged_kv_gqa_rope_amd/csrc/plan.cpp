@@ -62,7 +62,7 @@ bool desc_fast_decode(const pkv_attn_desc& d) {
   const int32_t G = d.num_heads / d.num_kv_heads;
   return d.io_dtype == PKV_BF16 && (d.kv_dtype == PKV_BF16 || d.kv_dtype == PKV_FP8_E4M3 || d.kv_dtype == PKV_INT8) &&
          G <= 16 &&
-         d.head_dim == 128;
+         (d.head_dim == 128 || d.head_dim == 64);
 }
 
 bool desc_fast_prefill(const pkv_attn_desc& d) {

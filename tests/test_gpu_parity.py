@@ -297,6 +297,45 @@ def test_generation_requests_with_draft_trees(H, case_i):
     print(b.label, stats)
 
 
+HEAD64_CASES = [
+    # (Hkv, G, T, cache, draft tokens per request or None, tree, context chunks, split workgroups)
+    (8, 4, 64, W.BF16, None, False, [], 0),             # four KV heads per workgroup
+    (32, 1, 16, W.BF16, None, False, [(40, 32)], 0),    # MHA, tiles over two blocks, a context chunk first
+    (4, 8, 32, W.FP8_E4M3, 4, False, [], 13),           # two column blocks: two waves share each tile
+    (4, 8, 64, W.INT8, 8, True, [], 0),                 # four column blocks, draft trees
+    (2, 8, 64, W.BF16, None, False, [], 5),             # one KV head per workgroup, waves share the tiles
+    (3, 4, 16, W.FP8_E4M3, 3, False, [], 0),            # one head per segment, several column blocks
+    (8, 8, 128, W.BF16, 2, True, [(64, 128)], 0),       # trees after a context chunk
+]
+
+
+@pytest.mark.parametrize("case_i", range(len(HEAD64_CASES)))
+def test_head_dim_64_generation(H, case_i):
+    """head_dim 64 on the MFMA split pass (every segment layout, bf16 / fp8 / int8
+    caches, chains and trees of draft tokens): q_out and the pool bit-exact, attention
+    within the bars."""
+    from paged_kv_gqa_rope_amd import _lib as L
+    Hkv, G, T, kv, draft, tree, ctx, wgs = HEAD64_CASES[case_i]
+    sh = W.Shape(f"d64-{case_i}", Hkv * G, Hkv, 64, T, W.BF16, kv, 1e4, max_num_tokens=1 << 16)
+    pasts = [0, 1, 31, 32, 63, 100, 511, 700, 1500, 5]
+    gen_new = None if draft is None else [1 + (i % draft) for i in range(len(pasts))]
+    b = W.make_batch(sh, ctx=ctx, gen_past=pasts, gen_new=gen_new, seed=5400 + case_i, pool_blocks_min=3,
+                     label=f"d64-{case_i}", tree=tree)
+    if kv in (W.FP8_E4M3, W.INT8):
+        b = W.fitted(b)
+    case("head_dim 64", b.label, b.shape.kv_dtype, "drafts", draft, "tree", tree, "ctx", ctx, "W", wgs)
+    old = L.pkv_set_decode_workgroups(wgs)
+    try:
+        st = run_step(H, b)
+    finally:
+        L.pkv_set_decode_workgroups(old)
+    tabs = O.tables(b)
+    ref_q = np.concatenate([O.append_request(b, r, tabs)[0] for r in range(b.num_requests)])
+    assert_bits_equal(st.q_out_host(), ref_q, "q_out")
+    assert_bits_equal(bits_of(st.pool_host()), O.expected_pool(b, sentinel(b.shape.kv_dtype)), "pool")
+    compare_attention(st.out_host(), O.run(b)["out"], b.shape, b.label)
+
+
 def test_full_tiny_workload(H):
     b = W.workload(1)
     case("full", b.label)
