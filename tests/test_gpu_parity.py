@@ -128,30 +128,42 @@ def test_qk_norm_append_and_attention(H, case_i):
 # the serial launches and within the bars against the oracle.
 MIXED_CASES = [
     # (shape, kv dtype, decode workgroups, context chunks (n, cached: a multiple of the block),
-    #  cached lengths of generation requests)
-    (4, None, 16, [(128, 0), (192, 128), (100, 384)], [20, 77, 140, 333, 500, 9]),        # GQA-8 bf16
-    (3, None, 8, [(300, 0), (65, 640)], [1, 64, 65, 900]),                                 # GQA-4 bf16
-    (2, None, 32, [(70, 0)], [0, 63, 64, 700, 1000]),                                      # MHA bf16
-    (5, "fp8", 24, [(200, 128)], [1000, 2500, 3000]),                                      # GQA-4 fp8
-    (4, "int8", 8, [(64, 64), (33, 0)], [5, 511, 512]),                                    # GQA-8 int8
+    #  cached lengths of generation requests, their new tokens (None: one each), draft trees)
+    (4, None, 16, [(128, 0), (192, 128), (100, 384)], [20, 77, 140, 333, 500, 9], None, False),   # GQA-8 bf16
+    (3, None, 8, [(300, 0), (65, 640)], [1, 64, 65, 900], None, False),                            # GQA-4 bf16
+    (2, None, 32, [(70, 0)], [0, 63, 64, 700, 1000], None, False),                                 # MHA bf16
+    (5, "fp8", 24, [(200, 128)], [1000, 2500, 3000], None, False),                                 # GQA-4 fp8
+    (4, "int8", 8, [(64, 64), (33, 0)], [5, 511, 512], None, False),                               # GQA-8 int8
+    (4, None, 16, [(128, 0), (64, 128)], [20, 300, 77, 900], [2, 1, 2, 1], True),                  # GQA-8, draft trees
+    (2, None, 16, [(70, 0)], [63, 700, 5], [4, 8, 16], True),                                      # MHA, draft trees
 ]
 
 
 @pytest.mark.parametrize("case_i", range(len(MIXED_CASES)))
 def test_mixed_launch_matches_serial(H, case_i):
     from paged_kv_gqa_rope_amd import _lib as L
-    k, kv, wgs, ctx, past = MIXED_CASES[case_i]
+    k, kv, wgs, ctx, past, new, tree = MIXED_CASES[case_i]
     sh = W.SHAPES[k]
     if kv == "fp8":
         sh = dataclasses.replace(sh, kv_dtype=W.FP8_E4M3, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
     elif kv == "int8":
         sh = dataclasses.replace(sh, kv_dtype=W.INT8, k_scale=2.0 ** -5, v_scale=2.0 ** -5)
-    b = W.make_batch(sh, ctx=ctx, gen_past=past, seed=6100 + case_i, pool_blocks_min=4, label=f"mixed-{case_i}")
-    case("mixed", b.label, sh.name, sh.kv_dtype, wgs)
+    b = W.make_batch(sh, ctx=ctx, gen_past=past, gen_new=new, seed=6100 + case_i, pool_blocks_min=4,
+                     label=f"mixed-{case_i}", tree=tree)
+    case("mixed", b.label, sh.name, sh.kv_dtype, wgs, "tree", tree)
     old_w = L.pkv_set_decode_workgroups(wgs)
     old_c = L.pkv_set_coschedule(1)
     try:
-        mixed = run_step(H, b).out_host()
+        st = run_step(H, b)
+        L.check(L.pkv_kernel_timing_enable(1))
+        st.step()
+        torch.cuda.synchronize()
+        names = {n for n, _ in L.pkv_kernel_timings()}
+        L.check(L.pkv_kernel_timing_enable(0))
+        # one launch for a bf16 cache; one-byte caches take the generic context kernel,
+        # so their batches run as two launches even when asked for one
+        assert ("mixed" in names) == (kv is None), names
+        mixed = st.out_host()
         L.pkv_set_coschedule(0)
         serial = run_step(H, b).out_host()
     finally:
