@@ -98,6 +98,10 @@ def variant_batch(name: str):
     if name == "fp8out3":        # workload 3 with the attention output written as fp8 (scale 2^-6)
         sh = dataclasses.replace(W.SHAPES[3], out_fp8_scale=2.0 ** -6)
         return W.make_batch(sh, ctx=[(2048, 0)] * 8, seed=1003, label="w3-fp8out")
+    if name == "mha64-2":        # workload 2's 64 requests with 64-dim heads
+        b = W.workload(2)
+        sh = dataclasses.replace(b.shape, name="decode-mha-bf16-d64", head_dim=64)
+        return dataclasses.replace(b, shape=sh, label="w2-d64")
     if name == "int8kv5":        # workload 5 with an int8 KV cache, K/V scales fitted to its values (amax/127)
         sk, sv = W.W5_INT8_SCALES
         sh = dataclasses.replace(W.SHAPES[5], name="longdecode-gqa4-int8kv", kv_dtype=W.INT8,
@@ -107,7 +111,7 @@ def variant_batch(name: str):
     raise KeyError(name)
 
 
-VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "fp8out3", "spec4-gqa8", "tree4-gqa8", "int8kv5")
+VARIANTS = ("gptj3", "gptj3-half", "qknorm3", "fp8out3", "spec4-gqa8", "tree4-gqa8", "int8kv5", "mha64-2")
 
 
 def decode_us(res: dict) -> float:
